@@ -1,0 +1,71 @@
+"""Build libevs.so (the HIP kernels + C ABI) in-tree for gfx950.
+
+    python -m attention_dna_lms_amd.build [--jobs N]
+
+Every source is compiled with hipcc for gfx950 only; objects go to _build/ at
+the repository root and the shared library next to this file.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+import time
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OUT = os.path.join(PKG, "libevs.so")
+BUILD = os.path.join(ROOT, "_build")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+SOURCES = ["gemm_bf16.hip", "gemm_f32.hip", "attn.hip", "small.hip", "evs_api.cpp"]
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    # every multiply-add in the kernels is written out (fmaf where fused)
+    "-ffp-contract=off",
+    # no packed fp32 arithmetic (v_pk_*_f32)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [HIPCC, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS
+    t0 = time.time()
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+    noisy = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+    if noisy:
+        sys.stderr.write("\n".join(noisy) + "\n")
+    return f"{src}: {time.time() - t0:.1f}s"
+
+
+def build(jobs: int = 0, verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        for msg in ex.map(_compile, SOURCES):
+            if verbose:
+                print("  compiled", msg, flush=True)
+    objs = [os.path.join(BUILD, s + ".o") for s in SOURCES]
+    tmp = OUT + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, OUT)
+    if verbose:
+        print("  linked", OUT, flush=True)
+    return OUT
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=0)
+    build(ap.parse_args().jobs)

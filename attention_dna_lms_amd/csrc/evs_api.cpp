@@ -1,0 +1,680 @@
+// Host side of the C ABI (include/evs.h): model and state layout, argument and
+// state-machine checks, and the launch sequence of the block-verification
+// forward, the verifier and the rollback. All device work is enqueued on the
+// caller's stream; nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/evs.h"
+#include "evs_dev.h"
+
+using namespace evs;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+constexpr int MAX_ROWS_PER_WG = 144;   // 9 MFMA row tiles
+constexpr int GEMM_CNT = 65536;        // split-K arrival counters
+
+size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
+int next_pow2(int x) { int p = 1; while (p < x) p <<= 1; return p; }
+
+struct Mat {            // one packed matrix
+  size_t off = 0;       // byte offset in the packed buffer
+  int rows_valid = 0, K = 0, n_groups = 0, NT = 1, map_kind = 0, map_stride = 0;
+  size_t bytes(int es) const { return (size_t)n_groups * NT * 16 * K * es; }
+};
+
+struct BlockPlan {
+  evs_block_desc d{};
+  Mat w_in, w_out, w_gu, w_down;
+  size_t taps = 0, lam = 0, res = 0;   // f32 parameter offsets
+};
+
+}  // namespace
+
+struct evs_model {
+  evs_model_desc desc{};
+  std::vector<evs_block_desc> blocks;
+  std::vector<BlockPlan> plan;
+  char* base = nullptr;
+  size_t embed = 0, total = 0;
+  Mat lm;
+  int es = 2, kstep = 32;
+  int max_dff = 0, max_heads = 0, max_dh = 0;
+};
+
+struct evs_state {
+  const evs_model* m = nullptr;
+  int B = 0, max_ctx = 0, max_block = 0, cap = 0, S = 1, qtn_max = 1, M_max = 0;
+  char* sb = nullptr;   // state buffer
+  char* wb = nullptr;   // workspace
+  size_t off_t = 0, off_ib = 0, off_is = 0, off_err = 0;
+  std::vector<size_t> ring, iir, kc, vt;   // per block
+  std::vector<int> R;
+  size_t state_total = 0;
+  // workspace
+  size_t w_x = 0, w_nrm = 0, w_o = 0, w_q = 0, w_h = 0, w_logit = 0, w_part = 0, w_cnt = 0, w_apart = 0,
+         w_acnt = 0, ws_total = 0;
+  size_t part_floats = 0, apart_floats = 0, acnt_n = 0;
+  bool pending = false;
+  int pending_P = 0;
+  // per-kernel timing (measurement aid): event pairs around launches
+  struct Rec { hipEvent_t a, b; int kc; double bytes; };
+  bool timing = false;
+  long long timing_ctx = 0;   // caller-supplied context length used for attention byte counts
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  ~evs_state() {
+    for (auto& r : recs) { pool.push_back(r.a); pool.push_back(r.b); }
+    for (auto e : pool) (void)hipEventDestroy(e);
+  }
+};
+
+namespace {
+
+bool check_desc(const evs_model_desc* d) {
+  if (!d || !d->blocks || d->n_blocks < 0 || d->vocab < 2 || d->d_model < 32 || d->d_model % 32) return false;
+  if (d->dtype != EVS_BF16 && d->dtype != EVS_F32) return false;
+  if (!(d->norm_eps >= 0.f)) return false;
+  for (int i = 0; i < d->n_blocks; ++i) {
+    const evs_block_desc& b = d->blocks[i];
+    switch (b.kind) {
+      case EVS_FIR: if (b.fir_len < 1 || b.fir_len > 4096) return false; break;
+      case EVS_IIR: if (b.iir_states < 1 || b.iir_states > 16) return false; break;
+      case EVS_ATTN:
+        if (b.head_dim != 32 && b.head_dim != 64 && b.head_dim != 128) return false;
+        if (b.n_heads < 1 || (long long)b.n_heads * b.head_dim != d->d_model) return false;
+        break;
+      case EVS_MLP: if (b.d_ff < 32 || b.d_ff % 32) return false; break;
+      default: return false;
+    }
+  }
+  return true;
+}
+
+// Lay out the packed buffer for `desc` into `m` (no device access).
+void plan_model(const evs_model_desc* desc, evs_model* m) {
+  m->desc = *desc;
+  m->blocks.assign(desc->blocks, desc->blocks + desc->n_blocks);
+  m->desc.blocks = m->blocks.data();
+  m->es = desc->dtype == EVS_BF16 ? 2 : 4;
+  m->kstep = desc->dtype == EVS_BF16 ? 32 : 16;
+  const int d = desc->d_model, V = desc->vocab, es = m->es;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  m->embed = take((size_t)V * d * es);
+  m->plan.clear();
+  m->max_dff = m->max_heads = m->max_dh = 0;
+  for (const auto& b : m->blocks) {
+    BlockPlan p;
+    p.d = b;
+    if (b.kind == EVS_MLP) {
+      p.w_gu = Mat{0, 2 * b.d_ff, d, b.d_ff / 16, 2, 1, b.d_ff};
+      p.w_gu.off = take(p.w_gu.bytes(es));
+      p.w_down = Mat{0, d, b.d_ff, d / 16, 1, 0, 0};
+      p.w_down.off = take(p.w_down.bytes(es));
+      m->max_dff = std::max(m->max_dff, b.d_ff);
+    } else {
+      p.w_in = Mat{0, 3 * d, d, d / 16, 3, 1, d};
+      p.w_in.off = take(p.w_in.bytes(es));
+      if (b.kind == EVS_FIR) p.taps = take((size_t)d * b.fir_len * 4);
+      if (b.kind == EVS_IIR) { p.lam = take((size_t)d * b.iir_states * 4); p.res = take((size_t)d * b.iir_states * 4); }
+      if (b.kind == EVS_ATTN) { m->max_heads = std::max(m->max_heads, b.n_heads); m->max_dh = std::max(m->max_dh, b.head_dim); }
+      p.w_out = Mat{0, d, d, d / 16, 1, 0, 0};
+      p.w_out.off = take(p.w_out.bytes(es));
+    }
+    m->plan.push_back(p);
+  }
+  m->lm = Mat{0, V, d, (V + 15) / 16, 1, 0, 0};
+  m->lm.off = take(m->lm.bytes(es));
+  m->total = off;
+}
+
+// canonical tensor list (see evs.h)
+struct Canon { int64_t rows, cols; int dtype; };
+std::vector<Canon> canon_list(const evs_model_desc* d) {
+  std::vector<Canon> v;
+  const int64_t D = d->d_model;
+  const int mt = d->dtype;
+  v.push_back({d->vocab, D, mt});
+  for (int i = 0; i < d->n_blocks; ++i) {
+    const evs_block_desc& b = d->blocks[i];
+    if (b.kind == EVS_FIR) { v.push_back({3 * D, D, mt}); v.push_back({D, b.fir_len, EVS_F32}); v.push_back({D, D, mt}); }
+    else if (b.kind == EVS_IIR) {
+      v.push_back({3 * D, D, mt}); v.push_back({D, b.iir_states, EVS_F32}); v.push_back({D, b.iir_states, EVS_F32});
+      v.push_back({D, D, mt});
+    } else if (b.kind == EVS_ATTN) { v.push_back({3 * D, D, mt}); v.push_back({D, D, mt}); }
+    else { v.push_back({2LL * b.d_ff, D, mt}); v.push_back({D, b.d_ff, mt}); }
+  }
+  v.push_back({d->vocab, D, mt});
+  return v;
+}
+
+// workgroup k-split so that a launch has >= ~256 workgroups while each keeps
+// >= 8 k-steps
+int choose_ks(int n_groups, int ksteps, int slices) {
+  int ks = 1;
+  while (n_groups * slices * ks < 256 && ksteps / (ks * 2) >= 8 && ks < 16) ks *= 2;
+  return ks;
+}
+
+struct Slicing { int rows_per_slice, slices, MT; };
+Slicing slicing(int nseq, int P) {
+  int sps = std::max(1, MAX_ROWS_PER_WG / P);
+  sps = std::min(sps, nseq);
+  Slicing s;
+  s.rows_per_slice = sps * P;
+  s.slices = (nseq + sps - 1) / sps;
+  s.MT = (s.rows_per_slice + 15) / 16;
+  return s;
+}
+
+int gemm_bufs(int MT, int NT) { return (4 * NT * MT <= 48) ? 4 : ((2 * NT * MT <= 48) ? 2 : 1); }
+
+size_t gemm_lds(int MT, int NT, int scratch_floats) {
+  const size_t RS = (size_t)NT * MT * 256;
+  return 4 * (MT * 16 + std::max(gemm_bufs(MT, NT) * RS, RS + (size_t)scratch_floats));
+}
+
+void layout_state(evs_state* s) {
+  const evs_model* m = s->m;
+  const int d = m->desc.d_model, es = m->es, B = s->B;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  s->off_t = take(4 * (size_t)B);
+  s->off_ib = take(4 * (size_t)B);
+  s->off_is = take(4 * (size_t)B);
+  s->off_err = take(4);
+  const size_t nb = m->blocks.size();
+  s->ring.assign(nb, 0); s->iir.assign(nb, 0); s->kc.assign(nb, 0); s->vt.assign(nb, 0); s->R.assign(nb, 0);
+  for (size_t i = 0; i < nb; ++i) {
+    const evs_block_desc& b = m->blocks[i];
+    if (b.kind == EVS_FIR) {
+      s->R[i] = next_pow2(b.fir_len - 1 + s->max_block);
+      s->ring[i] = take((size_t)B * s->R[i] * d * 4);
+    } else if (b.kind == EVS_IIR) {
+      s->iir[i] = take((size_t)B * 2 * s->max_block * d * b.iir_states * 4);
+    } else if (b.kind == EVS_ATTN) {
+      s->kc[i] = take((size_t)B * b.n_heads * s->cap * b.head_dim * es);
+      s->vt[i] = take((size_t)B * b.n_heads * s->cap * b.head_dim * es);
+    }
+  }
+  s->state_total = off;
+
+  // workspace
+  const int M = s->M_max;
+  off = 0;
+  s->w_x = take((size_t)M * d * 4);
+  s->w_nrm = take((size_t)(d / 16) * M * 4);
+  s->w_o = take((size_t)M * d * es);
+  s->w_q = take((size_t)M * d * es);
+  s->w_h = take((size_t)M * std::max(m->max_dff, 16) * es);
+  s->w_logit = take((size_t)s->max_block * m->desc.vocab * es);
+  // split-K partials: the largest requirement over every block size and batch
+  size_t pf = 0;
+  for (int P = 1; P <= s->max_block; ++P) {
+    for (int nseq : {1, B}) {
+      const Slicing sl = slicing(nseq, P);
+      auto acc = [&](const Mat& mm) {
+        const int ks = choose_ks(mm.n_groups, mm.K / m->kstep, sl.slices);
+        if (ks > 1) pf = std::max(pf, (size_t)sl.slices * mm.n_groups * ks * mm.NT * sl.MT * 256);
+      };
+      for (const auto& p : m->plan) {
+        if (p.d.kind == EVS_MLP) { acc(p.w_gu); acc(p.w_down); }
+        else { acc(p.w_in); acc(p.w_out); }
+      }
+      acc(m->lm);
+    }
+  }
+  s->part_floats = std::max<size_t>(pf, 256);
+  s->w_part = take(s->part_floats * 4);
+  s->w_cnt = take((size_t)GEMM_CNT * 4);
+  const int H = std::max(m->max_heads, 1), DHm = std::max(m->max_dh, 32);
+  s->qtn_max = (s->max_block + 15) / 16;
+  s->apart_floats = (size_t)B * s->qtn_max * H * s->S * 16 * (DHm + 2);
+  s->w_apart = take(s->apart_floats * 4);
+  s->acnt_n = (size_t)B * s->qtn_max * H;
+  s->w_acnt = take(s->acnt_n * 4);
+  s->ws_total = off;
+}
+
+template <typename T> T* sp(evs_state* s, size_t off) { return reinterpret_cast<T*>(s->sb + off); }
+template <typename T> T* wp(evs_state* s, size_t off) { return reinterpret_cast<T*>(s->wb + off); }
+
+evs_status hip_ok(hipError_t e) { return e == hipSuccess ? EVS_OK : EVS_E_HIP; }
+
+hipEvent_t pool_event(evs_state* s) {
+  if (!s->pool.empty()) { hipEvent_t e = s->pool.back(); s->pool.pop_back(); return e; }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Time one launch when the state's timing is on: `launch` enqueues the kernel.
+template <typename F>
+hipError_t timed(evs_state* s, int kc, double bytes, hipStream_t st, F&& launch) {
+  if (!s->timing) return launch();
+  hipEvent_t a = pool_event(s), b = pool_event(s);
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, st);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, st);
+  if (e != hipSuccess) return e;
+  s->recs.push_back({a, b, kc, bytes});
+  return hipSuccess;
+}
+#define EVS_TRY(x) do { evs_status _st = (x); if (_st != EVS_OK) return _st; } while (0)
+#define HIP_TRY(x) do { if ((x) != hipSuccess) return EVS_E_HIP; } while (0)
+
+// ------------------------------------------------------------------ forward
+template <typename T>
+evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int epi, const void* A, int lda,
+                     int nseq, int P, GemmArgs a, hipStream_t st, int scratch_floats = 0) {
+  const Slicing sl = slicing(nseq, P);
+  a.W = reinterpret_cast<const uint4*>(m->base + mat.off);
+  a.ksteps = mat.K / m->kstep;
+  a.n_groups = mat.n_groups;
+  a.KS = choose_ks(mat.n_groups, a.ksteps, sl.slices);
+  a.kps = (a.ksteps + a.KS - 1) / a.KS;
+  a.A = A;
+  a.lda = lda;
+  a.M = nseq * P;
+  a.rows_per_slice = sl.rows_per_slice;
+  a.nrm_part = wp<float>(s, s->w_nrm);
+  a.n_part = m->desc.d_model / 16;
+  a.nrm_ld = s->M_max;
+  a.fd = (float)m->desc.d_model;
+  a.eps = m->desc.norm_eps;
+  a.part = wp<float>(s, s->w_part);
+  a.cnt = wp<int>(s, s->w_cnt);
+  if (a.KS > 1) {
+    if ((size_t)sl.slices * mat.n_groups * a.KS * mat.NT * sl.MT * 256 > s->part_floats) return EVS_E_RANGE;
+    if ((size_t)sl.slices * mat.n_groups > (size_t)GEMM_CNT) return EVS_E_RANGE;
+  }
+  const size_t lds = gemm_lds(sl.MT, mat.NT, scratch_floats);
+  if (lds > 65536) return EVS_E_UNSUPPORTED;
+  // algorithmic bytes: the weights once, the A rows once, the outputs once
+  const double bytes = (double)mat.bytes(m->es) + (double)a.M * mat.K * (amode == A_NORM ? 4 : m->es) +
+                       (double)a.M * mat.rows_valid * (epi == E_RESID ? 8 : m->es);
+  return hip_ok(timed(s, EVS_KC_GEMM, bytes, st,
+                      [&] { return launch_gemm<T>(sl.MT, mat.NT, amode, epi, a, sl.slices, lds, st); }));
+}
+
+template <typename T>
+evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const int32_t* tokens, void* logits,
+                   hipStream_t st) {
+  const int d = m->desc.d_model, M = nseq * P;
+  float* x = wp<float>(s, s->w_x);
+  float* nrm = wp<float>(s, s->w_nrm);
+  int* t = sp<int>(s, s->off_t);
+  int* err = sp<int>(s, s->off_err);
+  HIP_TRY(launch_embed<T>(tokens, reinterpret_cast<const T*>(m->base + m->embed), x, nrm, s->M_max, M, d,
+                          m->desc.vocab, P, seq0, t, s->max_ctx, err, st));
+  for (size_t i = 0; i < m->plan.size(); ++i) {
+    const BlockPlan& p = m->plan[i];
+    GemmArgs a{};
+    if (p.d.kind == EVS_MLP) {
+      a.out = wp<void>(s, s->w_h);
+      a.ldo = p.d.d_ff;
+      EVS_TRY(gemm_call<T>(m, s, p.w_gu, A_NORM, E_GELU, x, d, nseq, P, a, st));
+      GemmArgs b{};
+      b.x = x; b.ldx = d; b.nrm_out = nrm;
+      EVS_TRY(gemm_call<T>(m, s, p.w_down, A_ACT, E_RESID, wp<void>(s, s->w_h), p.d.d_ff, nseq, P, b, st));
+      continue;
+    }
+    MixArgs& mx = a.mix;
+    mx.d = d; mx.P = P; mx.seq0 = seq0; mx.t = t;
+    mx.iir_buf = sp<int>(s, s->off_ib); mx.iir_slot = sp<int>(s, s->off_is); mx.err = err;
+    int scratch = 0;
+    if (p.d.kind == EVS_FIR) {
+      mx.kind = MIX_FIR;
+      mx.ring = sp<float>(s, s->ring[i]); mx.R = s->R[i]; mx.ring_bs = (long long)s->R[i] * d;
+      mx.taps = reinterpret_cast<const float*>(m->base + p.taps); mx.L = p.d.fir_len;
+      scratch = (p.d.fir_len - 1 + P) * 16 + 16 * p.d.fir_len;   // window + taps
+      a.out = wp<void>(s, s->w_o);
+    } else if (p.d.kind == EVS_IIR) {
+      mx.kind = MIX_IIR;
+      mx.iirst = sp<float>(s, s->iir[i]); mx.N = p.d.iir_states;
+      mx.iir_buf_s = (long long)s->max_block * d * p.d.iir_states;
+      mx.iir_bs = 2 * mx.iir_buf_s;
+      mx.lam = reinterpret_cast<const float*>(m->base + p.lam);
+      mx.res = reinterpret_cast<const float*>(m->base + p.res);
+      a.out = wp<void>(s, s->w_o);
+    } else {
+      mx.kind = MIX_ATTN;
+      mx.kc = sp<void>(s, s->kc[i]); mx.vt = sp<void>(s, s->vt[i]);
+      mx.kv_bs = (long long)p.d.n_heads * s->cap * p.d.head_dim; mx.cap = s->cap; mx.Dh = p.d.head_dim;
+      a.out = wp<void>(s, s->w_q);
+    }
+    a.ldo = d;
+    EVS_TRY(gemm_call<T>(m, s, p.w_in, A_NORM, E_MIXER, x, d, nseq, P, a, st, scratch));
+    if (p.d.kind == EVS_ATTN) {
+      AttnArgs at{};
+      at.q = wp<void>(s, s->w_q); at.out = wp<void>(s, s->w_o);
+      at.kc = mx.kc; at.vt = mx.vt; at.kv_bs = mx.kv_bs; at.cap = s->cap;
+      at.H = p.d.n_heads; at.Dh = p.d.head_dim; at.d = d; at.P = P; at.QTN = (P + 15) / 16; at.S = s->S;
+      at.seq0 = seq0; at.t = t; at.scale = 1.0f / std::sqrt((float)p.d.head_dim);
+      at.part = wp<float>(s, s->w_apart); at.cnt = wp<int>(s, s->w_acnt);
+      if ((size_t)nseq * at.QTN * at.H * at.S * 16 * (at.Dh + 2) > s->apart_floats) return EVS_E_RANGE;
+      // algorithmic bytes: K and V rows up to each sequence's block end (bounded
+      // here by the capacity-limited length known on the host: the state's
+      // committed lengths live on the device), q in, o out
+      const double kvb = (double)nseq * at.H * at.Dh * m->es * 2.0 * (double)s->timing_ctx;
+      HIP_TRY(timed(s, EVS_KC_ATTN, kvb + 2.0 * nseq * P * d * m->es, st, [&] { return launch_attn<T>(at, nseq, st); }));
+    }
+    GemmArgs b{};
+    b.x = x; b.ldx = d; b.nrm_out = nrm;
+    EVS_TRY(gemm_call<T>(m, s, p.w_out, A_ACT, E_RESID, wp<void>(s, s->w_o), d, nseq, P, b, st));
+  }
+  if (logits) {
+    GemmArgs a{};
+    a.N = m->desc.vocab; a.out = logits; a.ldo = m->desc.vocab;
+    EVS_TRY(gemm_call<T>(m, s, m->lm, A_NORM, E_STORE, x, d, nseq, P, a, st));
+  }
+  return EVS_OK;
+}
+
+evs_status forward_any(evs_model* m, evs_state* s, int seq0, int nseq, int P, const int32_t* tokens, void* logits,
+                       hipStream_t st) {
+  if (m->desc.dtype == EVS_BF16) return forward<bf16>(m, s, seq0, nseq, P, tokens, logits, st);
+  return forward<float>(m, s, seq0, nseq, P, tokens, logits, st);
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+extern "C" {
+
+const char* evs_status_string(evs_status s) {
+  switch (s) {
+    case EVS_OK: return "ok";
+    case EVS_E_INVALID: return "invalid argument";
+    case EVS_E_RANGE: return "size out of range for this state";
+    case EVS_E_STATE: return "call out of order";
+    case EVS_E_HIP: return "HIP runtime error";
+    case EVS_E_UNSUPPORTED: return "unsupported configuration";
+  }
+  return "unknown status";
+}
+
+evs_status evs_canonical_count(const evs_model_desc* desc, int32_t* count) {
+  if (!count || !check_desc(desc)) return EVS_E_INVALID;
+  *count = (int32_t)canon_list(desc).size();
+  return EVS_OK;
+}
+
+evs_status evs_canonical_shape(const evs_model_desc* desc, int32_t i, int64_t* rows, int64_t* cols,
+                               int32_t* dtype) {
+  if (!rows || !cols || !dtype || !check_desc(desc)) return EVS_E_INVALID;
+  const auto v = canon_list(desc);
+  if (i < 0 || (size_t)i >= v.size()) return EVS_E_RANGE;
+  *rows = v[i].rows; *cols = v[i].cols; *dtype = v[i].dtype;
+  return EVS_OK;
+}
+
+evs_status evs_weights_bytes(const evs_model_desc* desc, size_t* bytes) {
+  if (!bytes || !check_desc(desc)) return EVS_E_INVALID;
+  evs_model tmp;
+  plan_model(desc, &tmp);
+  *bytes = tmp.total;
+  return EVS_OK;
+}
+
+evs_status evs_model_create(const evs_model_desc* desc, void* packed_dev, evs_model** out) {
+  if (!out || !packed_dev || !check_desc(desc) || ((uintptr_t)packed_dev % ALIGN)) return EVS_E_INVALID;
+  evs_model* m = new (std::nothrow) evs_model();
+  if (!m) return EVS_E_INVALID;
+  plan_model(desc, m);
+  m->base = reinterpret_cast<char*>(packed_dev);
+  *out = m;
+  return EVS_OK;
+}
+
+void evs_model_destroy(evs_model* m) { delete m; }
+
+evs_status evs_pack_weights(evs_model* m, const void* const* canon, void* stream) {
+  if (!m || !canon) return EVS_E_INVALID;
+  const auto list = canon_list(&m->desc);
+  for (size_t i = 0; i < list.size(); ++i)
+    if (!canon[i] || ((uintptr_t)canon[i] % 16)) return EVS_E_INVALID;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool bf = m->desc.dtype == EVS_BF16;
+  auto pack = [&](const void* src, const Mat& mm) -> hipError_t {
+    uint4* dst = reinterpret_cast<uint4*>(m->base + mm.off);
+    if (bf) return launch_pack<bf16>(reinterpret_cast<const bf16*>(src), dst, mm.rows_valid, mm.K, mm.n_groups, mm.NT,
+                                     mm.map_kind, mm.map_stride, st);
+    return launch_pack<float>(reinterpret_cast<const float*>(src), dst, mm.rows_valid, mm.K, mm.n_groups, mm.NT,
+                              mm.map_kind, mm.map_stride, st);
+  };
+  auto copy = [&](const void* src, size_t off, size_t bytes) {
+    return launch_copy_row(src, m->base + off, bytes, st);
+  };
+  const int d = m->desc.d_model;
+  size_t k = 0;
+  HIP_TRY(copy(canon[k++], m->embed, (size_t)m->desc.vocab * d * m->es));
+  for (const auto& p : m->plan) {
+    if (p.d.kind == EVS_MLP) {
+      HIP_TRY(pack(canon[k++], p.w_gu));
+      HIP_TRY(pack(canon[k++], p.w_down));
+      continue;
+    }
+    HIP_TRY(pack(canon[k++], p.w_in));
+    if (p.d.kind == EVS_FIR) HIP_TRY(copy(canon[k++], p.taps, (size_t)d * p.d.fir_len * 4));
+    if (p.d.kind == EVS_IIR) {
+      HIP_TRY(copy(canon[k++], p.lam, (size_t)d * p.d.iir_states * 4));
+      HIP_TRY(copy(canon[k++], p.res, (size_t)d * p.d.iir_states * 4));
+    }
+    HIP_TRY(pack(canon[k++], p.w_out));
+  }
+  HIP_TRY(pack(canon[k++], m->lm));
+  return EVS_OK;
+}
+
+static evs_status state_setup(const evs_model* m, int32_t batch, int32_t max_ctx, int32_t max_block, evs_state* s) {
+  if (!m || batch < 1 || max_ctx < 1 || max_block < 1 || max_block > MAX_ROWS_PER_WG) return EVS_E_INVALID;
+  if ((long long)batch * max_block > 4096 || batch > 4096) return EVS_E_RANGE;
+  s->m = m;
+  s->B = batch;
+  s->max_ctx = max_ctx;
+  s->max_block = max_block;
+  s->cap = (int)align_up((size_t)max_ctx, ATTN_CHUNK);
+  s->S = std::min(64, std::max(1, s->cap / (2 * ATTN_CHUNK)));
+  s->M_max = batch * max_block;
+  layout_state(s);
+  return EVS_OK;
+}
+
+evs_status evs_state_bytes(const evs_model* m, int32_t batch, int32_t max_ctx, int32_t max_block,
+                           size_t* state_bytes, size_t* workspace_bytes) {
+  if (!state_bytes || !workspace_bytes) return EVS_E_INVALID;
+  evs_state tmp;
+  EVS_TRY(state_setup(m, batch, max_ctx, max_block, &tmp));
+  *state_bytes = tmp.state_total;
+  *workspace_bytes = tmp.ws_total;
+  return EVS_OK;
+}
+
+evs_status evs_state_create(const evs_model* m, int32_t batch, int32_t max_ctx, int32_t max_block, void* state_dev,
+                            void* workspace_dev, void* stream, evs_state** out) {
+  if (!out || !state_dev || !workspace_dev || ((uintptr_t)state_dev % ALIGN) || ((uintptr_t)workspace_dev % ALIGN))
+    return EVS_E_INVALID;
+  evs_state* s = new (std::nothrow) evs_state();
+  if (!s) return EVS_E_INVALID;
+  evs_status stt = state_setup(m, batch, max_ctx, max_block, s);
+  if (stt != EVS_OK) { delete s; return stt; }
+  s->sb = reinterpret_cast<char*>(state_dev);
+  s->wb = reinterpret_cast<char*>(workspace_dev);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (e == hipSuccess) e = launch_fill_i32(sp<int>(s, s->off_t), 0, batch, st);
+  if (e == hipSuccess) e = launch_fill_i32(sp<int>(s, s->off_ib), 0, batch, st);
+  if (e == hipSuccess) e = launch_fill_i32(sp<int>(s, s->off_is), -1, batch, st);
+  if (e == hipSuccess) e = launch_fill_i32(sp<int>(s, s->off_err), 0, 1, st);
+  if (e == hipSuccess) e = launch_fill_i32(wp<int>(s, s->w_cnt), 0, GEMM_CNT, st);
+  if (e == hipSuccess) e = launch_fill_i32(wp<int>(s, s->w_acnt), 0, (long long)s->acnt_n, st);
+  if (e != hipSuccess) { delete s; return EVS_E_HIP; }
+  *out = s;
+  return EVS_OK;
+}
+
+void evs_state_destroy(evs_state* s) { delete s; }
+
+evs_status evs_state_tensor(const evs_state* s, int32_t what, int32_t block, evs_tensor_desc* o) {
+  if (!s || !o) return EVS_E_INVALID;
+  std::memset(o, 0, sizeof(*o));
+  const evs_model* m = s->m;
+  const int B = s->B, d = m->desc.d_model;
+  const int dt = m->desc.dtype;
+  auto need_block = [&](int kind) {
+    return block >= 0 && (size_t)block < m->blocks.size() && m->blocks[block].kind == kind;
+  };
+  auto set = [&](uint64_t off, int dtype, std::initializer_list<int64_t> shape) {
+    o->offset = off; o->dtype = dtype; o->ndim = (int32_t)shape.size();
+    int i = 0;
+    for (int64_t v : shape) o->shape[i++] = v;
+    int64_t st = 1;
+    for (int k = o->ndim - 1; k >= 0; --k) { o->strides[k] = st; st *= o->shape[k]; }
+  };
+  switch (what) {
+    case EVS_ST_T: set(s->off_t, EVS_I32, {B}); return EVS_OK;
+    case EVS_ST_IIR_BUF: set(s->off_ib, EVS_I32, {B}); return EVS_OK;
+    case EVS_ST_IIR_SLOT: set(s->off_is, EVS_I32, {B}); return EVS_OK;
+    case EVS_ST_ERROR: set(s->off_err, EVS_I32, {1}); return EVS_OK;
+    case EVS_ST_FIR_RING:
+      if (!need_block(EVS_FIR)) return EVS_E_INVALID;
+      set(s->ring[block], EVS_F32, {B, s->R[block], d});
+      return EVS_OK;
+    case EVS_ST_IIR:
+      if (!need_block(EVS_IIR)) return EVS_E_INVALID;
+      set(s->iir[block], EVS_F32, {B, 2, s->max_block, d, m->blocks[block].iir_states});
+      return EVS_OK;
+    case EVS_ST_K:
+      if (!need_block(EVS_ATTN)) return EVS_E_INVALID;
+      set(s->kc[block], dt, {B, m->blocks[block].n_heads, s->cap, m->blocks[block].head_dim});
+      return EVS_OK;
+    case EVS_ST_VT:
+      if (!need_block(EVS_ATTN)) return EVS_E_INVALID;
+      set(s->vt[block], dt, {B, m->blocks[block].n_heads, m->blocks[block].head_dim, s->cap});
+      return EVS_OK;
+    default: return EVS_E_INVALID;
+  }
+}
+
+evs_status evs_state_error(evs_state* s, int32_t* host_word, int32_t clear, void* stream) {
+  if (!s || !host_word) return EVS_E_INVALID;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  HIP_TRY(hipStreamSynchronize(st));
+  HIP_TRY(hipMemcpy(host_word, sp<int>(s, s->off_err), 4, hipMemcpyDeviceToHost));
+  if (clear) {
+    HIP_TRY(launch_fill_i32(sp<int>(s, s->off_err), 0, 1, st));
+    HIP_TRY(hipStreamSynchronize(st));
+  }
+  return EVS_OK;
+}
+
+evs_status evs_prefill(evs_model* m, evs_state* s, const int32_t* tokens, const int32_t* offs, void* last_logits,
+                       void* stream) {
+  if (!m || !s || !tokens || !offs || s->m != m) return EVS_E_INVALID;
+  if (s->pending) return EVS_E_STATE;
+  for (int b = 0; b < s->B; ++b)
+    if (offs[b + 1] < offs[b] || offs[b] < 0) return EVS_E_INVALID;
+  for (int b = 0; b < s->B; ++b)
+    if (offs[b + 1] - offs[b] > s->max_ctx) return EVS_E_RANGE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int V = m->desc.vocab;
+  const int chunk = s->max_block;
+  for (int b = 0; b < s->B; ++b) {
+    const int n = offs[b + 1] - offs[b];
+    for (int a = 0; a < n; a += chunk) {
+      const int P = std::min(chunk, n - a);
+      const bool last = a + P == n;
+      void* lg = (last && last_logits) ? wp<void>(s, s->w_logit) : nullptr;
+      EVS_TRY(forward_any(m, s, b, 1, P, tokens + offs[b] + a, lg, st));
+      HIP_TRY(launch_commit(sp<int>(s, s->off_t) + b, sp<int>(s, s->off_ib) + b, sp<int>(s, s->off_is) + b,
+                            nullptr, P, 1, P, sp<int>(s, s->off_err), st));
+      if (lg)
+        HIP_TRY(launch_copy_row(wp<char>(s, s->w_logit) + (size_t)(P - 1) * V * m->es,
+                                reinterpret_cast<char*>(last_logits) + (size_t)b * V * m->es, (size_t)V * m->es, st));
+    }
+  }
+  return EVS_OK;
+}
+
+evs_status evs_block_verify(evs_model* m, evs_state* s, const int32_t* cand, int32_t gamma, void* logits,
+                            void* stream) {
+  if (!m || !s || !cand || !logits || s->m != m) return EVS_E_INVALID;
+  if (gamma < 0 || gamma + 1 > s->max_block) return EVS_E_RANGE;
+  s->pending = false;   // a pending block is discarded (rollback to 0 changes nothing on device)
+  EVS_TRY(forward_any(m, s, 0, s->B, gamma + 1, cand, logits, reinterpret_cast<hipStream_t>(stream)));
+  s->pending = true;
+  s->pending_P = gamma + 1;
+  return EVS_OK;
+}
+
+evs_status evs_rollback(evs_state* s, const int32_t* n_keep, void* stream) {
+  if (!s) return EVS_E_INVALID;
+  if (!s->pending) return EVS_E_STATE;
+  HIP_TRY(launch_commit(sp<int>(s, s->off_t), sp<int>(s, s->off_ib), sp<int>(s, s->off_is), n_keep, s->pending_P,
+                        s->B, s->pending_P, sp<int>(s, s->off_err), reinterpret_cast<hipStream_t>(stream)));
+  s->pending = false;
+  return EVS_OK;
+}
+
+evs_status evs_verify_sample(int32_t batch, int32_t gamma, int32_t vocab, const void* target, int32_t kind,
+                             const float* q, const int32_t* draft, const float* u, float temperature, int32_t top_k,
+                             int32_t greedy, int32_t* n_acc, int32_t* next, int32_t* n_keep, int32_t* err,
+                             void* stream) {
+  if (batch < 1 || gamma < 0 || gamma > 63 || vocab < 2 || !target || !n_acc || !next) return EVS_E_INVALID;
+  if (kind != EVS_TARGET_LOGITS_BF16 && kind != EVS_TARGET_LOGITS_F32 && kind != EVS_TARGET_PROBS_F32)
+    return EVS_E_INVALID;
+  if (gamma > 0 && !draft) return EVS_E_INVALID;
+  if (!greedy && (!u || (gamma > 0 && !q))) return EVS_E_INVALID;
+  if (!greedy && kind != EVS_TARGET_PROBS_F32 && !(temperature > 0.f)) return EVS_E_INVALID;
+  if ((long long)(gamma + 2) * vocab > 15872) return EVS_E_UNSUPPORTED;   // LDS: 62 KB of fp32 rows
+  VerifyArgs a{};
+  a.gamma = gamma; a.V = vocab; a.kind = kind; a.top_k = top_k; a.greedy = greedy ? 1 : 0;
+  a.temperature = temperature; a.target = target; a.q = q; a.draft = draft; a.u = u;
+  a.n_acc = n_acc; a.next = next; a.n_keep = n_keep; a.err = err;
+  return hip_ok(launch_verify(a, batch, reinterpret_cast<hipStream_t>(stream)));
+}
+
+evs_status evs_state_timing(evs_state* s, int32_t enable, int64_t context_hint) {
+  if (!s) return EVS_E_INVALID;
+  s->timing = enable != 0;
+  s->timing_ctx = context_hint;
+  return EVS_OK;
+}
+
+evs_status evs_state_timing_read(evs_state* s, int32_t kernel_class, double* total_ms, int64_t* launches,
+                                 double* bytes, void* stream) {
+  if (!s || !total_ms || !launches || !bytes) return EVS_E_INVALID;
+  HIP_TRY(hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)));
+  double ms = 0, by = 0;
+  int64_t n = 0;
+  std::vector<evs_state::Rec> keep;
+  for (auto& r : s->recs) {
+    if (r.kc != kernel_class) { keep.push_back(r); continue; }
+    float e = 0.f;
+    HIP_TRY(hipEventElapsedTime(&e, r.a, r.b));
+    ms += e;
+    by += r.bytes;
+    ++n;
+    s->pool.push_back(r.a);
+    s->pool.push_back(r.b);
+  }
+  s->recs.swap(keep);
+  *total_ms = ms;
+  *launches = n;
+  *bytes = by;
+  return EVS_OK;
+}
+
+}  // extern "C"

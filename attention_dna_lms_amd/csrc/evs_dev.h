@@ -1,0 +1,140 @@
+// Device-side types, MFMA fragments and kernel argument blocks shared by the
+// HIP kernels of the block-verification path (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace evs {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// A 16-byte fragment per lane feeds one 16x16 MFMA step: E elements of the
+// storage type, KSTEP = 4 * E reduction slots per step for the whole wave.
+template <typename T> struct St;
+template <> struct St<bf16> { static constexpr int E = 8, KSTEP = 32; };
+template <> struct St<float> { static constexpr int E = 4, KSTEP = 16; };
+
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+// value as held in storage type T (round-to-nearest-even for bf16)
+template <typename T> __device__ __forceinline__ float rnd(float x) { return to_f(from_f<T>(x)); }
+
+// D += A * B for one 16x16 tile. Fragments: lane l holds row (l % 16) of A and
+// column (l % 16) of B over the same reduction slots; D: lane l holds rows
+// 4*(l/16) + i (i = 0..3) of column l % 16.
+__device__ __forceinline__ f32x4 mma_frag(uint4 a, uint4 b, f32x4 c, bf16) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_frag(uint4 a, uint4 b, f32x4 c, float) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  return c;
+}
+// Four reduction slots per lane group (lane l holds slots 4*(l/16) .. +3).
+__device__ __forceinline__ f32x4 mma_k4(const float a[4], const float b[4], f32x4 c, bf16) {
+  bf16x4 av, bv;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { av[j] = (bf16)a[j]; bv[j] = (bf16)b[j]; }
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, av),
+                                                   __builtin_bit_cast(s16x4, bv), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_k4(const float a[4], const float b[4], f32x4 c, float) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+  return c;
+}
+
+// ------------------------------------------------------------------ GEMM args
+enum AMode { A_ACT = 0, A_NORM = 1 };                      // storage-type rows / fp32 rows + RMSNorm
+enum Epi { E_STORE = 0, E_RESID = 1, E_GELU = 2, E_MIXER = 3 };
+enum MixKind { MIX_FIR = 1, MIX_IIR = 2, MIX_ATTN = 3 };
+
+struct MixArgs {
+  int kind;
+  int d;                 // channels
+  int P;                 // positions per sequence in this call
+  int seq0;              // state index of the sequence owning row 0
+  const int* t;          // [B] committed lengths
+  const int* iir_buf;    // [B]
+  const int* iir_slot;   // [B]
+  int* err;              // sticky error word
+  // FIR
+  float* ring; int R; long long ring_bs; const float* taps; int L;
+  // IIR
+  float* iirst; long long iir_bs; long long iir_buf_s; int N; const float* lam; const float* res;
+  // ATTN
+  void* kc; void* vt; long long kv_bs; int cap; int Dh;
+};
+
+struct GemmArgs {
+  const uint4* W;        // packed [n_groups][ksteps][NT][64] fragments
+  int ksteps;            // K / KSTEP
+  int n_groups;
+  int KS;                // k-splits across workgroups (grid.x = n_groups * KS)
+  int kps;               // k-steps per split
+  const void* A;         // A_ACT: T [M, lda]; A_NORM: f32 [M, lda]
+  int lda;
+  int M;                 // rows in this call
+  int rows_per_slice;    // rows per blockIdx.y (a multiple of the positions per sequence)
+  const float* nrm_part; int n_part; int nrm_ld; float fd; float eps;      // A_NORM (fd = d)
+  float* part; int* cnt;                                                     // split-K scratch
+  // epilogue
+  int N;                 // valid output columns (E_STORE)
+  void* out; int ldo;    // E_STORE / E_GELU / E_MIXER output (storage type)
+  float* x; int ldx;     // E_RESID residual stream
+  float* nrm_out;        // E_RESID per-16-column sum of squares [n_tiles][nrm_ld]
+  MixArgs mix;
+};
+
+struct AttnArgs {
+  const void* q;         // [M, d] storage type
+  void* out;             // [M, d]
+  const void* kc;        // [B, H, cap, Dh]
+  const void* vt;        // [B, H, Dh, cap]
+  long long kv_bs;       // per-sequence stride (elements) of kc / vt
+  int cap, H, Dh, d, P, QTN, S, seq0;
+  const int* t;
+  float scale;
+  float* part;           // [B_call, QTN, H, S, 16, Dh + 2]
+  int* cnt;              // [B_call, QTN, H]
+};
+
+constexpr int ATTN_CHUNK = 256;   // keys per chunk (4 waves x 4 tiles of 16)
+
+struct VerifyArgs {
+  int gamma, V, kind, top_k, greedy;
+  float temperature;
+  const void* target; const float* q; const int* draft; const float* u;
+  int* n_acc; int* next; int* n_keep; int* err;
+};
+
+// ------------------------------------------------------------------ launchers
+template <typename T>
+hipError_t launch_gemm(int MT, int NT, int amode, int epi, const GemmArgs& a, int slices,
+                       size_t lds_bytes, hipStream_t st);
+template <typename T>
+hipError_t launch_attn(const AttnArgs& a, int n_seq, hipStream_t st);
+template <typename T>
+hipError_t launch_embed(const int* tokens, const T* E, float* x, float* nrm, int nrm_ld, int M, int d,
+                        int V, int P, int seq0, const int* t, int max_ctx, int* err, hipStream_t st);
+hipError_t launch_commit(int* t, int* iir_buf, int* iir_slot, const int* n_keep, int n_keep_all,
+                         int B, int P, int* err, hipStream_t st);
+hipError_t launch_fill_i32(int* p, int v, long long n, hipStream_t st);
+template <typename T>
+hipError_t launch_pack(const T* W, uint4* out, int rows_valid, int K, int n_groups, int NT,
+                       int map_kind, int map_stride, hipStream_t st);
+hipError_t launch_copy_row(const void* src, void* dst, size_t bytes, hipStream_t st);
+hipError_t launch_verify(const VerifyArgs& a, int B, hipStream_t st);
+
+}  // namespace evs

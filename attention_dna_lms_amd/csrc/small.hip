@@ -1,0 +1,326 @@
+// Small kernels of the path: embedding gather, state commit (the rollback),
+// weight packing, fills, and the fused verifier.
+#include <math.h>
+
+#include "evs_dev.h"
+
+namespace evs {
+
+// ---------------------------------------------------------------- embedding
+// x[m, :] = E[tok[m], :] in fp32, plus the per-16-column sums of squares the
+// first RMSNorm reads. One thread per (row, 16-column tile). Also flags a
+// block that would run past the context capacity.
+template <typename T>
+__global__ void embed_kernel(const int* __restrict__ tokens, const T* __restrict__ E, float* x, float* nrm,
+                             int nrm_ld, int M, int d, int V, int P, int seq0, const int* t, int max_ctx,
+                             int* err) {
+  const int ntile = d / 16;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= M * ntile) return;
+  const int m = idx / ntile, tile = idx % ntile;
+  int tok = tokens[m];
+  if (tok < 0 || tok >= V) {
+    if (tile == 0) atomicOr(err, 1);
+    tok = 0;
+  }
+  if (tile == 0 && m % P == 0 && t[seq0 + m / P] + P > max_ctx) atomicOr(err, 2);
+  const T* e = E + (size_t)tok * d + tile * 16;
+  float* xr = x + (size_t)m * d + tile * 16;
+  float ss = 0.f;
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    const float v = to_f(e[n]);
+    xr[n] = v;
+    ss = fmaf(v, v, ss);
+  }
+  nrm[(size_t)tile * nrm_ld + m] = ss;
+}
+
+template <typename T>
+hipError_t launch_embed(const int* tokens, const T* E, float* x, float* nrm, int nrm_ld, int M, int d, int V,
+                        int P, int seq0, const int* t, int max_ctx, int* err, hipStream_t st) {
+  const int n = M * (d / 16);
+  embed_kernel<T><<<(n + 255) / 256, 256, 0, st>>>(tokens, E, x, nrm, nrm_ld, M, d, V, P, seq0, t, max_ctx, err);
+  return hipGetLastError();
+}
+template hipError_t launch_embed<bf16>(const int*, const bf16*, float*, float*, int, int, int, int, int, int,
+                                       const int*, int, int*, hipStream_t);
+template hipError_t launch_embed<float>(const int*, const float*, float*, float*, int, int, int, int, int, int,
+                                        const int*, int, int*, hipStream_t);
+
+// ---------------------------------------------------------------- commit
+// Slice each sequence's state to its accepted boundary: the committed length
+// advances by n_keep and, if anything was kept, the IIR state pointer moves to
+// the buffer the block wrote and the slot of the last kept position. No state
+// bytes move (Evo2 discussion #232, "What we implemented": the state is sliced
+// directly to the accepted boundary).
+__global__ void commit_kernel(int* t, int* ib, int* is, const int* n_keep, int n_all, int B, int P, int* err) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  int n = n_keep ? n_keep[b] : n_all;
+  if (n < 0 || n > P) {
+    atomicOr(err, 4);
+    n = n < 0 ? 0 : P;
+  }
+  t[b] += n;
+  if (n > 0) {
+    ib[b] ^= 1;
+    is[b] = n - 1;
+  }
+}
+
+hipError_t launch_commit(int* t, int* ib, int* is, const int* n_keep, int n_all, int B, int P, int* err,
+                         hipStream_t st) {
+  commit_kernel<<<(B + 255) / 256, 256, 0, st>>>(t, ib, is, n_keep, n_all, B, P, err);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fills / copies
+__global__ void fill_i32_kernel(int* p, int v, long long n) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+hipError_t launch_fill_i32(int* p, int v, long long n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  long long blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  fill_i32_kernel<<<(int)blocks, 256, 0, st>>>(p, v, n);
+  return hipGetLastError();
+}
+
+__global__ void copy_bytes_kernel(const unsigned char* src, unsigned char* dst, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+hipError_t launch_copy_row(const void* src, void* dst, size_t bytes, hipStream_t st) {
+  if (!bytes) return hipSuccess;
+  size_t blocks = (bytes + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  copy_bytes_kernel<<<(int)blocks, 256, 0, st>>>((const unsigned char*)src, (unsigned char*)dst, bytes);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- packing
+// Canonical row-major W [rows, K] -> MFMA fragment stream
+// [n_groups][K/KSTEP][NT][64 lanes] of 16 bytes; lane l of (group g, step k,
+// tile nt) holds W[row][k*KSTEP + (l/16)*E .. + E-1] with row = the (l % 16)-th
+// row of that tile: consecutive tiles (map_kind 0) or tile g of section nt of
+// size map_stride (map_kind 1: q|k|v or gate|up kept side by side). Rows past
+// rows_valid are zero.
+template <typename T>
+__global__ void pack_kernel(const T* __restrict__ W, uint4* __restrict__ out, int rows_valid, int K, int n_groups,
+                            int NT, int map_kind, int map_stride) {
+  constexpr int E = St<T>::E, KSTEP = St<T>::KSTEP;
+  const int ksteps = K / KSTEP;
+  const long long total = (long long)n_groups * ksteps * NT * 64;
+  for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < total;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const int lane = (int)(idx % 64);
+    long long r1 = idx / 64;
+    const int nt = (int)(r1 % NT);
+    r1 /= NT;
+    const int k = (int)(r1 % ksteps);
+    const int g = (int)(r1 / ksteps);
+    const int r = lane % 16;
+    const long long row = map_kind == 0 ? (long long)(g * NT + nt) * 16 + r : (long long)nt * map_stride + g * 16 + r;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < rows_valid)
+      v = *reinterpret_cast<const uint4*>(W + row * (long long)K + (long long)k * KSTEP + (lane / 16) * E);
+    out[idx] = v;
+  }
+}
+
+template <typename T>
+hipError_t launch_pack(const T* W, uint4* out, int rows_valid, int K, int n_groups, int NT, int map_kind,
+                       int map_stride, hipStream_t st) {
+  pack_kernel<T><<<4096, 256, 0, st>>>(W, out, rows_valid, K, n_groups, NT, map_kind, map_stride);
+  return hipGetLastError();
+}
+template hipError_t launch_pack<bf16>(const bf16*, uint4*, int, int, int, int, int, int, hipStream_t);
+template hipError_t launch_pack<float>(const float*, uint4*, int, int, int, int, int, int, hipStream_t);
+
+// ---------------------------------------------------------------- verifier
+// One workgroup per sequence. Target distributions (softmax over the top-k of
+// logits / T) are built in parallel, one wave per position; the accept scan,
+// the residual normaliser and the inverse-CDF draw run in one lane in token
+// order, so every fp32 value matches a sequential evaluation exactly
+// (EvSpark preprint, abstract (iii): exact rejection-sampling verification).
+
+// total order used by top-k: larger value first, lower id on ties
+__device__ __forceinline__ bool ord_gt(float v1, int i1, float v2, int i2) {
+  return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float v2 = __shfl_xor(v, off);
+    const int i2 = __shfl_xor(i, off);
+    if (ord_gt(v2, i2, v, i)) { v = v2; i = i2; }
+  }
+}
+
+__device__ __forceinline__ float load_target(const VerifyArgs& a, size_t off) {
+  if (a.kind == 1) return to_f(reinterpret_cast<const bf16*>(a.target)[off]);
+  return reinterpret_cast<const float*>(a.target)[off];
+}
+
+__device__ int icdf_seq(const float* w, int V, float u, int fallback) {
+  float c = 0.f;
+  int last = -1;
+  for (int y = 0; y < V; ++y) {
+    c = c + w[y];
+    if (w[y] > 0.f) last = y;
+    if (c > u) return y;
+  }
+  return last >= 0 ? last : fallback;
+}
+
+__global__ void __launch_bounds__(256) verify_kernel(VerifyArgs a) {
+  extern __shared__ float sm[];
+  __shared__ int amax_s[64];
+  __shared__ int rej_s, nacc_s, next_s;
+  const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int gamma = a.gamma, P = gamma + 1, V = a.V;
+  const bool logits = a.kind != 3;
+  float* prob = sm;            // [P][V]
+  float* w = sm + (size_t)P * V;  // [V]
+
+  // phase 1: one wave per position, positions in rounds of 4 (uniform barriers)
+  __shared__ float ssum_s[4];
+  for (int i0 = 0; i0 < P; i0 += 4) {
+    const int i = i0 + wave;
+    const bool act = i < P;
+    float* pr = prob + (size_t)(act ? i : 0) * V;
+    const bool soft = act && !a.greedy && logits;
+    if (act) {
+      const size_t roff = ((size_t)b * P + i) * V;
+      float bv = -INFINITY;
+      int bi = 0;
+      for (int y = lane; y < V; y += 64) {
+        float z = load_target(a, roff + y);
+        if (isnan(z)) z = logits ? -INFINITY : 0.f;
+        pr[y] = z;
+        if (ord_gt(z, y, bv, bi)) { bv = z; bi = y; }
+      }
+      wave_argmax(bv, bi);
+      if (lane == 0) amax_s[i] = bi;
+    }
+    if (soft) {
+      // z / T, then the top-k threshold (the k-th element in the total order)
+      for (int y = lane; y < V; y += 64) pr[y] = pr[y] / a.temperature;
+      const bool all = a.top_k <= 0 || a.top_k >= V;
+      float tv = -INFINITY;
+      int ti = V;
+      if (!all) {
+        float pvv = INFINITY;
+        int pii = -1;
+        for (int r = 0; r < a.top_k; ++r) {
+          float cv = -INFINITY;
+          int ci = V;
+          for (int y = lane; y < V; y += 64) {
+            const float z = pr[y];
+            if (ord_gt(pvv, pii, z, y) && ord_gt(z, y, cv, ci)) { cv = z; ci = y; }
+          }
+          wave_argmax(cv, ci);
+          pvv = cv;
+          pii = ci;
+        }
+        tv = pvv;
+        ti = pii;
+      }
+      float m = -INFINITY;
+      for (int y = lane; y < V; y += 64) {
+        const float z = pr[y];
+        if ((all || !ord_gt(tv, ti, z, y)) && isfinite(z)) m = fmaxf(m, z);
+      }
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      for (int y = lane; y < V; y += 64) {
+        const float z = pr[y];
+        const bool keep = (all || !ord_gt(tv, ti, z, y)) && isfinite(z);
+        pr[y] = keep ? (float)exp((double)(z - m)) : 0.f;
+      }
+    }
+    __syncthreads();
+    if (soft && lane == 0) {
+      float S = 0.f;
+      for (int y = 0; y < V; ++y) S = S + pr[y];
+      ssum_s[wave] = S;
+    }
+    __syncthreads();
+    if (soft) {
+      const float S = ssum_s[wave];
+      for (int y = lane; y < V; y += 64) pr[y] = (S > 0.f) ? pr[y] / S : 0.f;
+    }
+    __syncthreads();
+  }
+
+  if (tid == 0) {
+    int n_acc = gamma, nxt = -1, rej = -1;
+    for (int i = 0; i < gamma; ++i) {
+      int x = a.draft[(size_t)b * gamma + i];
+      if (x < 0 || x >= V) {
+        if (a.err) atomicOr(a.err, 8);
+        x = x < 0 ? 0 : V - 1;
+      }
+      if (a.greedy) {
+        if (x != amax_s[i]) { n_acc = i; nxt = amax_s[i]; break; }
+      } else {
+        const float px = prob[(size_t)i * V + x];
+        float qx = a.q[((size_t)b * gamma + i) * V + x];
+        if (isnan(qx)) qx = 0.f;
+        const bool ok = qx > 0.f ? (a.u[(size_t)b * P + i] < px / qx) : (px > 0.f);
+        if (!ok) { n_acc = i; rej = i; break; }
+      }
+    }
+    if (a.greedy && nxt < 0) nxt = amax_s[gamma];
+    rej_s = rej;
+    nacc_s = n_acc;
+    next_s = nxt;
+  }
+  __syncthreads();
+  if (a.greedy) {
+    if (tid == 0) {
+      a.n_acc[b] = nacc_s;
+      a.next[b] = next_s;
+      if (a.n_keep) a.n_keep[b] = nacc_s + 1;
+    }
+    return;
+  }
+  const int rej = rej_s;
+  if (rej >= 0) {
+    const float* pr = prob + (size_t)rej * V;
+    const float* qr = a.q + ((size_t)b * gamma + rej) * V;
+    for (int y = tid; y < V; y += 256) {
+      float qv = qr[y];
+      if (isnan(qv)) qv = 0.f;
+      w[y] = fmaxf(0.f, pr[y] - qv);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const float uf = a.u[(size_t)b * P + gamma];
+    int nxt;
+    if (rej >= 0) {
+      float S = 0.f;
+      for (int y = 0; y < V; ++y) S = S + w[y];
+      if (S > 0.f)
+        nxt = icdf_seq(w, V, uf * S, amax_s[rej]);
+      else
+        nxt = icdf_seq(prob + (size_t)rej * V, V, uf, amax_s[rej]);
+    } else {
+      nxt = icdf_seq(prob + (size_t)gamma * V, V, uf, amax_s[gamma]);
+    }
+    a.n_acc[b] = nacc_s;
+    a.next[b] = nxt;
+    if (a.n_keep) a.n_keep[b] = nacc_s + 1;
+  }
+}
+
+hipError_t launch_verify(const VerifyArgs& a, int B, hipStream_t st) {
+  const size_t lds = ((size_t)(a.gamma + 2) * a.V) * sizeof(float);
+  verify_kernel<<<B, 256, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace evs

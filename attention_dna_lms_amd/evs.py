@@ -1,0 +1,268 @@
+"""Python binding of libevs (include/evs.h): ctypes marshalling only.
+
+Every function named evs_* here forwards to the C function of the same name;
+tensors are passed as device pointers and the current torch stream as the HIP
+stream. ``Model`` and ``State`` own the device buffers (torch tensors) that
+the C API asks the caller for. There is no fallback: if libevs.so is missing
+or cannot be loaded, importing the library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_uint64, c_void_p
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libevs.so")
+
+EVS_FIR, EVS_IIR, EVS_ATTN, EVS_MLP = 1, 2, 3, 4
+EVS_BF16, EVS_F32, EVS_I32 = 1, 2, 3
+EVS_TARGET_LOGITS_BF16, EVS_TARGET_LOGITS_F32, EVS_TARGET_PROBS_F32 = 1, 2, 3
+EVS_ST_T, EVS_ST_IIR_BUF, EVS_ST_IIR_SLOT, EVS_ST_FIR_RING, EVS_ST_IIR, EVS_ST_K, EVS_ST_VT, EVS_ST_ERROR = range(1, 9)
+EVS_ERR_TOKEN, EVS_ERR_CONTEXT, EVS_ERR_NKEEP, EVS_ERR_DRAFT = 1, 2, 4, 8
+STATUS = {0: "EVS_OK", -1: "EVS_E_INVALID", -2: "EVS_E_RANGE", -3: "EVS_E_STATE", -4: "EVS_E_HIP",
+          -5: "EVS_E_UNSUPPORTED"}
+_KINDS = {"fir": EVS_FIR, "iir": EVS_IIR, "attn": EVS_ATTN, "mlp": EVS_MLP}
+_TORCH_DT = {EVS_BF16: torch.bfloat16, EVS_F32: torch.float32, EVS_I32: torch.int32}
+
+# exported symbols declared in include/evs.h
+EXPORTS = ("evs_status_string", "evs_canonical_count", "evs_canonical_shape", "evs_weights_bytes",
+           "evs_model_create", "evs_pack_weights", "evs_model_destroy", "evs_state_bytes", "evs_state_create",
+           "evs_state_destroy", "evs_state_tensor", "evs_state_error", "evs_prefill", "evs_block_verify",
+           "evs_rollback", "evs_verify_sample", "evs_state_timing", "evs_state_timing_read")
+EVS_KC_GEMM, EVS_KC_ATTN = 1, 2
+
+
+class EvsError(RuntimeError):
+    def __init__(self, status, where):
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+class BlockDesc(ctypes.Structure):
+    _fields_ = [("kind", c_int32), ("fir_len", c_int32), ("iir_states", c_int32), ("n_heads", c_int32),
+                ("head_dim", c_int32), ("d_ff", c_int32)]
+
+
+class ModelDesc(ctypes.Structure):
+    _fields_ = [("d_model", c_int32), ("vocab", c_int32), ("n_blocks", c_int32), ("dtype", c_int32),
+                ("norm_eps", c_float), ("blocks", POINTER(BlockDesc))]
+
+
+class TensorDesc(ctypes.Structure):
+    _fields_ = [("offset", c_uint64), ("dtype", c_int32), ("ndim", c_int32), ("shape", c_int64 * 6),
+                ("strides", c_int64 * 6)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libevs.so (raises if it is absent or fails to load)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libevs.so not built ({LIB_PATH}); run python -m attention_dna_lms_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    L.evs_status_string.restype = ctypes.c_char_p
+    L.evs_status_string.argtypes = [c_int32]
+    sig = {
+        "evs_canonical_count": [POINTER(ModelDesc), POINTER(c_int32)],
+        "evs_canonical_shape": [POINTER(ModelDesc), c_int32, POINTER(c_int64), POINTER(c_int64), POINTER(c_int32)],
+        "evs_weights_bytes": [POINTER(ModelDesc), POINTER(c_size_t)],
+        "evs_model_create": [POINTER(ModelDesc), c_void_p, POINTER(c_void_p)],
+        "evs_pack_weights": [c_void_p, POINTER(c_void_p), c_void_p],
+        "evs_state_bytes": [c_void_p, c_int32, c_int32, c_int32, POINTER(c_size_t), POINTER(c_size_t)],
+        "evs_state_create": [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, POINTER(c_void_p)],
+        "evs_state_tensor": [c_void_p, c_int32, c_int32, POINTER(TensorDesc)],
+        "evs_state_error": [c_void_p, POINTER(c_int32), c_int32, c_void_p],
+        "evs_prefill": [c_void_p, c_void_p, c_void_p, POINTER(c_int32), c_void_p, c_void_p],
+        "evs_block_verify": [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p],
+        "evs_rollback": [c_void_p, c_void_p, c_void_p],
+        "evs_state_timing": [c_void_p, c_int32, c_int64],
+        "evs_state_timing_read": [c_void_p, c_int32, POINTER(ctypes.c_double), POINTER(c_int64),
+                                  POINTER(ctypes.c_double), c_void_p],
+        "evs_verify_sample": [c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_float,
+                              c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.restype = c_int32
+        f.argtypes = args
+    L.evs_model_destroy.argtypes = [c_void_p]
+    L.evs_model_destroy.restype = None
+    L.evs_state_destroy.argtypes = [c_void_p]
+    L.evs_state_destroy.restype = None
+    _lib = L
+    return L
+
+
+def _check(st, where):
+    if st != 0:
+        raise EvsError(st, where)
+
+
+def _ptr(t):
+    return c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return c_void_p(stream.cuda_stream)
+
+
+def _aligned_buffer(nbytes, device):
+    """uint8 device buffer of nbytes whose data pointer is 256-byte aligned."""
+    raw = torch.empty(max(int(nbytes), 1) + 256, dtype=torch.uint8, device=device)
+    off = (-raw.data_ptr()) % 256
+    return raw, raw[off: off + max(int(nbytes), 1)]
+
+
+def model_desc(cfg):
+    """ModelDesc from a config with d_model, vocab, dtype ('bf16'|'f32'),
+    norm_eps and blocks (kind, fir_len, iir_states, n_heads, head_dim, d_ff)."""
+    blocks = (BlockDesc * max(len(cfg.blocks), 1))()
+    for i, b in enumerate(cfg.blocks):
+        blocks[i] = BlockDesc(_KINDS[b.kind], b.fir_len, b.iir_states, b.n_heads, b.head_dim, b.d_ff)
+    d = ModelDesc(cfg.d_model, cfg.vocab, len(cfg.blocks), EVS_BF16 if cfg.dtype == "bf16" else EVS_F32,
+                  float(cfg.norm_eps), blocks)
+    d._keep = blocks
+    return d
+
+
+def canonical_order(cfg):
+    """Names of the canonical tensors in evs_pack_weights order."""
+    names = ["embed"]
+    for i, b in enumerate(cfg.blocks):
+        if b.kind == "fir":
+            names += [f"b{i}.w_in", f"b{i}.taps", f"b{i}.w_out"]
+        elif b.kind == "iir":
+            names += [f"b{i}.w_in", f"b{i}.lam", f"b{i}.res", f"b{i}.w_out"]
+        elif b.kind == "attn":
+            names += [f"b{i}.w_in", f"b{i}.w_out"]
+        else:
+            names += [f"b{i}.w_gu", f"b{i}.w_down"]
+    return names + ["lm_head"]
+
+
+class Model:
+    """A packed model on the device (evs_model_create + evs_pack_weights)."""
+
+    def __init__(self, cfg, weights, device="cuda"):
+        L = lib()
+        self.cfg = cfg
+        self.desc = model_desc(cfg)
+        n = c_size_t()
+        _check(L.evs_weights_bytes(ctypes.byref(self.desc), ctypes.byref(n)), "evs_weights_bytes")
+        self._raw, self.packed = _aligned_buffer(n.value, device)
+        h = c_void_p()
+        _check(L.evs_model_create(ctypes.byref(self.desc), _ptr(self.packed), ctypes.byref(h)), "evs_model_create")
+        self.handle = h
+        cnt = c_int32()
+        _check(L.evs_canonical_count(ctypes.byref(self.desc), ctypes.byref(cnt)), "evs_canonical_count")
+        names = canonical_order(cfg)
+        assert len(names) == cnt.value
+        tens = []
+        for i, name in enumerate(names):
+            r, c, dt = c_int64(), c_int64(), c_int32()
+            _check(L.evs_canonical_shape(ctypes.byref(self.desc), i, ctypes.byref(r), ctypes.byref(c),
+                                         ctypes.byref(dt)), "evs_canonical_shape")
+            t = weights[name].to(device=device, dtype=_TORCH_DT[dt.value]).contiguous()
+            if tuple(t.shape) != (r.value, c.value):
+                raise ValueError(f"{name}: shape {tuple(t.shape)} != {(r.value, c.value)}")
+            tens.append(t)
+        ptrs = (c_void_p * len(tens))(*[t.data_ptr() for t in tens])
+        _check(L.evs_pack_weights(self.handle, ptrs, _stream()), "evs_pack_weights")
+        torch.cuda.current_stream().synchronize()
+        del tens
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.evs_model_destroy(self.handle)
+            self.handle = None
+
+
+class State:
+    """Inference state of `batch` sequences plus the call workspace."""
+
+    def __init__(self, model: Model, batch: int, max_ctx: int, max_block: int, device="cuda"):
+        L = lib()
+        self.model = model
+        self.B, self.max_ctx, self.max_block = batch, max_ctx, max_block
+        sb, wb = c_size_t(), c_size_t()
+        _check(L.evs_state_bytes(model.handle, batch, max_ctx, max_block, ctypes.byref(sb), ctypes.byref(wb)),
+               "evs_state_bytes")
+        self.state_bytes, self.workspace_bytes = sb.value, wb.value
+        self._sraw, self.buf = _aligned_buffer(sb.value, device)
+        self._wraw, self.ws = _aligned_buffer(wb.value, device)
+        h = c_void_p()
+        _check(L.evs_state_create(model.handle, batch, max_ctx, max_block, _ptr(self.buf), _ptr(self.ws), _stream(),
+                                  ctypes.byref(h)), "evs_state_create")
+        self.handle = h
+
+    def tensor(self, what: int, block: int = -1) -> torch.Tensor:
+        """A torch view of a state tensor (evs_state_tensor)."""
+        d = TensorDesc()
+        _check(lib().evs_state_tensor(self.handle, what, block, ctypes.byref(d)), "evs_state_tensor")
+        dt = _TORCH_DT[d.dtype]
+        es = torch.tensor([], dtype=dt).element_size()
+        shape = [d.shape[i] for i in range(d.ndim)]
+        strides = [d.strides[i] for i in range(d.ndim)]
+        n = 1
+        for s in shape:
+            n *= s
+        flat = self.buf[d.offset: d.offset + n * es].view(dt)
+        return torch.as_strided(flat, shape, strides)
+
+    def error(self, clear: bool = False) -> int:
+        w = c_int32()
+        _check(lib().evs_state_error(self.handle, ctypes.byref(w), int(clear), _stream()), "evs_state_error")
+        return w.value
+
+    def timing(self, enable: bool, context_hint: int = 0):
+        """Enable or disable per-launch event timing (evs_state_timing)."""
+        _check(lib().evs_state_timing(self.handle, int(enable), int(context_hint)), "evs_state_timing")
+
+    def timing_read(self, kernel_class: int):
+        """(total ms, launches, algorithmic bytes) of the recorded launches of a class."""
+        ms, n, by = ctypes.c_double(), c_int64(), ctypes.c_double()
+        _check(lib().evs_state_timing_read(self.handle, int(kernel_class), ctypes.byref(ms), ctypes.byref(n),
+                                           ctypes.byref(by), _stream()), "evs_state_timing_read")
+        return ms.value, n.value, by.value
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.evs_state_destroy(self.handle)
+            self.handle = None
+
+
+# ------------------------------------------------------------------ hot path
+def evs_prefill(model: Model, state: State, tokens: torch.Tensor, seq_offsets, last_logits=None):
+    offs = (c_int32 * len(seq_offsets))(*[int(x) for x in seq_offsets])
+    _check(lib().evs_prefill(model.handle, state.handle, _ptr(tokens), offs, _ptr(last_logits), _stream()),
+           "evs_prefill")
+
+
+def evs_block_verify(model: Model, state: State, cand: torch.Tensor, gamma: int, logits: torch.Tensor):
+    _check(lib().evs_block_verify(model.handle, state.handle, _ptr(cand), int(gamma), _ptr(logits), _stream()),
+           "evs_block_verify")
+
+
+def evs_rollback(state: State, n_keep=None):
+    _check(lib().evs_rollback(state.handle, _ptr(n_keep), _stream()), "evs_rollback")
+
+
+def evs_verify_sample(batch, gamma, vocab, target, target_kind, q, draft, u, temperature, top_k, greedy,
+                      n_accepted, next_token, n_keep=None, error=None):
+    _check(lib().evs_verify_sample(int(batch), int(gamma), int(vocab), _ptr(target), int(target_kind), _ptr(q),
+                                   _ptr(draft), _ptr(u), float(temperature), int(top_k), int(greedy),
+                                   _ptr(n_accepted), _ptr(next_token), _ptr(n_keep), _ptr(error), _stream()),
+           "evs_verify_sample")
+
+
+def status_string(status: int) -> str:
+    return lib().evs_status_string(int(status)).decode()

@@ -1,0 +1,241 @@
+"""Block-verify throughput of the hybrid stack on one MI355X.
+
+A step is one speculative round on the 7B-shaped 32-layer bf16 stack (d=4096,
+d_ff=11008, vocab 512, attention every 8th layer) at 8192 tokens of context,
+gamma = 12, batch 1: evs_block_verify over the 13 candidates, evs_verify_sample
+(greedy) and evs_rollback, all enqueued on the device with no host sync
+inside the round. Drafts come from the identity drafter (the target's own
+greedy continuation, precomputed on the device), so every round accepts all
+12 drafts and emits 13 tokens.
+
+Prints one JSON line: tokens/s (= verified positions/s), the achieved HBM
+bandwidth of the round, a roofline object for the dominant kernel (the skinny
+GEMM, timed per launch with HIP events in a second pass of the same rounds),
+and the CPU oracle timed on a bounded sample on this host.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "block-verify tokens/s (γ=12, d=4096 hybrid stack) + achieved HBM GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--gamma", type=int, default=12)
+    ap.add_argument("--context", type=int, default=8192)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=8)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def round_bytes(cfg, ctx, gamma):
+    """Algorithmic HBM bytes of one round: every weight once, the K/V rows of
+    the attention layers up to the block end, the FIR windows and IIR modes
+    read, the per-position IIR modes and KV rows written, embeddings and logits."""
+    d, P = cfg.d_model, gamma + 1
+    n = cfg.layer_matrix_bytes() + P * d * 2 + cfg.vocab * d * 2   # layers, embedding rows, LM head
+    for b in cfg.blocks:
+        if b.kind == "attn":
+            n += 2 * (ctx + P) * d * 2            # K and V read
+            n += 2 * P * d * 2                    # K and V rows written
+        elif b.kind == "fir":
+            n += (b.fir_len - 1 + P) * d * 4      # window read + new inputs written
+            n += b.fir_len * d * 4                # taps
+        elif b.kind == "iir":
+            n += d * b.iir_states * 4 * (1 + P)   # committed modes read, per-position modes written
+            n += 2 * d * b.iir_states * 4         # poles + residues
+    n += P * cfg.vocab * 2                        # logits
+    return n
+
+
+def cpu_baseline(cfg_full, weights_gpu, ctx, gamma, seed, n_layers):
+    """The oracle, as it stands, on one block-verify round over the first
+    n_layers layers of the stack from a synthetic committed state at `ctx`;
+    scaled to the full depth."""
+    import numpy as np
+    import torch
+    import evs_synth as es
+    from evs_synth.configs import ModelConfig
+    from oracle import HybridLM
+
+    cores = len(os.sched_getaffinity(0))
+    nb = 2 * n_layers
+    cfg = ModelConfig(f"{cfg_full.name}_first{n_layers}", cfg_full.d_model, cfg_full.vocab,
+                      list(cfg_full.blocks[:nb]), dtype=cfg_full.dtype, norm_eps=cfg_full.norm_eps)
+    names = [n for n, _ in es.weight_names(cfg)]
+    w = {n: weights_gpu[n].cpu() for n in names}
+    synth = es.synthetic_state(cfg, ctx, seed=seed + 101)
+    orc = HybridLM(cfg, w)
+    st = orc.import_state(ctx, synth)
+    cand = es.prompt_tokens(cfg, gamma + 1, seed=seed + 7)[0]
+    orc.block(st, cand[:2])                        # warm-up
+    t0 = time.perf_counter()
+    orc.block(st, cand)
+    dt = time.perf_counter() - t0
+    full_s = dt * (len(cfg_full.blocks) / nb)
+    return {"value": round((gamma + 1) / full_s, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"one gamma={gamma} block-verify round through the first {n_layers} of "
+                      f"{len(cfg_full.blocks) // 2} layers (fp64 NumPy, synthetic state at {ctx} context), "
+                      f"{dt:.2f} s, scaled x{len(cfg_full.blocks) / nb:.0f} to the full depth",
+            "seconds_per_round": round(full_s, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the block-verify path is single-GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import evs_synth as es
+    from attention_dna_lms_amd import evs
+
+    dev = "cuda"
+    gamma, P, ctx = args.gamma, args.gamma + 1, args.context
+    cfg = es.stack_7b()
+    rounds = args.warmup + args.steps
+    t_all = time.time()
+    log("generating and packing weights")
+    weights = es.make_weights(cfg, seed=args.seed, device=dev)
+    model = evs.Model(cfg, weights, device=dev)
+    max_ctx = ctx + 2 * rounds * P + 64
+    state = evs.State(model, 1, max_ctx, 144, device=dev)
+    log(f"prefill {ctx} tokens")
+    prompt = torch.from_numpy(es.prompt_tokens(cfg, ctx, seed=args.seed)[0]).to(dev)
+    last = torch.empty(1, cfg.vocab, dtype=torch.bfloat16, device=dev)
+    evs.evs_prefill(model, state, prompt, [0, ctx], last)
+    torch.cuda.synchronize()
+    snap = state.buf.clone()
+
+    # identity drafter: the target's own greedy continuation, one token at a time
+    log("native greedy continuation")
+    n_native = rounds * P + 1
+    native = torch.zeros(n_native, dtype=torch.int32, device=dev)
+    native[0] = last[0].float().argmax().to(torch.int32)
+    one = torch.empty(1, 1, cfg.vocab, dtype=torch.bfloat16, device=dev)
+    nacc1 = torch.zeros(1, dtype=torch.int32, device=dev)
+    keep1 = torch.zeros(1, dtype=torch.int32, device=dev)
+    t0 = time.time()
+    for i in range(n_native - 1):
+        evs.evs_block_verify(model, state, native[i:i + 1].view(1, 1), 0, one)
+        evs.evs_verify_sample(1, 0, cfg.vocab, one, evs.EVS_TARGET_LOGITS_BF16, None, None, None, 1.0, 0, 1,
+                              nacc1, native[i + 1:i + 2], keep1)
+        evs.evs_rollback(state, keep1)
+    torch.cuda.synchronize()
+    native_step_ms = (time.time() - t0) * 1e3 / (n_native - 1)
+
+    lg = torch.empty(1, P, cfg.vocab, dtype=torch.bfloat16, device=dev)
+    n_acc = torch.zeros(rounds, dtype=torch.int32, device=dev)
+    nxt = torch.zeros(rounds, dtype=torch.int32, device=dev)
+    keep = torch.zeros(rounds, dtype=torch.int32, device=dev)
+
+    def run_round(r):
+        cand = native[r * P:(r + 1) * P].view(1, P)
+        evs.evs_block_verify(model, state, cand, gamma, lg)
+        evs.evs_verify_sample(1, gamma, cfg.vocab, lg, evs.EVS_TARGET_LOGITS_BF16, None,
+                              native[r * P + 1:(r + 1) * P].view(1, gamma), None, 1.0, 0, 1,
+                              n_acc[r:r + 1], nxt[r:r + 1], keep[r:r + 1])
+        evs.evs_rollback(state, keep[r:r + 1])
+
+    # ---- headline pass
+    state.buf.copy_(snap)
+    for r in range(args.warmup):
+        run_round(r)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    t_wall = time.perf_counter()
+    for r in range(args.warmup, rounds):
+        run_round(r)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    total_ms = ev0.elapsed_time(ev1)
+    ms = total_ms / args.steps
+    accepted = n_acc.cpu().numpy()
+    assert state.error() == 0, "device error word set"
+    all_accepted = bool((accepted == gamma).all())
+
+    # ---- per-launch timing pass over the same rounds
+    state.buf.copy_(snap)
+    for r in range(args.warmup):
+        run_round(r)
+    state.timing(True, ctx + args.warmup * P + args.steps * P // 2)
+    for r in range(args.warmup, rounds):
+        run_round(r)
+    g_ms, g_n, g_bytes = state.timing_read(evs.EVS_KC_GEMM)
+    a_ms, a_n, a_bytes = state.timing_read(evs.EVS_KC_ATTN)
+    state.timing(False)
+
+    tok_s = P / (ms / 1e3)
+    rb = round_bytes(cfg, ctx + args.warmup * P + args.steps * P // 2, gamma)
+    gbps = rb / (ms / 1e3) / 1e9
+    weight_frac = cfg.layer_matrix_bytes() / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS
+    gemm_avg_us = g_ms * 1e3 / max(g_n, 1)
+    gemm_gbps = g_bytes / (g_ms / 1e3) / 1e9 if g_ms > 0 else 0.0
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights, uniform ACGT prompt, identity drafter)",
+        "config": {"workload": "7B-shaped 32-layer hybrid stack (FIR-7/FIR-128/IIR-16 mixers, attention "
+                               "32x128 every 8th layer, gated MLP d_ff=11008, vocab 512, ~13 GB bf16), "
+                               f"{ctx}-token context, gamma={gamma}, batch 1, greedy identity drafter; "
+                               "step = block verify + verify + rollback",
+                   "batch": 1, "gamma": gamma, "context": ctx, "positions_per_step": P},
+        "achieved_hbm_gbps": round(gbps, 1),
+        "hbm_frac_of_8tbps": round(gbps / HBM_PEAK_GBPS, 4),
+        "weight_roofline_frac": round(weight_frac, 4),
+        "algorithmic_bytes_per_step": rb,
+        "native_step_ms": round(native_step_ms, 4),
+        "verification_tax": round(ms / native_step_ms, 4),
+        "all_drafts_accepted": all_accepted,
+        "wall_ms_per_step": round(wall_ms / args.steps, 4),
+        "roofline": {"bound": "hbm", "kernel": "gemm_kernel (skinny bf16 MFMA weight streamer)",
+                     "achieved": round(gemm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gemm_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "avg_launch_us": round(gemm_avg_us, 3), "launches_per_step": g_n / args.steps,
+                     "bytes_per_launch": round(g_bytes / max(g_n, 1)),
+                     "share_of_step": round(g_ms / args.steps / ms, 4)},
+        "attention": {"avg_launch_us": round(a_ms * 1e3 / max(a_n, 1), 3),
+                      "achieved_gbps": round(a_bytes / (a_ms / 1e3) / 1e9, 1) if a_ms > 0 else 0.0},
+    }
+    log(f"GPU part done in {time.time() - t_all:.1f}s: {ms:.3f} ms/round")
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(cfg, weights, ctx, gamma, args.seed, args.cpu_layers)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

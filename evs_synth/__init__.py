@@ -7,9 +7,9 @@ tests can draw the same inputs from it without sharing any computation.
 """
 from .configs import Block, ModelConfig, tiny_c1, pair_c2, stack_7b, small_stack, ACGT_IDS
 from .gen import (make_weights, prompt_tokens, draft_probs_softmax, dirichlet_acgt,
-                  uniforms, synthetic_state, rng_for, sample_from, weight_names)
+                  uniforms, synthetic_state, rng_for, sample_from, weight_names, dyadic_weights)
 
 __all__ = ["Block", "ModelConfig", "tiny_c1", "pair_c2", "stack_7b", "small_stack",
            "ACGT_IDS", "make_weights", "prompt_tokens", "draft_probs_softmax",
            "dirichlet_acgt", "uniforms", "synthetic_state", "rng_for", "sample_from",
-           "weight_names"]
+           "weight_names", "dyadic_weights"]

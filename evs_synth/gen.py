@@ -162,3 +162,28 @@ def synthetic_state(cfg: ModelConfig, t: int, seed: int = 0, device="cpu", std: 
             st[i] = {"k": _normal((t, b.n_heads, b.head_dim), std, device, seed, f"st{i}.k", kv_dtype),
                      "v": _normal((t, b.n_heads, b.head_dim), std, device, seed, f"st{i}.v", kv_dtype)}
     return st
+
+
+def dyadic_weights(cfg: ModelConfig, seed: int = 0, device="cpu", step_log2: int = 8, span: int = 4):
+    """Weights on a coarse dyadic grid for exact-arithmetic checks.
+
+    Matrices hold n * 2**-step_log2 with n uniform in [-span, span] and the
+    embedding holds +-1, so the first block's normalised input is +-1 and its
+    in-projection outputs are sums that fp32 and fp64 both carry exactly
+    (given d * span * 2**-step_log2 < 2**(24 - step_log2)). FIR taps, IIR poles
+    and residues are drawn as in ``make_weights``.
+    """
+    base = make_weights(cfg, seed, device)
+    mat_dtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    out = {}
+    for name, shape in weight_names(cfg):
+        if name.endswith((".lam", ".res", ".taps")):
+            out[name] = base[name]
+            continue
+        g = _torch_gen(device, seed, "dyadic", name)
+        if name == "embed":
+            w = torch.randint(0, 2, shape, generator=g, device=device).float() * 2 - 1
+        else:
+            w = torch.randint(-span, span + 1, shape, generator=g, device=device).float() * 2.0 ** -step_log2
+        out[name] = w.to(mat_dtype)
+    return out

@@ -1,0 +1,241 @@
+/*
+ * evs.h — C ABI of the block-verification hot path for hybrid (FIR / IIR /
+ * attention) DNA language models, on CDNA4 (gfx950).
+ *
+ * The operations follow the EvSpark pages:
+ *   - block-verification forward over gamma+1 candidate tokens keeping the
+ *     inference state of every position, for all three state classes (FIR
+ *     sliding windows, IIR modal recurrences, append-only KV caches)
+ *     [EvSpark preprint, abstract (i); Evo2 discussion #232, "What we
+ *     implemented" and the state-slicing contract, item 1];
+ *   - rollback by slicing that state to the accepted boundary, with no replay
+ *     and per-sequence boundaries in a batch [same; state-slicing contract,
+ *     item 2];
+ *   - the exact rejection-sampling verifier and greedy verification
+ *     [preprint abstract (iii); discussion #232, "A few other observations";
+ *     model card, "Library"].
+ *
+ * Conventions
+ *   Memory   — every buffer is caller-owned device memory passed as a plain
+ *              pointer; the library never allocates device memory. Host
+ *              handles (evs_model, evs_state) are small host objects.
+ *   Streams  — `stream` is a hipStream_t (NULL = default stream). Calls only
+ *              enqueue work; none synchronises except evs_state_error.
+ *   Errors   — argument and state-machine checks run on the host before
+ *              anything is enqueued: on failure nothing is enqueued and a
+ *              negative evs_status is returned. A failed kernel launch returns
+ *              EVS_E_HIP. Conditions only the device can see (a token id out
+ *              of range, a context overflow, a device-side n_keep out of
+ *              range) are clamped so every access stays in bounds, and set a
+ *              bit in the state's sticky error word (evs_state_error).
+ *   Threads  — handles are not thread-safe; distinct states may be used on
+ *              distinct streams.
+ *   Layout   — "storage type" below is bf16 for EVS_BF16 models and fp32 for
+ *              EVS_F32 models. Matrices are row-major with y = x W^T.
+ */
+#ifndef EVS_H
+#define EVS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  EVS_OK = 0,
+  EVS_E_INVALID = -1,     /* bad argument (null pointer, bad size, bad descriptor) */
+  EVS_E_RANGE = -2,       /* a size exceeds what the state was created for */
+  EVS_E_STATE = -3,       /* call out of order (e.g. rollback with nothing pending) */
+  EVS_E_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  EVS_E_UNSUPPORTED = -5  /* valid request outside what this build implements */
+} evs_status;
+
+/* block kinds */
+enum { EVS_FIR = 1, EVS_IIR = 2, EVS_ATTN = 3, EVS_MLP = 4 };
+/* storage types */
+enum { EVS_BF16 = 1, EVS_F32 = 2, EVS_I32 = 3 };
+/* target kinds for evs_verify_sample */
+enum { EVS_TARGET_LOGITS_BF16 = 1, EVS_TARGET_LOGITS_F32 = 2, EVS_TARGET_PROBS_F32 = 3 };
+/* sticky error-word bits */
+enum { EVS_ERR_TOKEN = 1, EVS_ERR_CONTEXT = 2, EVS_ERR_NKEEP = 4, EVS_ERR_DRAFT = 8 };
+
+/* One residual block (pre-norm). FIR: causal depthwise filter of fir_len
+ * taps on h = k*v (state: the last fir_len-1 inputs). IIR: diagonal real modal
+ * recurrence with iir_states (<= 16) modes per channel (state: the modes).
+ * ATTN: causal multi-head attention, n_heads * head_dim = d_model, head_dim a
+ * multiple of 32, no positional encoding (state: K and V rows). MLP: gated
+ * GELU with d_ff hidden units. */
+typedef struct {
+  int32_t kind, fir_len, iir_states, n_heads, head_dim, d_ff;
+} evs_block_desc;
+
+/* d_model and every d_ff are multiples of 32; vocab >= 2. */
+typedef struct {
+  int32_t d_model, vocab, n_blocks, dtype;
+  float norm_eps;
+  const evs_block_desc* blocks;
+} evs_model_desc;
+
+typedef struct evs_model evs_model;
+typedef struct evs_state evs_state;
+
+/* Where a state tensor lives inside the caller's state buffer. */
+typedef struct {
+  uint64_t offset;      /* byte offset from the start of the state buffer */
+  int32_t dtype;        /* EVS_BF16 | EVS_F32 | EVS_I32 */
+  int32_t ndim;
+  int64_t shape[6];
+  int64_t strides[6];   /* in elements */
+} evs_tensor_desc;
+
+/* state tensors (evs_state_tensor `what`) */
+enum {
+  EVS_ST_T = 1,         /* i32 [B]: committed length of each sequence */
+  EVS_ST_IIR_BUF = 2,   /* i32 [B]: which IIR buffer holds the committed state */
+  EVS_ST_IIR_SLOT = 3,  /* i32 [B]: its position slot, -1 = the zero state */
+  EVS_ST_FIR_RING = 4,  /* f32 [B, R, d] (FIR block): row (pos mod R) holds the
+                           filter input h at position pos */
+  EVS_ST_IIR = 5,       /* f32 [B, 2, max_block, d, N] (IIR block): the state after
+                           each position of a block, double-buffered */
+  EVS_ST_K = 6,         /* storage [B, H, cap, Dh] (ATTN block): key rows */
+  EVS_ST_VT = 7,        /* storage [B, H, Dh, cap] (ATTN block): value rows, transposed */
+  EVS_ST_ERROR = 8      /* i32 [1]: sticky error word (EVS_ERR_* bits) */
+};
+
+const char* evs_status_string(evs_status s);
+
+/* ------------------------------------------------------------------ model */
+
+/* Number of canonical weight tensors and the shape of tensor i, in the order
+ * evs_pack_weights expects them:
+ *   embed [V, d];
+ *   per block: FIR  w_in [3d, d], taps [d, L] (f32), w_out [d, d];
+ *              IIR  w_in [3d, d], lam [d, N] (f32), res [d, N] (f32), w_out [d, d];
+ *              ATTN w_in [3d, d] (rows: q, k, v), w_out [d, d];
+ *              MLP  w_gu [2 d_ff, d] (gate rows first), w_down [d, d_ff];
+ *   lm_head [V, d].
+ * Matrices are in the storage type; taps/lam/res are always f32. */
+evs_status evs_canonical_count(const evs_model_desc* desc, int32_t* count);
+evs_status evs_canonical_shape(const evs_model_desc* desc, int32_t i, int64_t* rows,
+                               int64_t* cols, int32_t* dtype);
+
+/* Bytes of the packed weight buffer for `desc`. */
+evs_status evs_weights_bytes(const evs_model_desc* desc, size_t* bytes);
+
+/* Create a model over a caller-owned packed weight buffer (evs_weights_bytes
+ * bytes, 256-byte aligned). The descriptor is copied. */
+evs_status evs_model_create(const evs_model_desc* desc, void* packed_dev, evs_model** out);
+
+/* Fill the packed buffer from the canonical tensors (device pointers, order
+ * and shapes as in evs_canonical_shape). Enqueued on `stream`; the canonical
+ * tensors may be freed once the stream has passed this point. */
+evs_status evs_pack_weights(evs_model* m, const void* const* canonical_dev, void* stream);
+
+void evs_model_destroy(evs_model* m);
+
+/* ------------------------------------------------------------------ state */
+
+/* Sizes of the state buffer (persistent across calls) and the workspace
+ * (scratch, reused by every call on this state) for `batch` sequences of up
+ * to `max_ctx` positions each, processed `max_block` positions per call
+ * (max_block = gamma_max + 1 for verification; it also bounds prefill chunks;
+ * batch * max_block <= 4096). */
+evs_status evs_state_bytes(const evs_model* m, int32_t batch, int32_t max_ctx,
+                           int32_t max_block, size_t* state_bytes, size_t* workspace_bytes);
+
+/* Create a state over caller-owned buffers (256-byte aligned) and enqueue their
+ * initialisation on `stream`: every sequence empty (t = 0, zero IIR state),
+ * error word cleared, workspace counters zeroed. */
+evs_status evs_state_create(const evs_model* m, int32_t batch, int32_t max_ctx,
+                            int32_t max_block, void* state_dev, void* workspace_dev,
+                            void* stream, evs_state** out);
+
+void evs_state_destroy(evs_state* s);
+
+/* Location of a state tensor (see EVS_ST_*); `block` selects the block for
+ * per-block tensors and is ignored otherwise. Lets a caller inspect the
+ * per-position state or import a committed state it synthesised. */
+evs_status evs_state_tensor(const evs_state* s, int32_t what, int32_t block,
+                            evs_tensor_desc* out);
+
+/* Synchronise `stream`, then read (and with `clear` != 0, reset) the sticky
+ * error word. */
+evs_status evs_state_error(evs_state* s, int32_t* host_word, int32_t clear, void* stream);
+
+/* --------------------------------------------------------------- hot path */
+
+/* Consume prompt tokens into committed sequences. tokens_dev holds the
+ * concatenated prompts (i32); seq_offsets_host[B+1] delimits sequence b's
+ * tokens. Each sequence's tokens are appended after its committed length, in
+ * chunks of at most max_block positions. last_logits_dev [B, V] (storage
+ * type; may be NULL) receives the logits after each sequence's last token
+ * (rows of sequences with no tokens are left untouched). Requires no pending
+ * block. */
+evs_status evs_prefill(evs_model* m, evs_state* s, const int32_t* tokens_dev,
+                       const int32_t* seq_offsets_host, void* last_logits_dev, void* stream);
+
+/* Block-verification forward. cand_dev [B, gamma+1] (i32) holds, per sequence,
+ * the last emitted (not yet consumed) token followed by gamma draft tokens.
+ * logits_dev [B, gamma+1, V] (storage type) receives the logits of every
+ * candidate position: row i is the next-token distribution after cand[i], so
+ * draft i+1 is judged by row i. The state of every position (FIR window rows,
+ * IIR modes, KV rows) is written beyond each sequence's committed boundary; the
+ * block stays pending until evs_rollback. A call on a pending state first
+ * discards the pending block (rollback to 0). 0 <= gamma < max_block. */
+evs_status evs_block_verify(evs_model* m, evs_state* s, const int32_t* cand_dev,
+                            int32_t gamma, void* logits_dev, void* stream);
+
+/* Commit the pending block: sequence b keeps the first n_keep_dev[b] positions
+ * (0 .. gamma+1; n_accepted + 1 after a verification). Zero bytes of state are
+ * copied: lengths advance and the IIR slot index moves to the kept position.
+ * n_keep_dev may be NULL to keep all gamma+1 positions. Device-side values out
+ * of range are clamped and flagged (EVS_ERR_NKEEP). */
+evs_status evs_rollback(evs_state* s, const int32_t* n_keep_dev, void* stream);
+
+/* Verify a drafted block for `batch` sequences (stateless).
+ *   target_dev  [B, gamma+1, V]: logits (bf16 or f32) or probabilities (f32)
+ *   q_dev       [B, gamma, V] f32: draft distributions (unused if greedy)
+ *   draft_dev   [B, gamma] i32: draft tokens d_1 .. d_gamma
+ *   u_dev       [B, gamma+1] f32 in [0,1): u[i] for the accept test of draft
+ *               i+1, u[gamma] for the final draw (unused if greedy)
+ *   temperature > 0, top_k (0 or >= V keeps all) apply to logits targets.
+ * Sampling: accept draft i+1 iff u[i] < p_i[x] / q_i[x] (iff p_i[x] > 0 when
+ * q_i[x] = 0); at the first reject draw from max(0, p_i - q_i) normalised
+ * (p_i if that is all zero); if all are accepted draw a bonus token from
+ * p_gamma. A draw is the inverse CDF with the running fp32 sum in token order.
+ * Greedy: accept while the draft equals the argmax (lowest id on ties); emit
+ * the argmax at the first mismatch or after the last row.
+ * Outputs (i32 [B]): n_accepted, next_token, and n_keep = n_accepted + 1 (may
+ * be NULL). Draft ids out of range are clamped and set EVS_ERR_DRAFT in
+ * *error_dev if given. Requires gamma <= 63 and (gamma + 2) * V <= 15872. */
+evs_status evs_verify_sample(int32_t batch, int32_t gamma, int32_t vocab, const void* target_dev,
+                             int32_t target_kind, const float* q_dev, const int32_t* draft_dev,
+                             const float* u_dev, float temperature, int32_t top_k, int32_t greedy,
+                             int32_t* n_accepted_dev, int32_t* next_token_dev,
+                             int32_t* n_keep_dev, int32_t* error_dev, void* stream);
+
+/* ------------------------------------------------------------ measurement */
+
+/* kernel classes for per-launch timing */
+enum { EVS_KC_GEMM = 1, EVS_KC_ATTN = 2 };
+
+/* Measurement aid: with timing enabled, every GEMM and attention launch made
+ * for this state is bracketed by a pair of HIP events on the call's stream and
+ * its algorithmic bytes are noted (weights + input rows + output rows for a
+ * GEMM; K/V rows up to `context_hint` positions + q + o for attention). Adds
+ * two event records per launch; leave it off for headline timing. */
+evs_status evs_state_timing(evs_state* s, int32_t enable, int64_t context_hint);
+
+/* Synchronise `stream`, then sum the recorded launches of one kernel class:
+ * total device time (ms), number of launches and algorithmic bytes. The
+ * records read are cleared. */
+evs_status evs_state_timing_read(evs_state* s, int32_t kernel_class, double* total_ms,
+                                 int64_t* launches, double* bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EVS_H */

@@ -1,0 +1,312 @@
+"""GPU parity: the HIP path through its C ABI against the CPU oracle on the
+same seeded inputs (tolerances: sliced states and accepted lengths bit-exact,
+fp32 states within 1e-5 relative, bf16 logits within 2e-2 absolute, greedy
+tokens identical except on ties)."""
+import numpy as np
+import pytest
+import torch
+
+import evs_synth as es
+from evs_synth.configs import Block, ModelConfig
+from oracle import HybridLM
+from oracle.verifier import argmax_lowest, verify_greedy, verify_sample
+
+from gpu_util import (DEV, block_verify, import_state, lengths, make_engine, max_rel, pending_iir, prefill,
+                      rel_close, rollback, snapshot)
+from attention_dna_lms_amd import evs
+
+pytestmark = pytest.mark.gpu
+
+LOGIT_ATOL = 2e-2
+
+
+def logit_err(a, b):
+    """Largest |a - b| beyond one bf16 quantum of b: logits are stored in bf16,
+    so values of magnitude >= 4 carry a quantum (0.03125) above the 2e-2 bar and
+    an honest one-quantum rounding flip must not count against it."""
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(b))[1] - 8)
+    return float(np.max(np.abs(a - b) - ulp))
+
+
+def _near_tie(row, tol=2 * LOGIT_ATOL):
+    s = np.sort(row)[::-1]
+    return s[0] - s[1] <= tol
+
+
+# --------------------------------------------------------------- C1 (fp32)
+def test_c1_tiny_fp32_prefill_verify_rollback_every_k():
+    cfg = es.tiny_c1()
+    w = es.make_weights(cfg, seed=0)
+    gamma = 4
+    P = gamma + 1
+    B = P + 1                               # sequence b rolls back to n_keep = b
+    prompt = es.prompt_tokens(cfg, 256, seed=0)[0]
+    cand = es.prompt_tokens(cfg, P, seed=1)[0]
+    model, state = make_engine(cfg, w, batch=B, max_ctx=512, max_block=64)
+    last = prefill(model, state, [prompt] * B)
+    orc = HybridLM(cfg, w)
+    olast, ost = orc.prefill(prompt, chunk=64)
+    assert np.max(np.abs(last - olast[None])) < 1e-4
+    lg, _ = block_verify(model, state, np.tile(cand, (B, 1)))
+    pend = orc.block(ost, cand)
+    assert np.max(np.abs(lg - pend.logits[None])) < 1e-4
+    for i, blk in enumerate(cfg.blocks):
+        if blk.kind == "iir":
+            assert rel_close(pending_iir(state, i, P), pend.iir_s[i]), max_rel(pending_iir(state, i, P), pend.iir_s[i])
+    rollback(state, np.arange(B))
+    assert list(lengths(state)) == [256 + k for k in range(B)]
+    for k in range(B):
+        g, o = snapshot(state, cfg, b=k), orc.rollback(pend, k)
+        for i in o.fir:
+            assert rel_close(g["fir"][i], o.fir[i]), (k, i)
+        for i in o.iir:
+            assert rel_close(g["iir"][i], o.iir[i]), (k, i)
+        for i in o.k:
+            assert rel_close(g["k"][i], o.k[i]) and rel_close(g["v"][i], o.v[i]), (k, i)
+    assert state.error() == 0
+
+
+# ------------------------------------------------ exact-arithmetic single blocks
+def _single(kind, d=4096, vocab=512, **kw):
+    return ModelConfig(f"single_{kind}", d, vocab, [Block(kind, **kw)], dtype="bf16")
+
+
+@pytest.mark.parametrize("blk", [dict(kind="fir", fir_len=7), dict(kind="fir", fir_len=128),
+                                 dict(kind="iir", iir_states=16)], ids=["fir7", "fir128", "iir16"])
+def test_c2_block_states_bitexact_and_rollback_every_k(blk):
+    """d=4096 mixer with dyadic weights: the in-projection is exact on both
+    sides, so FIR windows must match bit for bit and IIR modes within 1e-5, at
+    every candidate position and after rollback to every k in 0..13."""
+    cfg = _single(**blk)
+    w = es.dyadic_weights(cfg, seed=3)
+    gamma, t0 = 12, 1024
+    P = gamma + 1
+    B = P + 1
+    synth = es.synthetic_state(cfg, t0, seed=4)
+    model, state = make_engine(cfg, w, batch=B, max_ctx=t0 + 64, max_block=P)
+    for b in range(B):
+        import_state(state, cfg, synth, t0, b)
+    cand = es.prompt_tokens(cfg, P, seed=5)[0]
+    lg, _ = block_verify(model, state, np.tile(cand, (B, 1)))
+    orc = HybridLM(cfg, w)
+    ost = orc.import_state(t0, synth)
+    pend = orc.block(ost, cand)
+    assert logit_err(lg, pend.logits[None]) < LOGIT_ATOL
+    if blk["kind"] == "fir":
+        ring = state.tensor(evs.EVS_ST_FIR_RING, 0)[0]
+        R = ring.shape[0]
+        h = ring[torch.as_tensor((t0 + np.arange(P)) % R, device=DEV)].double().cpu().numpy()
+        assert np.array_equal(h, pend.fir_h[0])
+    else:
+        got = pending_iir(state, 0, P)
+        assert rel_close(got, pend.iir_s[0]), max_rel(got, pend.iir_s[0])
+    emitted = pending_iir(state, 0, P) if blk["kind"] == "iir" else None
+    rollback(state, np.arange(B))
+    for k in range(B):
+        g, o = snapshot(state, cfg, b=k), orc.rollback(pend, k)
+        assert g["t"] == t0 + k
+        if blk["kind"] == "fir":
+            assert np.array_equal(g["fir"][0], o.fir[0]), k
+        else:
+            assert rel_close(g["iir"][0], o.iir[0]), (k, max_rel(g["iir"][0], o.iir[0]))
+            if k > 0:   # the committed state IS the emitted per-position state (no copy, no replay)
+                assert np.array_equal(g["iir"][0], emitted[k - 1])
+    assert state.error() == 0
+
+
+def test_c3_attention_block_kv_bitexact_at_8k():
+    cfg = _single("attn", n_heads=32, head_dim=128)
+    w = es.dyadic_weights(cfg, seed=6)
+    gamma, t0 = 12, 8192
+    P = gamma + 1
+    synth = es.synthetic_state(cfg, t0, seed=7)
+    model, state = make_engine(cfg, w, batch=1, max_ctx=t0 + 64, max_block=P)
+    import_state(state, cfg, synth, t0)
+    cand = es.prompt_tokens(cfg, P, seed=8)[0]
+    lg, _ = block_verify(model, state, cand[None])
+    orc = HybridLM(cfg, w)
+    pend = orc.block(orc.import_state(t0, synth), cand)
+    assert logit_err(lg[0], pend.logits) < LOGIT_ATOL
+    rollback(state, [P])
+    g = snapshot(state, cfg)
+    assert np.array_equal(g["k"][0][t0:], pend.k_new[0]) and np.array_equal(g["v"][0][t0:], pend.v_new[0])
+
+
+# ---------------------------------------------------- free-running bf16 stacks
+def test_small_stack_bf16_ragged_batch_matches_oracle():
+    cfg = es.small_stack()
+    w = es.make_weights(cfg, seed=1)
+    gamma = 12
+    prompts = [es.prompt_tokens(cfg, n, seed=10 + n)[0] for n in (300, 177)]
+    model, state = make_engine(cfg, w, batch=2, max_ctx=512, max_block=gamma + 1)
+    last = prefill(model, state, prompts)
+    orc = HybridLM(cfg, w)
+    cands, pends = [], []
+    for b, pr in enumerate(prompts):
+        olast, ost = orc.prefill(pr, chunk=64)
+        assert logit_err(last[b], olast) < LOGIT_ATOL, b
+        cand = es.prompt_tokens(cfg, gamma + 1, seed=20 + b)[0]
+        cands.append(cand)
+        pends.append(orc.block(ost, cand))
+    lg, _ = block_verify(model, state, np.stack(cands))
+    for b in range(2):
+        err = logit_err(lg[b], pends[b].logits)
+        assert err < LOGIT_ATOL, (b, err)
+        for i in range(gamma + 1):
+            if not _near_tie(pends[b].logits[i]):
+                assert argmax_lowest(lg[b, i]) == argmax_lowest(pends[b].logits[i])
+    rollback(state, [5, 13])
+    assert list(lengths(state)) == [305, 190]
+
+
+def test_c2_pair_free_running_logits():
+    cfg = es.pair_c2(128)
+    w = es.make_weights(cfg, seed=2)
+    prompt = es.prompt_tokens(cfg, 1024, seed=2)[0]
+    model, state = make_engine(cfg, w, batch=1, max_ctx=1100, max_block=13)
+    last = prefill(model, state, [prompt])
+    orc = HybridLM(cfg, w)
+    olast, ost = orc.prefill(prompt, chunk=256)
+    assert logit_err(last[0], olast) < LOGIT_ATOL
+    cand = es.prompt_tokens(cfg, 13, seed=3)[0]
+    lg, _ = block_verify(model, state, cand[None])
+    assert logit_err(lg[0], orc.block(ost, cand).logits) < LOGIT_ATOL
+
+
+# ------------------------------------------------------- GPU invariants (exact)
+def test_block_equals_sequential_and_rollback_equals_steps_bitexact():
+    cfg = es.small_stack()
+    w = es.make_weights(cfg, seed=4)
+    gamma = 12
+    P = gamma + 1
+    prompt = es.prompt_tokens(cfg, 150, seed=4)[0]
+    cand = es.prompt_tokens(cfg, P, seed=5)[0]
+    mA, sA = make_engine(cfg, w, batch=1, max_ctx=512, max_block=P)
+    prefill(mA, sA, [prompt])
+    blk, _ = block_verify(mA, sA, cand[None])
+    mB, sB = make_engine(cfg, w, batch=1, max_ctx=512, max_block=P)
+    prefill(mB, sB, [prompt])
+    for k in range(P):
+        one, _ = block_verify(mB, sB, cand[None, k:k + 1])
+        assert np.array_equal(one[0, 0], blk[0, k]), k
+        rollback(sB, [1])
+        if k in (0, 5, P - 1):
+            # rollback(k+1) of a fresh block from the same prefix == k+1 single steps
+            mC, sC = make_engine(cfg, w, batch=1, max_ctx=512, max_block=P)
+            prefill(mC, sC, [prompt])
+            block_verify(mC, sC, cand[None])
+            rollback(sC, [k + 1])
+            a, b = snapshot(sC, cfg), snapshot(sB, cfg)
+            assert a["t"] == b["t"]
+            for key in ("fir", "iir", "k", "v"):
+                for i in a[key]:
+                    assert np.array_equal(a[key][i], b[key][i]), (k, key, i)
+
+
+def test_identity_drafter_accepts_everything_on_gpu():
+    cfg = es.small_stack()
+    w = es.make_weights(cfg, seed=5)
+    gamma, rounds = 12, 3
+    prompt = es.prompt_tokens(cfg, 120, seed=6)[0]
+    # native greedy continuation, one token at a time
+    mN, sN = make_engine(cfg, w, batch=1, max_ctx=512, max_block=gamma + 1)
+    last = prefill(mN, sN, [prompt])
+    x = argmax_lowest(last[0])
+    native = [x]
+    for _ in range(rounds * (gamma + 1)):
+        lg, _ = block_verify(mN, sN, np.array([[x]]))
+        assert np.isfinite(lg).all()
+        rollback(sN, [1])
+        x = argmax_lowest(lg[0, 0])
+        native.append(x)
+    # speculative rounds with the identity drafter, verified greedily on the GPU
+    mS, sS = make_engine(cfg, w, batch=1, max_ctx=512, max_block=gamma + 1)
+    prefill(mS, sS, [prompt])
+    out, pos = [native[0]], 0
+    n_acc = torch.zeros(1, dtype=torch.int32, device=DEV)
+    nxt = torch.zeros(1, dtype=torch.int32, device=DEV)
+    keep = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for _ in range(rounds):
+        cand = np.array([native[pos: pos + gamma + 1]], np.int32)
+        _, lgt = block_verify(mS, sS, cand)
+        drafts = torch.as_tensor(cand[:, 1:]).to(DEV)
+        evs.evs_verify_sample(1, gamma, cfg.vocab, lgt, evs.EVS_TARGET_LOGITS_BF16, None, drafts, None, 1.0, 0, 1,
+                              n_acc, nxt, keep)
+        evs.evs_rollback(sS, keep)
+        torch.cuda.synchronize()
+        assert int(n_acc[0]) == gamma
+        out += list(cand[0, 1:]) + [int(nxt[0])]
+        pos += gamma + 1
+    assert out == native[: len(out)]
+
+
+def test_repeat_is_bitwise_deterministic():
+    cfg = es.small_stack()
+    w = es.make_weights(cfg, seed=7)
+    prompt = es.prompt_tokens(cfg, 90, seed=7)[0]
+    cand = es.prompt_tokens(cfg, 13, seed=8)[0]
+    outs = []
+    for _ in range(2):
+        m, s = make_engine(cfg, w, batch=1, max_ctx=256, max_block=13)
+        prefill(m, s, [prompt])
+        outs.append(block_verify(m, s, cand[None])[0])
+    assert np.array_equal(outs[0], outs[1])
+
+
+# ---------------------------------------------------------------- verifier
+def _run_verify(B, gamma, V, target, kind, q, drafts, u, T=1.0, top_k=0, greedy=0):
+    n_acc = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    nxt = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    keep = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    qd = None if q is None else torch.as_tensor(q).to(DEV)
+    ud = None if u is None else torch.as_tensor(u).to(DEV)
+    evs.evs_verify_sample(B, gamma, V, target, kind, qd, torch.as_tensor(drafts).to(DEV), ud, T, top_k, greedy,
+                          n_acc, nxt, keep, err)
+    torch.cuda.synchronize()
+    assert int(err[0]) == 0
+    a, n, k = n_acc.cpu().numpy(), nxt.cpu().numpy(), keep.cpu().numpy()
+    assert np.array_equal(k, a + 1)
+    return a, n
+
+
+@pytest.mark.parametrize("gamma", [1, 4, 8, 12, 16])
+def test_verify_dirichlet_probs_bitexact(gamma):
+    B, V = 8, 512
+    p = es.dirichlet_acgt((B, gamma + 1), V, 0.3, seed=gamma, tag="p")
+    q = es.dirichlet_acgt((B, gamma), V, 0.3, seed=gamma, tag="q")
+    drafts = es.gen.sample_from(q, seed=gamma)
+    u = es.uniforms((B, gamma + 1), seed=gamma)
+    a, n = _run_verify(B, gamma, V, torch.as_tensor(p).to(DEV), evs.EVS_TARGET_PROBS_F32, q, drafts, u)
+    for b in range(B):
+        assert (a[b], n[b]) == verify_sample(p[b], q[b], drafts[b], u[b], target_is_probs=True), b
+
+
+@pytest.mark.parametrize("T,top_k", [(1.0, 0), (1.0, 4), (0.7, 17), (1.3, 511)])
+def test_verify_logits_bitexact(T, top_k):
+    B, gamma, V = 8, 12, 512
+    rng = np.random.default_rng(int(T * 10) + top_k)
+    logits = torch.from_numpy(rng.normal(0, 2.0, (B, gamma + 1, V)).astype(np.float32)).to(torch.bfloat16)
+    q = es.draft_probs_softmax((B, gamma), V, seed=top_k)
+    drafts = es.gen.sample_from(q, seed=top_k + 1)
+    # make some drafts the target argmax so that acceptance runs deep
+    lf = logits.float().numpy()
+    for b in range(0, B, 2):
+        drafts[b, : gamma // 2] = lf[b, : gamma // 2].argmax(-1)
+    u = es.uniforms((B, gamma + 1), seed=top_k + 2)
+    a, n = _run_verify(B, gamma, V, logits.to(DEV), evs.EVS_TARGET_LOGITS_BF16, q, drafts, u, T, top_k)
+    for b in range(B):
+        assert (a[b], n[b]) == verify_sample(lf[b], q[b], drafts[b], u[b], T, top_k), b
+
+
+def test_verify_greedy_bitexact_with_ties():
+    B, gamma, V = 8, 12, 512
+    rng = np.random.default_rng(11)
+    lf = rng.integers(-3, 4, (B, gamma + 1, V)).astype(np.float32)     # many exact ties
+    drafts = np.where(rng.random((B, gamma)) < 0.8, lf[:, :gamma].argmax(-1), rng.integers(0, V, (B, gamma)))
+    drafts = drafts.astype(np.int32)
+    logits = torch.from_numpy(lf).to(torch.bfloat16).to(DEV)
+    a, n = _run_verify(B, gamma, V, logits, evs.EVS_TARGET_LOGITS_BF16, None, drafts, None, greedy=1)
+    for b in range(B):
+        assert (a[b], n[b]) == verify_greedy(lf[b], drafts[b]), b
