@@ -7,8 +7,8 @@
 // is split over keys: chunk c holds keys [256c, 256c+256) and workgroup j of a
 // (sequence, query tile, head) visits chunks j, j+S, j+2S, ...; inside a chunk
 // wave w takes key tiles 4w .. 4w+3. Each wave keeps an online softmax in fp32,
-// waves merge in order inside the workgroup, and the last-arriving workgroup
-// of the S merges their partials in order. Every split boundary sits at an
+// waves merge in order inside the workgroup, and a second small kernel merges
+// the S workgroup partials in order. Every split boundary sits at an
 // absolute key position and masked keys contribute exact zeros, so a query's
 // result does not depend on how many other queries share the block.
 //
@@ -41,9 +41,6 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
   constexpr int ROW = DH + 2;
   __shared__ float wm[4][16], wl[4][16];
   __shared__ float wo[4][16][DH];
-  __shared__ float fac[64][16];
-  __shared__ float fl[16];
-  __shared__ int flag_s;
 
   const int j = blockIdx.x, h = blockIdx.y;
   const int bl = blockIdx.z / a.QTN, qt = blockIdx.z % a.QTN;
@@ -161,14 +158,21 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
     }
     part[((size_t)j * 16 + q) * ROW + e] = v;
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) flag_s = (atomicAdd(a.cnt + head, 1) == a.S - 1);
-  __syncthreads();
-  if (!flag_s) return;
-  __threadfence();
+}
 
-  // last arriver: merge the S partials in order
+// Merge the S workgroup partials of one (sequence, query tile, head) in split
+// order and write the normalised output rows. A separate launch, so the
+// partials are visible by kernel ordering alone.
+template <typename T, int DH>
+__global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
+  constexpr int ROW = DH + 2;
+  __shared__ float fac[64][16];
+  __shared__ float fl[16];
+  const int h = blockIdx.x;
+  const int bl = blockIdx.y / a.QTN, qt = blockIdx.y % a.QTN;
+  const int tid = threadIdx.x, P = a.P;
+  const size_t head = (size_t)blockIdx.y * a.H + h;
+  const float* part = a.part + head * a.S * 16 * ROW;
   if (tid < 16) {
     const int q = tid;
     float M = -INFINITY;
@@ -191,17 +195,16 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
     for (int s = 0; s < a.S; ++s) v += part[((size_t)s * 16 + q) * ROW + e] * fac[s][q];
     out[(size_t)(bl * P + qt * 16 + q) * a.d + h * DH + e] = from_f<T>(v / fl[q]);
   }
-  if (tid == 0) a.cnt[head] = 0;
 }
 
 template <typename T>
 hipError_t launch_attn(const AttnArgs& a, int n_seq, hipStream_t st) {
   if (a.S > 64 || a.S < 1) return hipErrorInvalidValue;
-  dim3 grid(a.S, a.H, n_seq * a.QTN), block(256);
+  dim3 grid(a.S, a.H, n_seq * a.QTN), block(256), cgrid(a.H, n_seq * a.QTN);
   switch (a.Dh) {
-    case 32: attn_kernel<T, 32><<<grid, block, 0, st>>>(a); break;
-    case 64: attn_kernel<T, 64><<<grid, block, 0, st>>>(a); break;
-    case 128: attn_kernel<T, 128><<<grid, block, 0, st>>>(a); break;
+    case 32: attn_kernel<T, 32><<<grid, block, 0, st>>>(a); attn_combine_kernel<T, 32><<<cgrid, block, 0, st>>>(a); break;
+    case 64: attn_kernel<T, 64><<<grid, block, 0, st>>>(a); attn_combine_kernel<T, 64><<<cgrid, block, 0, st>>>(a); break;
+    case 128: attn_kernel<T, 128><<<grid, block, 0, st>>>(a); attn_combine_kernel<T, 128><<<cgrid, block, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -20,6 +20,7 @@ namespace {
 constexpr size_t ALIGN = 256;
 constexpr int MAX_ROWS_PER_WG = 144;   // 9 MFMA row tiles
 constexpr int GEMM_CNT = 65536;        // split-K arrival counters
+constexpr int GEMM_WAVES = 8;          // waves per GEMM workgroup (gemm_kernel default)
 
 size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
 int next_pow2(int x) { int p = 1; while (p < x) p <<= 1; return p; }
@@ -158,10 +159,11 @@ std::vector<Canon> canon_list(const evs_model_desc* d) {
 
 // workgroup k-split so that a launch has >= ~256 workgroups while each keeps
 // >= 8 k-steps
+// (k-splits meet through device-scope fences, whose L2 write-back costs more
+// than the parallelism gains at these sizes, so every GEMM runs unsplit)
 int choose_ks(int n_groups, int ksteps, int slices) {
-  int ks = 1;
-  while (n_groups * slices * ks < 256 && ksteps / (ks * 2) >= 8 && ks < 16) ks *= 2;
-  return ks;
+  (void)n_groups; (void)ksteps; (void)slices;
+  return 1;
 }
 
 struct Slicing { int rows_per_slice, slices, MT; };
@@ -284,6 +286,15 @@ evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int 
   a.n_groups = mat.n_groups;
   a.KS = choose_ks(mat.n_groups, a.ksteps, sl.slices);
   a.kps = (a.ksteps + a.KS - 1) / a.KS;
+  if (a.KS != 1) return EVS_E_UNSUPPORTED;
+  // packed layout: [group][k-step][NT][64 lanes]; wave w of a workgroup owns
+  // the contiguous k-steps [w * per_wave, (w + 1) * per_wave)
+  {
+    const long long per_wave = (a.ksteps + GEMM_WAVES - 1) / GEMM_WAVES;
+    a.gstride = (long long)a.ksteps * mat.NT * 64;
+    a.wstride = per_wave * mat.NT * 64;
+    a.tstride = (long long)mat.NT * 64;
+  }
   a.A = A;
   a.lda = lda;
   a.M = nseq * P;

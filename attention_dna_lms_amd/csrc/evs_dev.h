@@ -12,6 +12,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // A 16-byte fragment per lane feeds one 16x16 MFMA step: E elements of the
 // storage type, KSTEP = 4 * E reduction slots per step for the whole wave.
@@ -78,7 +79,10 @@ struct MixArgs {
 };
 
 struct GemmArgs {
-  const uint4* W;        // packed [n_groups][ksteps][NT][64] fragments
+  const uint4* W;        // packed MFMA fragments (16 bytes per lane)
+  long long gstride;     // fragment-row stride (in 16-byte units) between groups,
+  long long wstride;     //   between the waves of a group,
+  long long tstride;     //   and between consecutive k-steps of one wave
   int ksteps;            // K / KSTEP
   int n_groups;
   int KS;                // k-splits across workgroups (grid.x = n_groups * KS)
@@ -107,7 +111,7 @@ struct AttnArgs {
   const int* t;
   float scale;
   float* part;           // [B_call, QTN, H, S, 16, Dh + 2]
-  int* cnt;              // [B_call, QTN, H]
+  int* cnt;              // unused (kept for layout stability)
 };
 
 constexpr int ATTN_CHUNK = 256;   // keys per chunk (4 waves x 4 tiles of 16)

@@ -23,8 +23,8 @@
 
 namespace evs {
 
-template <int MT, int NT> struct GemmCfg {
-  static constexpr int WAVES = 8;
+template <int MT, int NT, int WV = 8> struct GemmCfg {
+  static constexpr int WAVES = WV;
   static constexpr int BUFS = (4 * NT * MT <= 48) ? 4 : ((2 * NT * MT <= 48) ? 2 : 1);
   static constexpr int RS = NT * MT * 256;                          // floats per wave partial
 };
@@ -34,6 +34,12 @@ template <int MT, int NT> struct GemmCfg {
 // never stalls the load pipeline). Rows past `rows` re-read the last valid
 // row: an MFMA output column depends only on its own activation row and the
 // columns of rows past `rows` are never stored, so no masking is needed.
+// weights are read exactly once per call: non-temporal loads keep them from
+// displacing the activations in the caches
+__device__ __forceinline__ uint4 ld_stream(const u32x4* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(p));
+}
+
 template <typename T, int AMODE> struct AFrag;
 template <typename T> struct AFrag<T, A_ACT> {            // storage-type rows
   uint4 v;
@@ -279,16 +285,17 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
 }
 
 // ---------------------------------------------------------------- kernel
-template <typename T, int MT, int NT, int AMODE, int EPI>
-__global__ void __launch_bounds__(512) gemm_kernel(GemmArgs a) {
-  using C = GemmCfg<MT, NT>;
+template <typename T, int MT, int NT, int AMODE, int EPI, int WV = 8, int CHO = 0>
+__global__ void __launch_bounds__(WV * 64) gemm_kernel(GemmArgs a) {
+  static_assert(EPI != E_MIXER || WV == 8, "the mixer epilogue assumes 512 threads");
+  using C = GemmCfg<MT, NT, WV>;
   constexpr int E = St<T>::E, KSTEP = St<T>::KSTEP, RS = C::RS;
   // k-steps per pipeline chunk: one chunk of NT weight fragments and MT
   // activation fragments (8 registers each for fp32 rows feeding bf16, else 4)
   // per step stays within ~80 registers, two chunks within ~160
   constexpr int AREG = (AMODE == A_NORM && sizeof(T) == 2) ? 2 : 1;
   constexpr int PER = 20 / (NT + AREG * MT);
-  constexpr int CH = PER >= 8 ? 8 : PER >= 4 ? 4 : PER >= 2 ? 2 : 1;
+  constexpr int CH = CHO ? CHO : PER >= 8 ? 8 : PER >= 4 ? 4 : PER >= 2 ? 2 : 1;
   extern __shared__ float lds[];
   __shared__ int flag_s;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -305,7 +312,9 @@ __global__ void __launch_bounds__(512) gemm_kernel(GemmArgs a) {
   const int per_wave = (ke - kb + C::WAVES - 1) / C::WAVES;
   const int wk0 = min(kb + wave * per_wave, ke), wk1 = min(wk0 + per_wave, ke);
   const int nch = (wk1 - wk0) / CH;          // full chunks of CH k-steps
-  const uint4* wp = a.W + (size_t)g * a.ksteps * NT * 64 + lane;
+  // this wave's fragment stream: step i of the wave's k-range lives at
+  // wp[i * tstride + nt * 64] (the packed layout fixes the strides)
+  const u32x4* wp = reinterpret_cast<const u32x4*>(a.W) + (size_t)g * a.gstride + (size_t)wave * a.wstride + lane;
   const int rl = lane & 15, aoff = (lane >> 4) * E;
 
   // epilogue inputs first (only the workgroup that runs the epilogue needs
@@ -324,7 +333,7 @@ __global__ void __launch_bounds__(512) gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < CH; ++u)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) w[u][nt] = wp[((size_t)(k0 + u) * NT + nt) * 64];
+      for (int nt = 0; nt < NT; ++nt) w[u][nt] = ld_stream(wp + (size_t)(k0 - wk0 + u) * a.tstride + nt * 64);
   };
   auto issue_x = [&](AFrag<T, AMODE> (&x)[CH][MT], int k0) {
 #pragma unroll
@@ -416,7 +425,7 @@ __global__ void __launch_bounds__(512) gemm_kernel(GemmArgs a) {
     uint4 wr[NT];
     AFrag<T, AMODE> xr[MT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) wr[nt] = wp[((size_t)k * NT + nt) * 64];
+    for (int nt = 0; nt < NT; ++nt) wr[nt] = ld_stream(wp + (size_t)(k - wk0) * a.tstride + nt * 64);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) xr[mt].load(a, arow[mt], k * KSTEP + aoff);
 #pragma unroll
