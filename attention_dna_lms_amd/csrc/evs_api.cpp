@@ -177,10 +177,31 @@ Slicing slicing(int nseq, int P) {
   return s;
 }
 
+// The balanced (stream-K) launch serves the gated-MLP gate/up projection when
+// its column groups do not divide evenly over the workgroups: one 16-row tile,
+// each wave's run of k-steps within one group boundary, each group within two
+// workgroups.
+bool use_sk(const Mat& mat, int ksteps, int amode, int epi, const Slicing& sl) {
+  if (!(mat.NT == 2 && amode == A_NORM && epi == E_GELU)) return false;
+  if (sl.slices != 1 || sl.MT != 1) return false;
+  if (mat.n_groups <= SK_WGS || mat.n_groups % SK_WGS == 0) return false;
+  const long long total = (long long)mat.n_groups * ksteps;
+  const long long per_wave = (total + SK_WGS * 8 - 1) / (SK_WGS * 8);
+  const long long per_wg = (total + SK_WGS - 1) / SK_WGS;
+  const long long max_groups = (ksteps - 1 + per_wg - 1) / ksteps + 1;   // groups one workgroup touches
+  return per_wave <= ksteps && total / SK_WGS >= ksteps && max_groups <= 4;
+}
+size_t sk_part_floats(const Mat& mat) { return (size_t)mat.n_groups * 2 * mat.NT * 256; }
+size_t sk_lds(const Mat& mat) { return 4 * (16 + (size_t)8 * 2 * mat.NT * 256 + (size_t)mat.NT * 256); }
+
 int gemm_bufs(int MT, int NT) { return (4 * NT * MT <= 48) ? 4 : ((2 * NT * MT <= 48) ? 2 : 1); }
 
+// LDS of a gemm_kernel launch: row scales, then either all 8 wave partials
+// followed by the epilogue tile (small tiles, one-barrier reduction) or the
+// staged-tree buffers overlapped with the epilogue tile.
 size_t gemm_lds(int MT, int NT, int scratch_floats) {
   const size_t RS = (size_t)NT * MT * 256;
+  if (NT * MT <= 4) return 4 * (MT * 16 + 9 * RS + (size_t)scratch_floats);
   return 4 * (MT * 16 + std::max(gemm_bufs(MT, NT) * RS, RS + (size_t)scratch_floats));
 }
 
@@ -228,6 +249,8 @@ void layout_state(evs_state* s) {
         if (ks > 1) pf = std::max(pf, (size_t)sl.slices * mm.n_groups * ks * mm.NT * sl.MT * 256);
       };
       for (const auto& p : m->plan) {
+        if (p.d.kind == EVS_MLP && use_sk(p.w_gu, p.w_gu.K / m->kstep, A_NORM, E_GELU, sl))
+          pf = std::max(pf, sk_part_floats(p.w_gu));
         if (p.d.kind == EVS_MLP) { acc(p.w_gu); acc(p.w_down); }
         else { acc(p.w_in); acc(p.w_out); }
       }
@@ -310,11 +333,16 @@ evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int 
     if ((size_t)sl.slices * mat.n_groups * a.KS * mat.NT * sl.MT * 256 > s->part_floats) return EVS_E_RANGE;
     if ((size_t)sl.slices * mat.n_groups > (size_t)GEMM_CNT) return EVS_E_RANGE;
   }
-  const size_t lds = gemm_lds(sl.MT, mat.NT, scratch_floats);
-  if (lds > 65536) return EVS_E_UNSUPPORTED;
   // algorithmic bytes: the weights once, the A rows once, the outputs once
   const double bytes = (double)mat.bytes(m->es) + (double)a.M * mat.K * (amode == A_NORM ? 4 : m->es) +
                        (double)a.M * mat.rows_valid * (epi == E_RESID ? 8 : m->es);
+  if (use_sk(mat, a.ksteps, amode, epi, sl)) {
+    if (sk_part_floats(mat) > s->part_floats || (size_t)mat.n_groups > (size_t)GEMM_CNT) return EVS_E_RANGE;
+    const size_t lds = sk_lds(mat);
+    return hip_ok(timed(s, EVS_KC_GEMM, bytes, st, [&] { return launch_gemm_sk<T>(mat.NT, amode, epi, a, lds, st); }));
+  }
+  const size_t lds = gemm_lds(sl.MT, mat.NT, scratch_floats);
+  if (lds > 65536) return EVS_E_UNSUPPORTED;
   return hip_ok(timed(s, EVS_KC_GEMM, bytes, st,
                       [&] { return launch_gemm<T>(sl.MT, mat.NT, amode, epi, a, sl.slices, lds, st); }));
 }
@@ -349,7 +377,7 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
       mx.kind = MIX_FIR;
       mx.ring = sp<float>(s, s->ring[i]); mx.R = s->R[i]; mx.ring_bs = (long long)s->R[i] * d;
       mx.taps = reinterpret_cast<const float*>(m->base + p.taps); mx.L = p.d.fir_len;
-      scratch = (p.d.fir_len - 1 + P) * 16 + 16 * p.d.fir_len;   // window + taps
+      scratch = (p.d.fir_len - 1 + P) * 16 + 16 * (p.d.fir_len | 1);   // window + taps (odd row stride)
       a.out = wp<void>(s, s->w_o);
     } else if (p.d.kind == EVS_IIR) {
       mx.kind = MIX_IIR;
@@ -358,6 +386,7 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
       mx.iir_bs = 2 * mx.iir_buf_s;
       mx.lam = reinterpret_cast<const float*>(m->base + p.lam);
       mx.res = reinterpret_cast<const float*>(m->base + p.res);
+      scratch = IIR_CH * 256 + 256;   // one chunk of modes + the residues
       a.out = wp<void>(s, s->w_o);
     } else {
       mx.kind = MIX_ATTN;

@@ -115,6 +115,7 @@ struct AttnArgs {
 };
 
 constexpr int ATTN_CHUNK = 256;   // keys per chunk (4 waves x 4 tiles of 16)
+constexpr int IIR_CH = 16;        // positions per chunk of the IIR mixer epilogue
 
 struct VerifyArgs {
   int gamma, V, kind, top_k, greedy;
@@ -127,6 +128,9 @@ struct VerifyArgs {
 template <typename T>
 hipError_t launch_gemm(int MT, int NT, int amode, int epi, const GemmArgs& a, int slices,
                        size_t lds_bytes, hipStream_t st);
+template <typename T>
+hipError_t launch_gemm_sk(int NT, int amode, int epi, const GemmArgs& a, size_t lds_bytes, hipStream_t st);
+constexpr int SK_WGS = 256;   // workgroups of a balanced (stream-K) GEMM launch
 template <typename T>
 hipError_t launch_attn(const AttnArgs& a, int n_seq, hipStream_t st);
 template <typename T>

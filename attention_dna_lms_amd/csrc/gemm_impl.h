@@ -27,6 +27,7 @@ template <int MT, int NT, int WV = 8> struct GemmCfg {
   static constexpr int WAVES = WV;
   static constexpr int BUFS = (4 * NT * MT <= 48) ? 4 : ((2 * NT * MT <= 48) ? 2 : 1);
   static constexpr int RS = NT * MT * 256;                          // floats per wave partial
+  static constexpr bool FLAT = WV == 8 && NT * MT <= 4;             // one-barrier reduction
 };
 
 // Activation fragment of one k-step for one 16-row tile, loaded raw and
@@ -203,17 +204,18 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
       }
     } else if (x.kind == MIX_FIR) {
       const int L = x.L, W = L - 1 + P;
+      const int LP = L | 1;            // odd row stride: the 16 channels' taps sit in 16 distinct banks
       const bool pre = L <= FIR_PRE * 32;
-      float* tp = scratch;             // [16][L] taps
-      float* hw = scratch + 16 * L;    // [W][16]: filter inputs at positions t-L+1 .. t+P-1
+      float* tp = scratch;             // [16][LP] taps
+      float* hw = scratch + 16 * LP;   // [W][16]: filter inputs at positions t-L+1 .. t+P-1
       if (pre) {
 #pragma unroll
         for (int q = 0; q < FIR_PRE; ++q) {
           const int idx = tid + q * 512;
-          if (idx < 16 * L) tp[idx] = pf.tap[q];
+          if (idx < 16 * L) tp[(idx / L) * LP + idx % L] = pf.tap[q];
         }
       } else {
-        for (int idx = tid; idx < 16 * L; idx += nth) tp[idx] = x.taps[(size_t)(ch0 + idx / L) * L + idx % L];
+        for (int idx = tid; idx < 16 * L; idx += nth) tp[(idx / L) * LP + idx % L] = x.taps[(size_t)(ch0 + idx / L) * L + idx % L];
       }
       for (int j = 0; j < nseq; ++j) {
         const int b = sbase + j;
@@ -241,23 +243,43 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
         __syncthreads();
         for (int idx = tid; idx < P * 16; idx += nth) {
           const int p = idx >> 4, c = idx & 15, m = j * P + p;
-          const float* tc = tp + c * L;
+          const float* tc = tp + c * LP;
+          const float* hc = hw + (L - 1 + p) * 16 + c;   // input at lag jj: hc[-16 * jj]
+          // taps in order 0 .. L-1 (one fma chain); the LDS reads of 16 taps go
+          // out together ahead of their fmas
           float y = 0.f;
-          for (int jj = 0; jj < L; ++jj) y = fmaf(tc[jj], hw[(L - 1 + p - jj) * 16 + c], y);
+          int jj = 0;
+          for (; jj + 16 <= L; jj += 16) {
+            float tv[16], hv[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) { tv[q] = tc[jj + q]; hv[q] = hc[-16 * (jj + q)]; }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) y = fmaf(tv[q], hv[q], y);
+          }
+          for (; jj < L; ++jj) y = fmaf(tc[jj], hc[-16 * jj], y);
           out[(size_t)(row0 + m) * a.ldo + ch0 + c] = from_f<T>(rnd<T>(eq[m * 16 + c]) * y);
         }
         __syncthreads();
       }
       (void)W;
-    } else {  // MIX_IIR: lanes (c, n), 16 modes of one channel in 16 adjacent lanes
+    } else {  // MIX_IIR
+      // Per chunk of up to IIR_CH positions: (1) lanes (c, n), the 16 modes of
+      // one channel in 16 adjacent lanes, run the recurrence in position order
+      // (one fma per step), writing every position's modes to the state and to
+      // LDS; (2) threads (position, channel) sum the 16 mode contributions in
+      // the fixed order ((r0+r8)+(r4+r12)) + ((r2+r10)+(r6+r14)) +
+      // (((r1+r9)+(r5+r13)) + ((r3+r11)+(r7+r15))).
+      float* sb = scratch;                    // [IIR_CH][16 channels][16 modes]
+      float* rb = scratch + IIR_CH * 256;     // [16 channels][16 modes] residues
+      const int c = (tid >> 4) & 15, n = tid & 15, ch = ch0 + c;
+      const bool vn = n < x.N;
       for (int j = 0; j < nseq; ++j) {
         const int b = sbase + j;
+        const int buf = x.iir_buf[b], slot = x.iir_slot[b];
+        float* base = x.iirst + (size_t)b * x.iir_bs;
+        float s = 0.f, lam = 0.f;
         if (tid < 256) {
-          const int c = tid >> 4, n = tid & 15, ch = ch0 + c;
-          const bool vn = n < x.N;
-          const int buf = x.iir_buf[b], slot = x.iir_slot[b];
-          float* base = x.iirst + (size_t)b * x.iir_bs;
-          float s, lam, res;
+          float res;
           if (j == 0) {
             s = pf.s0; lam = pf.lam; res = pf.res;
           } else {
@@ -265,19 +287,40 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
             lam = vn ? x.lam[(size_t)ch * x.N + n] : 0.f;
             res = vn ? x.res[(size_t)ch * x.N + n] : 0.f;
           }
-          float* dst = base + (size_t)(buf ^ 1) * x.iir_buf_s;
-          for (int p = 0; p < P; ++p) {
-            const int m = j * P + p;
-            const float h = rnd<T>(ek[m * 16 + c]) * rnd<T>(ev[m * 16 + c]);
-            s = fmaf(lam, s, h);
-            if (vn) dst[((size_t)p * x.d + ch) * x.N + n] = s;
-            float r = vn ? res * s : 0.f;
-            r += __shfl_xor(r, 8, 16);
-            r += __shfl_xor(r, 4, 16);
-            r += __shfl_xor(r, 2, 16);
-            r += __shfl_xor(r, 1, 16);
-            if (n == 0) out[(size_t)(row0 + m) * a.ldo + ch] = from_f<T>(rnd<T>(eq[m * 16 + c]) * r);
+          rb[tid] = res;
+        }
+        float* dst = base + (size_t)(buf ^ 1) * x.iir_buf_s;
+        for (int p0 = 0; p0 < P; p0 += IIR_CH) {
+          const int np = min(IIR_CH, P - p0);
+          if (tid < 256) {
+            float hv[IIR_CH];
+#pragma unroll
+            for (int q = 0; q < IIR_CH; ++q) {
+              const int m = j * P + p0 + min(q, np - 1);
+              hv[q] = rnd<T>(ek[m * 16 + c]) * rnd<T>(ev[m * 16 + c]);
+            }
+#pragma unroll
+            for (int q = 0; q < IIR_CH; ++q) {
+              if (q < np) {
+                s = fmaf(lam, s, hv[q]);
+                if (vn) dst[((size_t)(p0 + q) * x.d + ch) * x.N + n] = s;
+                sb[q * 256 + tid] = s;
+              }
+            }
           }
+          __syncthreads();
+          for (int idx = tid; idx < np * 16; idx += nth) {
+            const int q = idx >> 4, cc = idx & 15, m = j * P + p0 + q;
+            const float* sp = sb + q * 256 + cc * 16;
+            const float* rp = rb + cc * 16;
+            float r[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) r[k] = k < x.N ? rp[k] * sp[k] : 0.f;
+            const float tot = (((r[0] + r[8]) + (r[4] + r[12])) + ((r[2] + r[10]) + (r[6] + r[14]))) +
+                              (((r[1] + r[9]) + (r[5] + r[13])) + ((r[3] + r[11]) + (r[7] + r[15])));
+            out[(size_t)(row0 + m) * a.ldo + ch0 + cc] = from_f<T>(rnd<T>(eq[m * 16 + cc]) * tot);
+          }
+          __syncthreads();
         }
       }
     }
@@ -292,12 +335,11 @@ __global__ void __launch_bounds__(WV * 64) gemm_kernel(GemmArgs a) {
   constexpr int E = St<T>::E, KSTEP = St<T>::KSTEP, RS = C::RS;
   // k-steps per pipeline chunk: one chunk of NT weight fragments and MT
   // activation fragments (8 registers each for fp32 rows feeding bf16, else 4)
-  // per step stays within ~80 registers, two chunks within ~160
+  // per step stays within ~64 registers, the two chunks in flight within ~128
   constexpr int AREG = (AMODE == A_NORM && sizeof(T) == 2) ? 2 : 1;
-  constexpr int PER = 20 / (NT + AREG * MT);
-  constexpr int CH = CHO ? CHO : PER >= 8 ? 8 : PER >= 4 ? 4 : PER >= 2 ? 2 : 1;
+  constexpr int PER = 16 / (NT + AREG * MT);
+  constexpr int CH = CHO ? CHO : PER >= 8 ? 8 : PER >= 1 ? PER : 1;
   extern __shared__ float lds[];
-  __shared__ int flag_s;
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform values live in scalar registers, so every guard below is a
   // uniform branch and the load/wait schedule stays exact
@@ -311,10 +353,14 @@ __global__ void __launch_bounds__(WV * 64) gemm_kernel(GemmArgs a) {
   const int kb = s * a.kps, ke = min(kb + a.kps, a.ksteps);
   const int per_wave = (ke - kb + C::WAVES - 1) / C::WAVES;
   const int wk0 = min(kb + wave * per_wave, ke), wk1 = min(wk0 + per_wave, ke);
-  const int nch = (wk1 - wk0) / CH;          // full chunks of CH k-steps
+  const int nch = (wk1 - wk0 + CH - 1) / CH;   // chunks of CH k-steps (the last may be partial)
   // this wave's fragment stream: step i of the wave's k-range lives at
-  // wp[i * tstride + nt * 64] (the packed layout fixes the strides)
-  const u32x4* wp = reinterpret_cast<const u32x4*>(a.W) + (size_t)g * a.gstride + (size_t)wave * a.wstride + lane;
+  // wp[i * tstride + nt * 64] (the packed layout fixes the strides). A wave
+  // with no k-steps streams nothing useful: its (never consumed) loads read
+  // the matrix's first fragment, so every load below is unconditional and
+  // each wait covers exactly the loads it needs.
+  const u32x4* wp = reinterpret_cast<const u32x4*>(a.W) + lane +
+                    (nch > 0 ? (size_t)g * a.gstride + (size_t)wave * a.wstride : 0);
   const int rl = lane & 15, aoff = (lane >> 4) * E;
 
   // epilogue inputs first (only the workgroup that runs the epilogue needs
@@ -329,17 +375,20 @@ __global__ void __launch_bounds__(WV * 64) gemm_kernel(GemmArgs a) {
   // two chunk buffers
   uint4 w0[CH][NT], w1[CH][NT];
   AFrag<T, AMODE> x0[CH][MT], x1[CH][MT];
+  // steps past wk1 (the tail of the last chunk, or the chunk after it)
+  // re-read step wk1 - 1 and are skipped by compute
+  auto wstep = [&](int k) { return max(min(k, wk1 - 1) - wk0, 0); };
   auto issue_w = [&](uint4 (&w)[CH][NT], int k0) {
 #pragma unroll
     for (int u = 0; u < CH; ++u)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) w[u][nt] = ld_stream(wp + (size_t)(k0 - wk0 + u) * a.tstride + nt * 64);
+      for (int nt = 0; nt < NT; ++nt) w[u][nt] = ld_stream(wp + (size_t)wstep(k0 + u) * a.tstride + nt * 64);
   };
   auto issue_x = [&](AFrag<T, AMODE> (&x)[CH][MT], int k0) {
 #pragma unroll
     for (int u = 0; u < CH; ++u)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) x[u][mt].load(a, arow[mt], (k0 + u) * KSTEP + aoff);
+      for (int mt = 0; mt < MT; ++mt) x[u][mt].load(a, arow[mt], max(min(k0 + u, wk1 - 1), 0) * KSTEP + aoff);
   };
   f32x4 acc[NT][MT];
 #pragma unroll
@@ -347,42 +396,67 @@ __global__ void __launch_bounds__(WV * 64) gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float rr[MT];   // this lane's RMSNorm scale per row tile (A_NORM)
-  auto compute = [&](uint4 (&w)[CH][NT], AFrag<T, AMODE> (&x)[CH][MT]) {
+  auto compute = [&](uint4 (&w)[CH][NT], AFrag<T, AMODE> (&x)[CH][MT], int k0) {
 #pragma unroll
-    for (int u = 0; u < CH; ++u)
+    for (int u = 0; u < CH; ++u) {
+      if (k0 + u >= wk1) break;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const uint4 xv = x[u][mt].get(rr[mt]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt][mt] = mma_frag(w[u][nt], xv, acc[nt][mt], T());
       }
+    }
   };
 
-  // the first chunk's weights go out before the norm prologue
-  if (nch > 0) issue_w(w0, wk0);
+  // Start-up order: the norm's per-16-column sums of squares are loaded
+  // first, then the first two chunks of activations and weights, and only
+  // then does the norm prologue wait (for its own loads alone), so the
+  // weight stream starts at once and two chunks are in flight from the start.
+  // (many-row launches skip the early load: its registers would spill)
+  constexpr int NP = AMODE == A_NORM ? (MT * 16 * 32 + C::WAVES * 64 - 1) / (C::WAVES * 64) : 1;
+  constexpr bool PRE = AMODE == A_NORM && MT <= 2;
+  float nv[PRE ? NP : 1][8];
+  const bool nrm_pre = PRE && a.n_part <= 256;
+  if constexpr (PRE) {
+#pragma unroll
+    for (int pss = 0; pss < NP; ++pss) {
+      const int idx = pss * C::WAVES * 64 + tid, r = idx >> 5, j = idx & 31;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = j + 32 * q;
+        nv[pss][q] = (nrm_pre && r < rows && i < a.n_part) ? a.nrm_part[(size_t)i * a.nrm_ld + row0 + r] : 0.f;
+      }
+    }
+  }
+  issue_x(x0, wk0);
+  issue_w(w0, wk0);
+  issue_x(x1, wk0 + CH);
+  issue_w(w1, wk0 + CH);
 
   if constexpr (AMODE == A_NORM) {
-    // rinv[r] = 1 / sqrt(mean(x_r^2) + eps) from the per-16-column sums of
-    // squares: 32 lanes per row each add 8 partials (all loads in flight at
-    // once), then a fixed butterfly over the 32 lanes.
-    for (int base = 0; base < MT * 16 * 32; base += C::WAVES * 64) {   // whole waves per pass
-      const int idx = base + tid;
+    // rinv[r] = 1 / sqrt(mean(x_r^2) + eps): 32 lanes per row each add 8
+    // partials (per pass of 256 partials), then a fixed butterfly over the 32.
+#pragma unroll
+    for (int pss = 0; pss < NP; ++pss) {
+      const int idx = pss * C::WAVES * 64 + tid;
       const int r = idx >> 5, j = idx & 31;
-      if (r < MT * 16) {
-        float sum = 0.f;
-        for (int i0 = 0; i0 < a.n_part; i0 += 256) {
-          float v[8];
+      float sum = 0.f;
+      if constexpr (PRE)
+        sum = ((nv[pss][0] + nv[pss][1]) + (nv[pss][2] + nv[pss][3])) +
+              ((nv[pss][4] + nv[pss][5]) + (nv[pss][6] + nv[pss][7]));
+      for (int i0 = nrm_pre ? a.n_part : 0; i0 < a.n_part; i0 += 256) {   // wide models only
+        float v[8];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const int i = i0 + j + 32 * q;
-            v[q] = (r < rows && i < a.n_part) ? a.nrm_part[(size_t)i * a.nrm_ld + row0 + r] : 0.f;
-          }
-          sum += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+        for (int q = 0; q < 8; ++q) {
+          const int i = i0 + j + 32 * q;
+          v[q] = (r < rows && i < a.n_part) ? a.nrm_part[(size_t)i * a.nrm_ld + row0 + r] : 0.f;
         }
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 32);
-        if (j == 0) rinv[r] = (r < rows) ? 1.0f / sqrtf(sum / a.fd + a.eps) : 0.f;
+        sum += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
       }
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 32);
+      if (j == 0 && r < MT * 16) rinv[r] = (r < rows) ? 1.0f / sqrtf(sum / a.fd + a.eps) : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -391,120 +465,100 @@ __global__ void __launch_bounds__(WV * 64) gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) rr[mt] = 1.f;
   }
-  if (nch > 0) issue_x(x0, wk0);
 
-  // chunk pipeline: the next chunk's loads are issued (and pinned ahead by a
-  // scheduling barrier) before this chunk computes; inside the loop the issue
-  // is unconditional, so each MFMA waits only for its own fragments.
-  if (nch > 0) {
+  // chunk pipeline: chunks c and c + 1 are in flight while chunk c computes;
+  // the loop body issues unconditionally (the tail is peeled), so each MFMA
+  // waits only for its own fragments.
+  {
     int c = 0;
-    for (; c + 2 < nch; c += 2) {
-      issue_w(w1, wk0 + (c + 1) * CH);
-      issue_x(x1, wk0 + (c + 1) * CH);
+    for (; c + 3 < nch; c += 2) {
+      compute(w0, x0, wk0 + c * CH);
       __builtin_amdgcn_sched_barrier(0);
-      compute(w0, x0);
-      __builtin_amdgcn_sched_barrier(0);
-      issue_w(w0, wk0 + (c + 2) * CH);
       issue_x(x0, wk0 + (c + 2) * CH);
+      issue_w(w0, wk0 + (c + 2) * CH);
       __builtin_amdgcn_sched_barrier(0);
-      compute(w1, x1);
+      compute(w1, x1, wk0 + (c + 1) * CH);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_x(x1, wk0 + (c + 3) * CH);
+      issue_w(w1, wk0 + (c + 3) * CH);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (c + 1 < nch) {
-      issue_w(w1, wk0 + (c + 1) * CH);
-      issue_x(x1, wk0 + (c + 1) * CH);
+    if (nch - c == 3) {
+      compute(w0, x0, wk0 + c * CH);
       __builtin_amdgcn_sched_barrier(0);
-      compute(w0, x0);
-      compute(w1, x1);
-    } else {
-      compute(w0, x0);
-    }
-  }
-  // leftover k-steps (fewer than CH), one at a time
-  for (int k = wk0 + nch * CH; k < wk1; ++k) {
-    uint4 wr[NT];
-    AFrag<T, AMODE> xr[MT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) wr[nt] = ld_stream(wp + (size_t)(k - wk0) * a.tstride + nt * 64);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) xr[mt].load(a, arow[mt], k * KSTEP + aoff);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint4 xv = xr[mt].get(rr[mt]);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt][mt] = mma_frag(wr[nt], xv, acc[nt][mt], T());
+      issue_x(x0, wk0 + (c + 2) * CH);
+      issue_w(w0, wk0 + (c + 2) * CH);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(w1, x1, wk0 + (c + 1) * CH);
+      compute(w0, x0, wk0 + (c + 2) * CH);
+    } else if (nch - c == 2) {
+      compute(w0, x0, wk0 + c * CH);
+      compute(w1, x1, wk0 + (c + 1) * CH);
+    } else if (nch - c == 1) {
+      compute(w0, x0, wk0 + c * CH);
     }
   }
 
-  // fixed-tree reduction of the 8 waves' partial tiles through LDS
-#pragma unroll
-  for (int n = C::WAVES; n > 1;) {
-    const int h = (C::BUFS < n / 2) ? C::BUFS : n / 2;
-    if (wave >= n - h && wave < n) {
-      float* b = red + (wave - (n - h)) * RS;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          *reinterpret_cast<f32x4*>(b + (nt * MT + mt) * 256 + lane * 4) = acc[nt][mt];
-    }
-    __syncthreads();
-    if (wave >= n - 2 * h && wave < n - h) {
-      const float* b = red + (wave - (n - 2 * h)) * RS;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[nt][mt] += *reinterpret_cast<const f32x4*>(b + (nt * MT + mt) * 256 + lane * 4);
-    }
-    __syncthreads();
-    n -= h;
-  }
-
-  if (a.KS > 1) {
-    const size_t tile = (size_t)blockIdx.y * a.n_groups + g;
-    if (wave == 0) {
-      float* mp = a.part + (tile * a.KS + s) * RS;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          *reinterpret_cast<f32x4*>(mp + (nt * MT + mt) * 256 + lane * 4) = acc[nt][mt];
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) flag_s = (atomicAdd(a.cnt + tile, 1) == a.KS - 1);
-    __syncthreads();
-    if (!flag_s) return;
-    __threadfence();
-    if (wave == 0) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int s2 = 0; s2 < a.KS; ++s2) {
-        const float* pp = a.part + (tile * a.KS + s2) * RS;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            acc[nt][mt] += *reinterpret_cast<const f32x4*>(pp + (nt * MT + mt) * 256 + lane * 4);
-      }
-    }
-    if (tid == 0) a.cnt[tile] = 0;
-  }
-
-  // epilogue tile ep[nt][m][n] (m < MT*16, n < 16)
-  float* ep = red;
-  if (wave == 0) {
+  // Reduction of the 8 waves' partial tiles in the fixed tree
+  // ((w0 + w4) + (w2 + w6)) + ((w1 + w5) + (w3 + w7)). Small tiles: every wave
+  // stores its partial once and each thread sums its elements straight into
+  // the epilogue tile (one barrier). Large tiles: a staged tree through the
+  // BUFS buffers (same association when BUFS = 4).
+  float* ep;
+  if constexpr (C::FLAT) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        *reinterpret_cast<f32x4*>(ep + ((nt * MT * 16 + mt * 16 + rl) * 16 + 4 * (lane >> 4))) = acc[nt][mt];
+        *reinterpret_cast<f32x4*>(red + wave * RS + (nt * MT + mt) * 256 + lane * 4) = acc[nt][mt];
+    __syncthreads();
+    ep = red + C::WAVES * RS;
+    for (int e = tid; e < RS; e += C::WAVES * 64) {
+      const float* pp = red + e;
+      const float v = ((pp[0] + pp[4 * RS]) + (pp[2 * RS] + pp[6 * RS])) +
+                      ((pp[RS] + pp[5 * RS]) + (pp[3 * RS] + pp[7 * RS]));
+      // MFMA D fragment (nt, mt, lane l, i): output column 4 * (l / 16) + i of
+      // activation row 16 * mt + l % 16 -> epilogue tile ep[nt][row][column]
+      const int ntmt = e >> 8, l = (e >> 2) & 63, i = e & 3;
+      const int nt = ntmt / MT, mt = ntmt % MT;
+      ep[((nt * MT * 16 + mt * 16 + (l & 15)) * 16) + 4 * (l >> 4) + i] = v;
+    }
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int n = C::WAVES; n > 1;) {
+      const int h = (C::BUFS < n / 2) ? C::BUFS : n / 2;
+      if (wave >= n - h && wave < n) {
+        float* b = red + (wave - (n - h)) * RS;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            *reinterpret_cast<f32x4*>(b + (nt * MT + mt) * 256 + lane * 4) = acc[nt][mt];
+      }
+      __syncthreads();
+      if (wave >= n - 2 * h && wave < n - h) {
+        const float* b = red + (wave - (n - 2 * h)) * RS;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[nt][mt] += *reinterpret_cast<const f32x4*>(b + (nt * MT + mt) * 256 + lane * 4);
+      }
+      __syncthreads();
+      n -= h;
+    }
+    // epilogue tile ep[nt][m][n] (m < MT*16, n < 16)
+    ep = red;
+    if (wave == 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          *reinterpret_cast<f32x4*>(ep + ((nt * MT * 16 + mt * 16 + rl) * 16 + 4 * (lane >> 4))) = acc[nt][mt];
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (a.KS > 1) epi_prefetch<T, MT, NT, EPI>(a, pf, g, row0, rows);
   gemm_epilogue<T, MT, NT, EPI>(a, pf, ep, ep + NT * MT * 256, g, row0, rows);
 }
 

@@ -204,6 +204,53 @@ def test_block_equals_sequential_and_rollback_equals_steps_bitexact():
                     assert np.array_equal(a[key][i], b[key][i]), (k, key, i)
 
 
+def test_full_width_mlp_streamk_matches_oracle_bitexact_steps():
+    """Full-width gated MLP (d = 4096, d_ff = 11008) as the first block, on the
+    dyadic weight grid so its gate/up sums are exact on both sides: at <= 16
+    rows the gate/up projection runs the balanced (stream-K) launch. Block
+    logits against the oracle, and block == 13 single steps bit for bit."""
+    cfg = ModelConfig("mlp_d4096", 4096, 512,
+                      [Block("mlp", d_ff=11008), Block("fir", fir_len=7), Block("mlp", d_ff=11008)], dtype="bf16")
+    w = es.dyadic_weights(cfg, seed=9)
+    gamma = 12
+    P = gamma + 1
+    prompt = es.prompt_tokens(cfg, 40, seed=9)[0]
+    cand = es.prompt_tokens(cfg, P, seed=10)[0]
+    mA, sA = make_engine(cfg, w, batch=1, max_ctx=128, max_block=16)
+    prefill(mA, sA, [prompt])
+    blk, _ = block_verify(mA, sA, cand[None])
+    orc = HybridLM(cfg, w)
+    _, ost = orc.prefill(prompt, chunk=16)
+    assert logit_err(blk[0], orc.block(ost, cand).logits) < LOGIT_ATOL
+    mB, sB = make_engine(cfg, w, batch=1, max_ctx=128, max_block=16)
+    prefill(mB, sB, [prompt])
+    for k in range(P):
+        one, _ = block_verify(mB, sB, cand[None, k:k + 1])
+        assert np.array_equal(one[0, 0], blk[0, k]), k
+        rollback(sB, [1])
+
+
+def test_full_width_stack_streamk_and_tiled_paths_agree():
+    """Three 7B-width layers with normal random-init weights: a 13-row block
+    (stream-K gate/up) against the same block duplicated in a batch of two (26
+    rows: the per-group tiled gate/up launch). Both are fp32 sums of the same
+    products in different orders, so they agree up to rare bf16 rounding
+    flips; the duplicated rows agree bit for bit."""
+    cfg = es.stack_7b(n_layers=3)
+    w = es.make_weights(cfg, seed=7)
+    P = 13
+    prompt = es.prompt_tokens(cfg, 40, seed=7)[0]
+    cand = es.prompt_tokens(cfg, P, seed=8)[0]
+    m1, s1 = make_engine(cfg, w, batch=1, max_ctx=128, max_block=16)
+    prefill(m1, s1, [prompt])
+    one, _ = block_verify(m1, s1, cand[None])
+    m2, s2 = make_engine(cfg, w, batch=2, max_ctx=128, max_block=16)
+    prefill(m2, s2, [prompt, prompt])
+    two, _ = block_verify(m2, s2, np.stack([cand, cand]))
+    assert np.array_equal(two[0], two[1])
+    assert logit_err(one[0], two[0]) < 0.1
+
+
 def test_identity_drafter_accepts_everything_on_gpu():
     cfg = es.small_stack()
     w = es.make_weights(cfg, seed=5)
