@@ -3,14 +3,16 @@
 // attention state is an append-only KV cache; the block's own K/V rows were
 // appended by the in-projection epilogue before this kernel runs).
 //
-// Query p of a sequence sits at position t+p and sees keys 0 .. t+p. The work
-// is split over keys: chunk c holds keys [256c, 256c+256) and workgroup j of a
-// (sequence, query tile, head) visits chunks j, j+S, j+2S, ...; inside a chunk
-// wave w takes key tiles 4w .. 4w+3. Each wave keeps an online softmax in fp32,
-// waves merge in order inside the workgroup, and a second small kernel merges
-// the S workgroup partials in order. Every split boundary sits at an
-// absolute key position and masked keys contribute exact zeros, so a query's
-// result does not depend on how many other queries share the block.
+// Query p of a sequence sits at position t+p and sees keys 0 .. t+p. The keys
+// are split into S contiguous ranges of LS keys (LS and S depend only on the
+// cache capacity, never on the block); workgroup j of a (sequence, query tile,
+// head) takes range j. Inside it wave w takes the 16-key tiles w, w+4, w+8, ...
+// with the next tile's loads in flight while the current one computes; each
+// wave keeps an online softmax in fp32 and the
+// waves merge in order; a second small kernel merges the S workgroup
+// partials of each (sequence, query tile, head) in range order. Masked keys
+// contribute exact zeros, so a query's result does not depend on how many
+// other queries share the block.
 //
 // K rows are [key][Dh]; V rows are stored transposed ([Dh][key]) so both
 // MFMA operands load as contiguous vectors: S^T = K q^T puts the 4 keys a lane
@@ -52,6 +54,7 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
   const int kv_len = min(t + P, a.cap);
   const int pe = min(qt * 16 + qc, P - 1);   // padding queries repeat the last real one
   const int qpos = t + pe;
+  const int k0 = j * a.LS, k1 = min(k0 + a.LS, kv_len);   // this workgroup's keys
 
   const T* qrow = reinterpret_cast<const T*>(a.q) + (size_t)(bl * P + pe) * a.d + h * DH;
   uint4 qf[NKS];
@@ -66,69 +69,88 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int c = j; c * ATTN_CHUNK < kv_len; c += a.S) {
-    const int kw = c * ATTN_CHUNK + wave * 64;   // this wave's 4 key tiles
-    if (kw >= kv_len) continue;
-    // the loads of two tiles go out together; keys past kv_len are read (they
-    // lie inside the cache, which is a whole number of chunks) and masked
+  // this wave's tiles: key0 = k0 + 16 * (wave + 4 * i), i = 0 .. ntile-1,
+  // two tiles in flight (double buffer). Tiles past the last re-read the last
+  // tile (always inside the cache) and are skipped.
+  const int nt_all = (k1 > k0) ? (k1 - k0 + 15) / 16 : 0;
+  const int ntile = nt_all > wave ? (nt_all - wave + 3) / 4 : 0;
+  auto tile_key = [&](int i) { return k0 + 16 * (wave + 4 * min(i, max(ntile - 1, 0))); };
+  struct Buf { uint4 kf[NKS]; VQuad<T> vf[NDT]; };
+  auto issue = [&](Buf& bf, int i) {
+    const int key0 = ntile > 0 ? tile_key(i) : 0;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int kh = kw + half * 32;
-      if (kh >= kv_len) break;
-      uint4 kf[2][NKS];
-      VQuad<T> vf[2][NDT];
+    for (int ks = 0; ks < NKS; ++ks)
+      bf.kf[ks] = *reinterpret_cast<const uint4*>(K + (size_t)(key0 + qc) * DH + ks * KSTEP + g * E);
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int key0 = kh + tt * 16;
+    for (int dt = 0; dt < NDT; ++dt) bf.vf[dt].load(Vt + (size_t)(dt * 16 + qc) * a.cap + key0 + 4 * g);
+  };
+  auto compute = [&](const Buf& bf, int i) {
+    const int key0 = tile_key(i);
+    // S^T tile: rows = keys key0 .. key0+15, columns = the 16 queries
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-          kf[tt][ks] = *reinterpret_cast<const uint4*>(K + (size_t)(key0 + qc) * DH + ks * KSTEP + g * E);
+    for (int ks = 0; ks < NKS; ++ks) sc = mma_frag(bf.kf[ks], qf[ks], sc, T());
+    // lane holds scores of keys key0 + 4g + q for query qc
+    float sv[4];
+    float mt = -INFINITY;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) vf[tt][dt].load(Vt + (size_t)(dt * 16 + qc) * a.cap + key0 + 4 * g);
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int key = key0 + 4 * g + q;
+      sv[q] = (key <= qpos && key < k1) ? sc[q] * a.scale : -INFINITY;
+      mt = fmaxf(mt, sv[q]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = (m_new == -INFINITY) ? 1.f : expf(m_run - m_new);
+    float pv[4];
+    float ls = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      pv[q] = (sv[q] == -INFINITY) ? 0.f : expf(sv[q] - m_new);
+      ls += pv[q];
+    }
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+    // O^T += V^T P^T: A rows = head dims, B columns = queries, slots = keys
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      float va[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) va[q] = (key0 + 4 * g + q < k1) ? bf.vf[dt].get(q) : 0.f;
+      o[dt] = o[dt] * alpha;
+      o[dt] = mma_k4(va, pv, o[dt], T());
+    }
+  };
+  Buf b0, b1;
+  issue(b0, 0);
+  issue(b1, 1);
+  {
+    int i = 0;
+    for (; i + 3 < ntile; i += 2) {
+      compute(b0, i);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int key0 = kh + tt * 16;
-        if (key0 >= kv_len) break;
-        // S^T tile: rows = keys key0 .. key0+15, columns = the 16 queries
-        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) sc = mma_frag(kf[tt][ks], qf[ks], sc, T());
-        // lane holds scores of keys key0 + 4g + i for query qc
-        float sv[4];
-        float mt = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = key0 + 4 * g + i;
-          sv[i] = (key <= qpos) ? sc[i] * a.scale : -INFINITY;
-          mt = fmaxf(mt, sv[i]);
-        }
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = (m_new == -INFINITY) ? 1.f : expf(m_run - m_new);
-        float pv[4];
-        float ls = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[i] = (sv[i] == -INFINITY) ? 0.f : expf(sv[i] - m_new);
-          ls += pv[i];
-        }
-        ls += __shfl_xor(ls, 16);
-        ls += __shfl_xor(ls, 32);
-        l_run = l_run * alpha + ls;
-        m_run = m_new;
-        // O^T += V^T P^T: A rows = head dims, B columns = queries, slots = keys
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          float va[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) va[i] = (key0 + 4 * g + i < kv_len) ? vf[tt][dt].get(i) : 0.f;
-          o[dt] = o[dt] * alpha;
-          o[dt] = mma_k4(va, pv, o[dt], T());
-        }
-      }
+      issue(b0, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(b1, i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(b1, i + 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (ntile - i == 3) {
+      compute(b0, i);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(b0, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(b1, i + 1);
+      compute(b0, i + 2);
+    } else if (ntile - i == 2) {
+      compute(b0, i);
+      compute(b1, i + 1);
+    } else if (ntile - i == 1) {
+      compute(b0, i);
     }
   }
 
@@ -137,7 +159,7 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wo[wave][qc][dt * 16 + 4 * g + i] = o[dt][i];
+    for (int q = 0; q < 4; ++q) wo[wave][qc][dt * 16 + 4 * g + q] = o[dt][q];
   __syncthreads();
   const size_t head = (size_t)blockIdx.z * a.H + h;
   float* part = a.part + head * a.S * 16 * ROW;
@@ -158,53 +180,61 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
     }
     part[((size_t)j * 16 + q) * ROW + e] = v;
   }
+
 }
 
-// Merge the S workgroup partials of one (sequence, query tile, head) in split
-// order and write the normalised output rows. A separate launch, so the
-// partials are visible by kernel ordering alone.
+// Merge the S split partials of each (sequence, query tile, head) in range
+// order: one thread per (query, head dimension), all of a thread's partial
+// loads in flight together. A separate launch, so the partials are visible by
+// kernel ordering alone.
 template <typename T, int DH>
-__global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
-  constexpr int ROW = DH + 2;
-  __shared__ float fac[64][16];
-  __shared__ float fl[16];
-  const int h = blockIdx.x;
-  const int bl = blockIdx.y / a.QTN, qt = blockIdx.y % a.QTN;
-  const int tid = threadIdx.x, P = a.P;
-  const size_t head = (size_t)blockIdx.y * a.H + h;
-  const float* part = a.part + head * a.S * 16 * ROW;
-  if (tid < 16) {
-    const int q = tid;
-    float M = -INFINITY;
-    for (int s = 0; s < a.S; ++s) M = fmaxf(M, part[((size_t)s * 16 + q) * ROW + DH]);
-    float L = 0.f;
-    for (int s = 0; s < a.S; ++s) {
-      const float ms = part[((size_t)s * 16 + q) * ROW + DH];
-      const float f = (ms == -INFINITY) ? 0.f : expf(ms - M);
-      fac[s][q] = f;
-      L += part[((size_t)s * 16 + q) * ROW + DH + 1] * f;
+__global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a) {
+  constexpr int ROW = DH + 2, SB = 16;
+  const int e = blockIdx.x * 16 + (threadIdx.x & 15), q = threadIdx.x >> 4;
+  const int h = blockIdx.y;
+  const int bl = blockIdx.z / a.QTN, qt = blockIdx.z % a.QTN;
+  if (qt * 16 + q >= a.P) return;
+  const size_t head = (size_t)blockIdx.z * a.H + h;
+  const float* part = a.part + head * a.S * 16 * ROW + (size_t)q * ROW;   // split s at part[s * 16 * ROW]
+  float M = -INFINITY;
+  for (int s0 = 0; s0 < a.S; s0 += SB) {
+    float mv[SB];
+#pragma unroll
+    for (int u = 0; u < SB; ++u) mv[u] = part[(size_t)min(s0 + u, a.S - 1) * 16 * ROW + DH];
+#pragma unroll
+    for (int u = 0; u < SB; ++u) M = fmaxf(M, mv[u]);
+  }
+  float L = 0.f, v = 0.f;
+  for (int s0 = 0; s0 < a.S; s0 += SB) {
+    float mv[SB], lv[SB], pv[SB];
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const float* ps = part + (size_t)min(s0 + u, a.S - 1) * 16 * ROW;
+      mv[u] = ps[DH];
+      lv[u] = ps[DH + 1];
+      pv[u] = ps[e];
     }
-    fl[q] = L;
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      if (s0 + u < a.S) {
+        const float f = (mv[u] == -INFINITY) ? 0.f : expf(mv[u] - M);
+        L += lv[u] * f;
+        v += pv[u] * f;
+      }
+    }
   }
-  __syncthreads();
   T* out = reinterpret_cast<T*>(a.out);
-  for (int idx = tid; idx < 16 * DH; idx += 256) {
-    const int q = idx / DH, e = idx % DH;
-    if (qt * 16 + q >= P) continue;
-    float v = 0.f;
-    for (int s = 0; s < a.S; ++s) v += part[((size_t)s * 16 + q) * ROW + e] * fac[s][q];
-    out[(size_t)(bl * P + qt * 16 + q) * a.d + h * DH + e] = from_f<T>(v / fl[q]);
-  }
+  out[(size_t)(bl * a.P + qt * 16 + q) * a.d + h * DH + e] = from_f<T>(v / L);
 }
 
 template <typename T>
 hipError_t launch_attn(const AttnArgs& a, int n_seq, hipStream_t st) {
-  if (a.S > 64 || a.S < 1) return hipErrorInvalidValue;
-  dim3 grid(a.S, a.H, n_seq * a.QTN), block(256), cgrid(a.H, n_seq * a.QTN);
+  if (a.S > 64 || a.S < 1 || a.LS < 16 || a.LS % 16) return hipErrorInvalidValue;
+  dim3 grid(a.S, a.H, n_seq * a.QTN), block(256), mgrid(a.Dh / 16, a.H, n_seq * a.QTN);
   switch (a.Dh) {
-    case 32: attn_kernel<T, 32><<<grid, block, 0, st>>>(a); attn_combine_kernel<T, 32><<<cgrid, block, 0, st>>>(a); break;
-    case 64: attn_kernel<T, 64><<<grid, block, 0, st>>>(a); attn_combine_kernel<T, 64><<<cgrid, block, 0, st>>>(a); break;
-    case 128: attn_kernel<T, 128><<<grid, block, 0, st>>>(a); attn_combine_kernel<T, 128><<<cgrid, block, 0, st>>>(a); break;
+    case 32: attn_kernel<T, 32><<<grid, block, 0, st>>>(a); attn_merge_kernel<T, 32><<<mgrid, block, 0, st>>>(a); break;
+    case 64: attn_kernel<T, 64><<<grid, block, 0, st>>>(a); attn_merge_kernel<T, 64><<<mgrid, block, 0, st>>>(a); break;
+    case 128: attn_kernel<T, 128><<<grid, block, 0, st>>>(a); attn_merge_kernel<T, 128><<<mgrid, block, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

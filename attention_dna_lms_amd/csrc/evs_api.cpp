@@ -21,6 +21,7 @@ constexpr size_t ALIGN = 256;
 constexpr int MAX_ROWS_PER_WG = 144;   // 9 MFMA row tiles
 constexpr int GEMM_CNT = 65536;        // split-K arrival counters
 constexpr int GEMM_WAVES = 8;          // waves per GEMM workgroup (gemm_kernel default)
+constexpr int ATTN_CUS = 256;          // compute units the attention split count is sized for
 
 size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
 int next_pow2(int x) { int p = 1; while (p < x) p <<= 1; return p; }
@@ -52,7 +53,7 @@ struct evs_model {
 
 struct evs_state {
   const evs_model* m = nullptr;
-  int B = 0, max_ctx = 0, max_block = 0, cap = 0, S = 1, qtn_max = 1, M_max = 0;
+  int B = 0, max_ctx = 0, max_block = 0, cap = 0, S = 1, LS = 1, qtn_max = 1, M_max = 0;
   char* sb = nullptr;   // state buffer
   char* wb = nullptr;   // workspace
   size_t off_t = 0, off_ib = 0, off_is = 0, off_err = 0;
@@ -400,7 +401,7 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
       AttnArgs at{};
       at.q = wp<void>(s, s->w_q); at.out = wp<void>(s, s->w_o);
       at.kc = mx.kc; at.vt = mx.vt; at.kv_bs = mx.kv_bs; at.cap = s->cap;
-      at.H = p.d.n_heads; at.Dh = p.d.head_dim; at.d = d; at.P = P; at.QTN = (P + 15) / 16; at.S = s->S;
+      at.H = p.d.n_heads; at.Dh = p.d.head_dim; at.d = d; at.P = P; at.QTN = (P + 15) / 16; at.S = s->S; at.LS = s->LS;
       at.seq0 = seq0; at.t = t; at.scale = 1.0f / std::sqrt((float)p.d.head_dim);
       at.part = wp<float>(s, s->w_apart); at.cnt = wp<int>(s, s->w_acnt);
       if ((size_t)nseq * at.QTN * at.H * at.S * 16 * (at.Dh + 2) > s->apart_floats) return EVS_E_RANGE;
@@ -526,7 +527,19 @@ static evs_status state_setup(const evs_model* m, int32_t batch, int32_t max_ctx
   s->max_ctx = max_ctx;
   s->max_block = max_block;
   s->cap = (int)align_up((size_t)max_ctx, ATTN_CHUNK);
-  s->S = std::min(64, std::max(1, s->cap / (2 * ATTN_CHUNK)));
+  // attention splits: contiguous ranges of LS keys (a multiple of 64, so each
+  // of a workgroup's 4 waves gets whole 16-key tiles), fixed by the state's
+  // capacity, batch and head count (never by the block): about two
+  // workgroups per CU for a full batch of one query tile, so the launch runs
+  // in a single round
+  {
+    const int heads = std::max(1, m->max_heads);
+    int s0 = (2 * ATTN_CUS) / std::max(1, heads * batch);
+    s0 = std::min(std::min(64, s0), s->cap / 64);
+    s0 = std::max(1, s0);
+    s->LS = (int)align_up((size_t)((s->cap + s0 - 1) / s0), 64);
+    s->S = (s->cap + s->LS - 1) / s->LS;
+  }
   s->M_max = batch * max_block;
   layout_state(s);
   return EVS_OK;

@@ -108,13 +108,14 @@ struct AttnArgs {
   const void* vt;        // [B, H, Dh, cap]
   long long kv_bs;       // per-sequence stride (elements) of kc / vt
   int cap, H, Dh, d, P, QTN, S, seq0;
+  int LS;                // keys per split range (a multiple of 16); S * LS >= cap
   const int* t;
   float scale;
-  float* part;           // [B_call, QTN, H, S, 16, Dh + 2]
-  int* cnt;              // unused (kept for layout stability)
+  float* part;           // [B_call, QTN, H, S, 16, Dh + 2] split partials
+  int* cnt;              // unused
 };
 
-constexpr int ATTN_CHUNK = 256;   // keys per chunk (4 waves x 4 tiles of 16)
+constexpr int ATTN_CHUNK = 256;   // the KV capacity is a multiple of this many keys
 constexpr int IIR_CH = 16;        // positions per chunk of the IIR mixer epilogue
 
 struct VerifyArgs {
