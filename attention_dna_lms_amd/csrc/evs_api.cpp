@@ -22,6 +22,7 @@ constexpr int MAX_ROWS_PER_WG = 144;   // 9 MFMA row tiles
 constexpr int GEMM_CNT = 65536;        // split-K arrival counters
 constexpr int GEMM_WAVES = 8;          // waves per GEMM workgroup (gemm_kernel default)
 constexpr int ATTN_CUS = 256;          // compute units the attention split count is sized for
+constexpr int SK_LDS_LIMIT = 156 * 1024;   // dynamic LDS of a balanced launch (MI355X: 160 KB per CU, less static)
 
 size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
 int next_pow2(int x) { int p = 1; while (p < x) p <<= 1; return p; }
@@ -193,7 +194,14 @@ bool use_sk(const Mat& mat, int ksteps, int amode, int epi, const Slicing& sl) {
   return per_wave <= ksteps && total / SK_WGS >= ksteps && max_groups <= 4;
 }
 size_t sk_part_floats(const Mat& mat) { return (size_t)mat.n_groups * 2 * mat.NT * 256; }
-size_t sk_lds(const Mat& mat) { return 4 * (16 + (size_t)8 * 2 * mat.NT * 256 + (size_t)mat.NT * 256); }
+// LDS of a balanced launch: row scales, then the finish region (8 waves x 2
+// sides of partial tiles + the epilogue tile); bf16 models first stage the 16
+// normalised input rows (row stride K + 8) in the same region.
+size_t sk_lds(const Mat& mat, int es) {
+  const size_t finish = 4 * ((size_t)8 * 2 * mat.NT * 256 + (size_t)mat.NT * 256);
+  const size_t staged = es == 2 ? (size_t)16 * (mat.K + 8) * 2 : 0;
+  return 4 * 16 + std::max(finish, staged);
+}
 
 int gemm_bufs(int MT, int NT) { return (4 * NT * MT <= 48) ? 4 : ((2 * NT * MT <= 48) ? 2 : 1); }
 
@@ -339,7 +347,8 @@ evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int 
                        (double)a.M * mat.rows_valid * (epi == E_RESID ? 8 : m->es);
   if (use_sk(mat, a.ksteps, amode, epi, sl)) {
     if (sk_part_floats(mat) > s->part_floats || (size_t)mat.n_groups > (size_t)GEMM_CNT) return EVS_E_RANGE;
-    const size_t lds = sk_lds(mat);
+    const size_t lds = sk_lds(mat, m->es);
+    if (lds > (size_t)SK_LDS_LIMIT) return EVS_E_UNSUPPORTED;
     return hip_ok(timed(s, EVS_KC_GEMM, bytes, st, [&] { return launch_gemm_sk<T>(mat.NT, amode, epi, a, lds, st); }));
   }
   const size_t lds = gemm_lds(sl.MT, mat.NT, scratch_floats);
