@@ -56,10 +56,11 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
   const int qpos = t + pe;
   const int k0 = j * a.LS, k1 = min(k0 + a.LS, kv_len);   // this workgroup's keys
 
-  const T* qrow = reinterpret_cast<const T*>(a.q) + (size_t)(bl * P + pe) * a.d + h * DH;
+  const T* qm = reinterpret_cast<const T*>(a.q);
   uint4 qf[NKS];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const uint4*>(qrow + ks * KSTEP + g * E);
+  for (int ks = 0; ks < NKS; ++ks)
+    qf[ks] = *reinterpret_cast<const uint4*>(qm + act_off<E>(bl * P + pe, h * DH + ks * KSTEP + g * E, a.d));
 
   const T* K = reinterpret_cast<const T*>(a.kc) + (size_t)b * a.kv_bs + (size_t)h * a.cap * DH;
   const T* Vt = reinterpret_cast<const T*>(a.vt) + (size_t)b * a.kv_bs + (size_t)h * DH * a.cap;
@@ -224,7 +225,7 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a) {
     }
   }
   T* out = reinterpret_cast<T*>(a.out);
-  out[(size_t)(bl * a.P + qt * 16 + q) * a.d + h * DH + e] = from_f<T>(v / L);
+  out[act_off<St<T>::E>(bl * a.P + qt * 16 + q, h * DH + e, a.d)] = from_f<T>(v / L);
 }
 
 template <typename T>

@@ -22,6 +22,7 @@ constexpr int MAX_ROWS_PER_WG = 144;   // 9 MFMA row tiles
 constexpr int GEMM_CNT = 65536;        // split-K arrival counters
 constexpr int GEMM_WAVES = 8;          // waves per GEMM workgroup (gemm_kernel default)
 constexpr int ATTN_CUS = 256;          // compute units the attention split count is sized for
+constexpr bool kUseBalancedGateUp = false;   // stream-K gate/up launch (kept selectable)
 constexpr int SK_LDS_LIMIT = 156 * 1024;   // dynamic LDS of a balanced launch (MI355X: 160 KB per CU, less static)
 
 size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
@@ -184,6 +185,9 @@ Slicing slicing(int nseq, int P) {
 // each wave's run of k-steps within one group boundary, each group within two
 // workgroups.
 bool use_sk(const Mat& mat, int ksteps, int amode, int epi, const Slicing& sl) {
+  // With the activations in operand order the per-group launch is faster at
+  // the 7B shape (three partial rounds beat the cross-workgroup finish).
+  if (!kUseBalancedGateUp) return false;
   if (!(mat.NT == 2 && amode == A_NORM && epi == E_GELU)) return false;
   if (sl.slices != 1 || sl.MT != 1) return false;
   if (mat.n_groups <= SK_WGS || mat.n_groups % SK_WGS == 0) return false;
@@ -242,11 +246,12 @@ void layout_state(evs_state* s) {
   // workspace
   const int M = s->M_max;
   off = 0;
-  s->w_x = take((size_t)M * d * 4);
+  const size_t M16 = align_up((size_t)M, 16);   // activations are stored in whole 16-row tiles
+  s->w_x = take(M16 * d * 4);
   s->w_nrm = take((size_t)(d / 16) * M * 4);
-  s->w_o = take((size_t)M * d * es);
-  s->w_q = take((size_t)M * d * es);
-  s->w_h = take((size_t)M * std::max(m->max_dff, 16) * es);
+  s->w_o = take(M16 * d * es);
+  s->w_q = take(M16 * d * es);
+  s->w_h = take(M16 * std::max(m->max_dff, 32) * es);
   s->w_logit = take((size_t)s->max_block * m->desc.vocab * es);
   // split-K partials: the largest requirement over every block size and batch
   size_t pf = 0;

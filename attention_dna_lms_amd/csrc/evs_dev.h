@@ -28,6 +28,21 @@ template <> __device__ __forceinline__ float from_f<float>(float x) { return x; 
 // value as held in storage type T (round-to-nearest-even for bf16)
 template <typename T> __device__ __forceinline__ float rnd(float x) { return to_f(from_f<T>(x)); }
 
+// Layout of the activations inside the forward (the residual stream x, the
+// mixer outputs, the MLP hidden rows, the attention queries): rows in tiles of
+// 16, each tile split into k-steps of 4E columns, each step stored in MFMA
+// operand order [column group of E][row][E]. The operand fragment of row tile
+// t and k-step s is then one contiguous run of 64 lanes x E elements, lane l
+// at offset l * E (rows of a tile past the valid count are never written and
+// only feed discarded output columns). E is the storage type's per-lane
+// element count (8 for bf16 models, 4 for fp32), also for the fp32 residual
+// stream. K is the matrix's column count (a multiple of 4E).
+template <int E>
+__host__ __device__ __forceinline__ size_t act_off(int m, int c, int K) {
+  constexpr int KS = 4 * E;
+  return ((size_t)(m >> 4) * (K / KS) + c / KS) * (16 * KS) + (size_t)((c % KS) / E) * (16 * E) + (m & 15) * E + (c % E);
+}
+
 // D += A * B for one 16x16 tile. Fragments: lane l holds row (l % 16) of A and
 // column (l % 16) of B over the same reduction slots; D: lane l holds rows
 // 4*(l/16) + i (i = 0..3) of column l % 16.

@@ -45,14 +45,14 @@ template <typename T, int AMODE> struct AFrag;
 template <typename T> struct AFrag<T, A_ACT> {            // storage-type rows
   uint4 v;
   __device__ __forceinline__ void load(const GemmArgs& a, size_t m, int kofs) {
-    v = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.A) + m * a.lda + kofs);
+    v = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.A) + act_off<St<T>::E>((int)m, kofs, a.lda));
   }
   __device__ __forceinline__ uint4 get(float) const { return v; }
 };
 template <> struct AFrag<bf16, A_NORM> {                  // fp32 rows, RMSNorm -> bf16
   float4 lo, hi;
   __device__ __forceinline__ void load(const GemmArgs& a, size_t m, int kofs) {
-    const float* xr = reinterpret_cast<const float*>(a.A) + m * a.lda + kofs;
+    const float* xr = reinterpret_cast<const float*>(a.A) + act_off<8>((int)m, kofs, a.lda);
     lo = *reinterpret_cast<const float4*>(xr);
     hi = *reinterpret_cast<const float4*>(xr + 4);
   }
@@ -66,7 +66,7 @@ template <> struct AFrag<bf16, A_NORM> {                  // fp32 rows, RMSNorm 
 template <> struct AFrag<float, A_NORM> {                 // fp32 rows, RMSNorm -> fp32
   float4 v;
   __device__ __forceinline__ void load(const GemmArgs& a, size_t m, int kofs) {
-    v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.A) + m * a.lda + kofs);
+    v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.A) + act_off<4>((int)m, kofs, a.lda));
   }
   __device__ __forceinline__ uint4 get(float r) const {
     return __builtin_bit_cast(uint4, make_float4(v.x * r, v.y * r, v.z * r, v.w * r));
@@ -98,9 +98,9 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, EpiPre& pf, int 
     static_assert(NT * MR <= 512, "one residual row segment per thread");
     const int nt = tid / MR, m = tid % MR;
     if (tid < NT * MR && m < rows) {
-      const float4* xr = reinterpret_cast<const float4*>(a.x + (size_t)(row0 + m) * a.ldx + (g * NT + nt) * 16);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) pf.xr[q] = xr[q];
+      for (int q = 0; q < 4; ++q)
+        pf.xr[q] = *reinterpret_cast<const float4*>(a.x + act_off<St<T>::E>(row0 + m, (g * NT + nt) * 16 + 4 * q, a.ldx));
     }
   } else if constexpr (EPI == E_MIXER) {
     const MixArgs& x = a.mix;
@@ -149,7 +149,6 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
     const int nt = tid / MR, m = tid % MR;
     if (tid < NT * MR && m < rows) {
       const int col0 = (g * NT + nt) * 16;
-      float* xr = a.x + (size_t)(row0 + m) * a.ldx + col0;
       const float* er = ep + (nt * MR + m) * 16;
       float v[16];
 #pragma unroll
@@ -164,7 +163,8 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        reinterpret_cast<float4*>(xr)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        *reinterpret_cast<float4*>(a.x + act_off<St<T>::E>(row0 + m, col0 + 4 * q, a.ldx)) =
+            make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
       a.nrm_out[(size_t)(g * NT + nt) * a.nrm_ld + row0 + m] = ss;
     }
   } else if constexpr (EPI == E_GELU) {
@@ -174,7 +174,7 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
       if (m >= rows) continue;
       const float gv = rnd<T>(ep[idx]);
       const float uv = rnd<T>(ep[MR * 16 + idx]);
-      out[(size_t)(row0 + m) * a.ldo + g * 16 + n] = from_f<T>(gelu_f(gv) * uv);
+      out[act_off<St<T>::E>(row0 + m, g * 16 + n, a.ldo)] = from_f<T>(gelu_f(gv) * uv);
     }
   } else {  // E_MIXER: ep[0] = q, ep[1] = k, ep[2] = v for channels g*16 .. g*16+15
     const MixArgs& x = a.mix;
@@ -194,7 +194,7 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
         const int b = sbase + m / P, p = m % P;
         const int pos = x.t[b] + p;
         const int ch = ch0 + c, h = ch / x.Dh, dh = ch % x.Dh;
-        out[(size_t)(row0 + m) * a.ldo + ch] = from_f<T>(eq[idx]);
+        out[act_off<St<T>::E>(row0 + m, ch, a.ldo)] = from_f<T>(eq[idx]);
         if (pos < x.cap) {
           kc[(size_t)b * x.kv_bs + ((size_t)h * x.cap + pos) * x.Dh + dh] = from_f<T>(ek[idx]);
           vt[(size_t)b * x.kv_bs + ((size_t)h * x.Dh + dh) * x.cap + pos] = from_f<T>(ev[idx]);
@@ -257,7 +257,7 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
             for (int q = 0; q < 16; ++q) y = fmaf(tv[q], hv[q], y);
           }
           for (; jj < L; ++jj) y = fmaf(tc[jj], hc[-16 * jj], y);
-          out[(size_t)(row0 + m) * a.ldo + ch0 + c] = from_f<T>(rnd<T>(eq[m * 16 + c]) * y);
+          out[act_off<St<T>::E>(row0 + m, ch0 + c, a.ldo)] = from_f<T>(rnd<T>(eq[m * 16 + c]) * y);
         }
         __syncthreads();
       }
@@ -318,7 +318,7 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
             for (int k = 0; k < 16; ++k) r[k] = k < x.N ? rp[k] * sp[k] : 0.f;
             const float tot = (((r[0] + r[8]) + (r[4] + r[12])) + ((r[2] + r[10]) + (r[6] + r[14]))) +
                               (((r[1] + r[9]) + (r[5] + r[13])) + ((r[3] + r[11]) + (r[7] + r[15])));
-            out[(size_t)(row0 + m) * a.ldo + ch0 + cc] = from_f<T>(rnd<T>(eq[m * 16 + cc]) * tot);
+            out[act_off<St<T>::E>(row0 + m, ch0 + cc, a.ldo)] = from_f<T>(rnd<T>(eq[m * 16 + cc]) * tot);
           }
           __syncthreads();
         }

@@ -366,7 +366,7 @@ __global__ void __launch_bounds__(512) gemm_sk_staged_kernel(GemmArgs a) {
     for (int q = 0; q < XB; ++q) {
       const int idx = min((pass * XB + q) * 512 + tid, n8 - 1);
       const int rr = idx / (K / 8), kk = (idx % (K / 8)) * 8;
-      const float* xr = X + (size_t)rr * a.lda + kk;
+      const float* xr = X + act_off<8>(rr, kk, a.lda);
       xb[q][0] = *reinterpret_cast<const float4*>(xr);
       xb[q][1] = *reinterpret_cast<const float4*>(xr + 4);
     }

@@ -25,13 +25,16 @@ __global__ void embed_kernel(const int* __restrict__ tokens, const T* __restrict
   }
   if (tile == 0 && m % P == 0 && t[seq0 + m / P] + P > max_ctx) atomicOr(err, 2);
   const T* e = E + (size_t)tok * d + tile * 16;
-  float* xr = x + (size_t)m * d + tile * 16;
   float ss = 0.f;
 #pragma unroll
-  for (int n = 0; n < 16; ++n) {
-    const float v = to_f(e[n]);
-    xr[n] = v;
-    ss = fmaf(v, v, ss);
+  for (int q = 0; q < 4; ++q) {
+    float* xr = x + act_off<St<T>::E>(m, tile * 16 + 4 * q, d);   // the forward's activation layout
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const float v = to_f(e[4 * q + n]);
+      xr[n] = v;
+      ss = fmaf(v, v, ss);
+    }
   }
   nrm[(size_t)tile * nrm_ld + m] = ss;
 }
