@@ -328,8 +328,8 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
 }
 
 // ---------------------------------------------------------------- kernel
-template <typename T, int MT, int NT, int AMODE, int EPI, int WV = 8, int CHO = 0>
-__global__ void __launch_bounds__(WV * 64) gemm_kernel(GemmArgs a) {
+template <typename T, int MT, int NT, int AMODE, int EPI, int WV = 8, int CHO = 0, int MINB = 1>
+__global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   static_assert(EPI != E_MIXER || WV == 8, "the mixer epilogue assumes 512 threads");
   using C = GemmCfg<MT, NT, WV>;
   constexpr int E = St<T>::E, KSTEP = St<T>::KSTEP, RS = C::RS;
@@ -337,8 +337,11 @@ __global__ void __launch_bounds__(WV * 64) gemm_kernel(GemmArgs a) {
   // activation fragments (8 registers each for fp32 rows feeding bf16, else 4)
   // per step stays within ~64 registers, the two chunks in flight within ~128
   constexpr int AREG = (AMODE == A_NORM && sizeof(T) == 2) ? 2 : 1;
+  // (measured at the 7B shapes: 4 steps for single-tile projections, 2 for
+  // the gate/up pairs, the register bound for the in-projection triples)
   constexpr int PER = 16 / (NT + AREG * MT);
-  constexpr int CH = CHO ? CHO : PER >= 8 ? 8 : PER >= 1 ? PER : 1;
+  constexpr int CAP = NT == 1 ? 4 : NT == 2 ? 2 : 8;
+  constexpr int CH = CHO ? CHO : PER < 1 ? 1 : PER < CAP ? PER : CAP;
   extern __shared__ float lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform values live in scalar registers, so every guard below is a
