@@ -14,14 +14,16 @@
 // contribute exact zeros, so a query's result does not depend on how many
 // other queries share the block.
 //
-// K rows are [key][Dh]; V rows are stored transposed ([Dh][key]) so both
-// MFMA operands load as contiguous vectors: S^T = K q^T puts the 4 keys a lane
-// needs for the P V product in its own registers.
+// K rows are [key][Dh]; V is stored in blocks of 16 keys, each block
+// dimension-major ([Dh][16 keys], 4 KB contiguous for bf16 at Dh = 128), so
+// both MFMA operands load as contiguous runs: S^T = K q^T puts the 4 keys a
+// lane needs for the P V product in its own registers, and a tile's values
+// are one block.
 #include "evs_dev.h"
 
 namespace evs {
 
-// four consecutive keys of one transposed value row
+// four consecutive keys of one head dimension inside a value block
 template <typename T> struct VQuad;
 template <> struct VQuad<bf16> {
   uint2 v;
@@ -83,7 +85,7 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
     for (int ks = 0; ks < NKS; ++ks)
       bf.kf[ks] = *reinterpret_cast<const uint4*>(K + (size_t)(key0 + qc) * DH + ks * KSTEP + g * E);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) bf.vf[dt].load(Vt + (size_t)(dt * 16 + qc) * a.cap + key0 + 4 * g);
+    for (int dt = 0; dt < NDT; ++dt) bf.vf[dt].load(Vt + (size_t)key0 * DH + (dt * 16 + qc) * 16 + 4 * g);
   };
   auto compute = [&](const Buf& bf, int i) {
     const int key0 = tile_key(i);

@@ -629,7 +629,7 @@ evs_status evs_state_tensor(const evs_state* s, int32_t what, int32_t block, evs
       return EVS_OK;
     case EVS_ST_VT:
       if (!need_block(EVS_ATTN)) return EVS_E_INVALID;
-      set(s->vt[block], dt, {B, m->blocks[block].n_heads, m->blocks[block].head_dim, s->cap});
+      set(s->vt[block], dt, {B, m->blocks[block].n_heads, s->cap / 16, m->blocks[block].head_dim, 16});
       return EVS_OK;
     default: return EVS_E_INVALID;
   }

@@ -120,7 +120,7 @@ struct AttnArgs {
   const void* q;         // [M, d] storage type
   void* out;             // [M, d]
   const void* kc;        // [B, H, cap, Dh]
-  const void* vt;        // [B, H, Dh, cap]
+  const void* vt;        // [B, H, cap/16, Dh, 16]: 16-key blocks, dimension-major inside
   long long kv_bs;       // per-sequence stride (elements) of kc / vt
   int cap, H, Dh, d, P, QTN, S, seq0;
   int LS;                // keys per split range (a multiple of 16); S * LS >= cap

@@ -197,7 +197,8 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
         out[act_off<St<T>::E>(row0 + m, ch, a.ldo)] = from_f<T>(eq[idx]);
         if (pos < x.cap) {
           kc[(size_t)b * x.kv_bs + ((size_t)h * x.cap + pos) * x.Dh + dh] = from_f<T>(ek[idx]);
-          vt[(size_t)b * x.kv_bs + ((size_t)h * x.Dh + dh) * x.cap + pos] = from_f<T>(ev[idx]);
+          vt[(size_t)b * x.kv_bs + (size_t)h * x.Dh * x.cap + ((size_t)(pos >> 4) * x.Dh + dh) * 16 + (pos & 15)] =
+              from_f<T>(ev[idx]);
         } else {
           atomicOr(x.err, 2);
         }

@@ -168,6 +168,21 @@ __device__ __forceinline__ float load_target(const VerifyArgs& a, size_t off) {
   return reinterpret_cast<const float*>(a.target)[off];
 }
 
+template <typename S>
+__device__ __forceinline__ void stage_rows(const S* src, int n, bool logits, float* dst) {
+  const int tid = threadIdx.x;
+  for (int i0 = 0; i0 < n; i0 += 256 * 16) {
+    float zv[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) zv[q] = to_f(src[min(i0 + q * 256 + tid, n - 1)]);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int i = i0 + q * 256 + tid;
+      if (i < n) dst[i] = isnan(zv[q]) ? (logits ? -INFINITY : 0.f) : zv[q];
+    }
+  }
+}
+
 __device__ int icdf_seq(const float* w, int V, float u, int fallback) {
   float c = 0.f;
   int last = -1;
@@ -181,7 +196,8 @@ __device__ int icdf_seq(const float* w, int V, float u, int fallback) {
 
 __global__ void __launch_bounds__(256) verify_kernel(VerifyArgs a) {
   extern __shared__ float sm[];
-  __shared__ int amax_s[64];
+  __shared__ int amax_s[64], draft_s[64];
+  __shared__ float qx_s[64], u_s[64];
   __shared__ int rej_s, nacc_s, next_s;
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int gamma = a.gamma, P = gamma + 1, V = a.V;
@@ -189,21 +205,43 @@ __global__ void __launch_bounds__(256) verify_kernel(VerifyArgs a) {
   float* prob = sm;            // [P][V]
   float* w = sm + (size_t)P * V;  // [V]
 
-  // phase 1: one wave per position, positions in rounds of 4 (uniform barriers)
+  // phase 0: the sequence's [P][V] target values into LDS, all threads, 16
+  // loads in flight per thread (NaN logits read as -inf, NaN probabilities as 0)
+  if (a.kind == 1)
+    stage_rows(reinterpret_cast<const bf16*>(a.target) + (size_t)b * P * V, P * V, logits, prob);
+  else
+    stage_rows(reinterpret_cast<const float*>(a.target) + (size_t)b * P * V, P * V, logits, prob);
+  // the draft tokens (and in sampling mode q(x) and u at each drafted position),
+  // one thread per position, so the accept scan reads only LDS
+  if (tid < gamma) {
+    int x = a.draft[(size_t)b * gamma + tid];
+    if (x < 0 || x >= V) {
+      if (a.err) atomicOr(a.err, 8);
+      x = x < 0 ? 0 : V - 1;
+    }
+    draft_s[tid] = x;
+    if (!a.greedy) {
+      const float qx = a.q[((size_t)b * gamma + tid) * V + x];
+      qx_s[tid] = isnan(qx) ? 0.f : qx;
+      u_s[tid] = a.u[(size_t)b * P + tid];
+    }
+  }
+  __syncthreads();
+
+  // phase 1: one wave per position, positions in rounds of 4 (the barriers,
+  // needed only to normalise sampled rows, are uniform across the block)
   __shared__ float ssum_s[4];
+  const bool any_soft = !a.greedy && logits;
   for (int i0 = 0; i0 < P; i0 += 4) {
     const int i = i0 + wave;
     const bool act = i < P;
     float* pr = prob + (size_t)(act ? i : 0) * V;
     const bool soft = act && !a.greedy && logits;
     if (act) {
-      const size_t roff = ((size_t)b * P + i) * V;
       float bv = -INFINITY;
       int bi = 0;
       for (int y = lane; y < V; y += 64) {
-        float z = load_target(a, roff + y);
-        if (isnan(z)) z = logits ? -INFINITY : 0.f;
-        pr[y] = z;
+        const float z = pr[y];
         if (ord_gt(z, y, bv, bi)) { bv = z; bi = y; }
       }
       wave_argmax(bv, bi);
@@ -244,6 +282,7 @@ __global__ void __launch_bounds__(256) verify_kernel(VerifyArgs a) {
         pr[y] = keep ? (float)exp((double)(z - m)) : 0.f;
       }
     }
+    if (!any_soft) continue;
     __syncthreads();
     if (soft && lane == 0) {
       float S = 0.f;
@@ -257,22 +296,18 @@ __global__ void __launch_bounds__(256) verify_kernel(VerifyArgs a) {
     }
     __syncthreads();
   }
+  __syncthreads();
 
   if (tid == 0) {
     int n_acc = gamma, nxt = -1, rej = -1;
     for (int i = 0; i < gamma; ++i) {
-      int x = a.draft[(size_t)b * gamma + i];
-      if (x < 0 || x >= V) {
-        if (a.err) atomicOr(a.err, 8);
-        x = x < 0 ? 0 : V - 1;
-      }
+      const int x = draft_s[i];
       if (a.greedy) {
         if (x != amax_s[i]) { n_acc = i; nxt = amax_s[i]; break; }
       } else {
         const float px = prob[(size_t)i * V + x];
-        float qx = a.q[((size_t)b * gamma + i) * V + x];
-        if (isnan(qx)) qx = 0.f;
-        const bool ok = qx > 0.f ? (a.u[(size_t)b * P + i] < px / qx) : (px > 0.f);
+        const float qx = qx_s[i];
+        const bool ok = qx > 0.f ? (u_s[i] < px / qx) : (px > 0.f);
         if (!ok) { n_acc = i; rej = i; break; }
       }
     }

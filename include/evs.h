@@ -100,7 +100,9 @@ enum {
   EVS_ST_IIR = 5,       /* f32 [B, 2, max_block, d, N] (IIR block): the state after
                            each position of a block, double-buffered */
   EVS_ST_K = 6,         /* storage [B, H, cap, Dh] (ATTN block): key rows */
-  EVS_ST_VT = 7,        /* storage [B, H, Dh, cap] (ATTN block): value rows, transposed */
+  EVS_ST_VT = 7,        /* storage [B, H, cap/16, Dh, 16] (ATTN block): value rows in
+                           blocks of 16 positions, each block dimension-major:
+                           [b, h, pos/16, e, pos%16] holds V[pos][h][e] */
   EVS_ST_ERROR = 8      /* i32 [1]: sticky error word (EVS_ERR_* bits) */
 };
 

@@ -72,7 +72,8 @@ def snapshot(state, cfg, b=0):
             out["iir"][i] = np.zeros(st.shape[-2:]) if isl < 0 else st[ib, isl].double().cpu().numpy()
         elif blk.kind == "attn":
             out["k"][i] = state.tensor(evs.EVS_ST_K, i)[b, :, :t].permute(1, 0, 2).double().cpu().numpy()
-            out["v"][i] = state.tensor(evs.EVS_ST_VT, i)[b, :, :, :t].permute(2, 0, 1).double().cpu().numpy()
+            vb = state.tensor(evs.EVS_ST_VT, i)[b]                  # [H, cap/16, Dh, 16]
+            out["v"][i] = vb.permute(1, 3, 0, 2).reshape(-1, vb.shape[0], vb.shape[2])[:t].double().cpu().numpy()
     return out
 
 
@@ -99,7 +100,11 @@ def import_state(state, cfg, synth, t, b=0):
             state.tensor(evs.EVS_ST_IIR, i)[b, 0, 0] = synth[i]["s"].to(DEV)
         elif blk.kind == "attn":
             state.tensor(evs.EVS_ST_K, i)[b, :, :t] = synth[i]["k"].to(DEV).permute(1, 0, 2)
-            state.tensor(evs.EVS_ST_VT, i)[b, :, :, :t] = synth[i]["v"].to(DEV).permute(1, 2, 0)
+            vb = state.tensor(evs.EVS_ST_VT, i)[b]                  # [H, cap/16, Dh, 16]
+            nb = (t + 15) // 16
+            v = torch.zeros(nb * 16, vb.shape[0], vb.shape[2], dtype=vb.dtype, device=DEV)
+            v[:t] = synth[i]["v"].to(DEV)
+            vb[:, :nb] = v.reshape(nb, 16, vb.shape[0], vb.shape[2]).permute(2, 0, 3, 1)
     torch.cuda.synchronize()
 
 
