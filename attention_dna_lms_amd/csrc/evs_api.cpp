@@ -19,11 +19,8 @@ namespace {
 
 constexpr size_t ALIGN = 256;
 constexpr int MAX_ROWS_PER_WG = 144;   // 9 MFMA row tiles
-constexpr int GEMM_CNT = 65536;        // split-K arrival counters
 constexpr int GEMM_WAVES = 8;          // waves per GEMM workgroup (gemm_kernel default)
 constexpr int ATTN_CUS = 256;          // compute units the attention split count is sized for
-constexpr bool kUseBalancedGateUp = false;   // stream-K gate/up launch (kept selectable)
-constexpr int SK_LDS_LIMIT = 156 * 1024;   // dynamic LDS of a balanced launch (MI355X: 160 KB per CU, less static)
 
 size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
 int next_pow2(int x) { int p = 1; while (p < x) p <<= 1; return p; }
@@ -63,19 +60,25 @@ struct evs_state {
   std::vector<int> R;
   size_t state_total = 0;
   // workspace
-  size_t w_x = 0, w_nrm = 0, w_o = 0, w_q = 0, w_h = 0, w_logit = 0, w_part = 0, w_cnt = 0, w_apart = 0,
-         w_acnt = 0, ws_total = 0;
-  size_t part_floats = 0, apart_floats = 0, acnt_n = 0;
+  size_t w_x = 0, w_nrm = 0, w_o = 0, w_q = 0, w_h = 0, w_logit = 0, w_apart = 0, ws_total = 0;
+  size_t apart_floats = 0;
   bool pending = false;
   int pending_P = 0;
-  // per-kernel timing (measurement aid): event pairs around launches
-  struct Rec { hipEvent_t a, b; int kc; double bytes; };
+  // per-kernel timing (measurement aid): one event pair around each run of
+  // consecutive launches of one kernel class
+  struct Rec { hipEvent_t a, b; int kc; double bytes; long long n; };
   bool timing = false;
   long long timing_ctx = 0;   // caller-supplied context length used for attention byte counts
   std::vector<Rec> recs;
   std::vector<hipEvent_t> pool;
+  hipEvent_t span_a = nullptr;   // open run: start event, class, launches, bytes, stream
+  int span_kc = 0;
+  long long span_n = 0;
+  double span_bytes = 0;
+  hipStream_t span_st = nullptr;
   ~evs_state() {
     for (auto& r : recs) { pool.push_back(r.a); pool.push_back(r.b); }
+    if (span_a) pool.push_back(span_a);
     for (auto e : pool) (void)hipEventDestroy(e);
   }
 };
@@ -160,14 +163,6 @@ std::vector<Canon> canon_list(const evs_model_desc* d) {
   return v;
 }
 
-// workgroup k-split so that a launch has >= ~256 workgroups while each keeps
-// >= 8 k-steps
-// (k-splits meet through device-scope fences, whose L2 write-back costs more
-// than the parallelism gains at these sizes, so every GEMM runs unsplit)
-int choose_ks(int n_groups, int ksteps, int slices) {
-  (void)n_groups; (void)ksteps; (void)slices;
-  return 1;
-}
 
 struct Slicing { int rows_per_slice, slices, MT; };
 Slicing slicing(int nseq, int P) {
@@ -180,32 +175,6 @@ Slicing slicing(int nseq, int P) {
   return s;
 }
 
-// The balanced (stream-K) launch serves the gated-MLP gate/up projection when
-// its column groups do not divide evenly over the workgroups: one 16-row tile,
-// each wave's run of k-steps within one group boundary, each group within two
-// workgroups.
-bool use_sk(const Mat& mat, int ksteps, int amode, int epi, const Slicing& sl) {
-  // With the activations in operand order the per-group launch is faster at
-  // the 7B shape (three partial rounds beat the cross-workgroup finish).
-  if (!kUseBalancedGateUp) return false;
-  if (!(mat.NT == 2 && amode == A_NORM && epi == E_GELU)) return false;
-  if (sl.slices != 1 || sl.MT != 1) return false;
-  if (mat.n_groups <= SK_WGS || mat.n_groups % SK_WGS == 0) return false;
-  const long long total = (long long)mat.n_groups * ksteps;
-  const long long per_wave = (total + SK_WGS * 8 - 1) / (SK_WGS * 8);
-  const long long per_wg = (total + SK_WGS - 1) / SK_WGS;
-  const long long max_groups = (ksteps - 1 + per_wg - 1) / ksteps + 1;   // groups one workgroup touches
-  return per_wave <= ksteps && total / SK_WGS >= ksteps && max_groups <= 4;
-}
-size_t sk_part_floats(const Mat& mat) { return (size_t)mat.n_groups * 2 * mat.NT * 256; }
-// LDS of a balanced launch: row scales, then the finish region (8 waves x 2
-// sides of partial tiles + the epilogue tile); bf16 models first stage the 16
-// normalised input rows (row stride K + 8) in the same region.
-size_t sk_lds(const Mat& mat, int es) {
-  const size_t finish = 4 * ((size_t)8 * 2 * mat.NT * 256 + (size_t)mat.NT * 256);
-  const size_t staged = es == 2 ? (size_t)16 * (mat.K + 8) * 2 : 0;
-  return 4 * 16 + std::max(finish, staged);
-}
 
 int gemm_bufs(int MT, int NT) { return (4 * NT * MT <= 48) ? 4 : ((2 * NT * MT <= 48) ? 2 : 1); }
 
@@ -253,33 +222,10 @@ void layout_state(evs_state* s) {
   s->w_q = take(M16 * d * es);
   s->w_h = take(M16 * std::max(m->max_dff, 32) * es);
   s->w_logit = take((size_t)s->max_block * m->desc.vocab * es);
-  // split-K partials: the largest requirement over every block size and batch
-  size_t pf = 0;
-  for (int P = 1; P <= s->max_block; ++P) {
-    for (int nseq : {1, B}) {
-      const Slicing sl = slicing(nseq, P);
-      auto acc = [&](const Mat& mm) {
-        const int ks = choose_ks(mm.n_groups, mm.K / m->kstep, sl.slices);
-        if (ks > 1) pf = std::max(pf, (size_t)sl.slices * mm.n_groups * ks * mm.NT * sl.MT * 256);
-      };
-      for (const auto& p : m->plan) {
-        if (p.d.kind == EVS_MLP && use_sk(p.w_gu, p.w_gu.K / m->kstep, A_NORM, E_GELU, sl))
-          pf = std::max(pf, sk_part_floats(p.w_gu));
-        if (p.d.kind == EVS_MLP) { acc(p.w_gu); acc(p.w_down); }
-        else { acc(p.w_in); acc(p.w_out); }
-      }
-      acc(m->lm);
-    }
-  }
-  s->part_floats = std::max<size_t>(pf, 256);
-  s->w_part = take(s->part_floats * 4);
-  s->w_cnt = take((size_t)GEMM_CNT * 4);
   const int H = std::max(m->max_heads, 1), DHm = std::max(m->max_dh, 32);
   s->qtn_max = (s->max_block + 15) / 16;
   s->apart_floats = (size_t)B * s->qtn_max * H * s->S * 16 * (DHm + 2);
   s->w_apart = take(s->apart_floats * 4);
-  s->acnt_n = (size_t)B * s->qtn_max * H;
-  s->w_acnt = take(s->acnt_n * 4);
   s->ws_total = off;
 }
 
@@ -295,19 +241,40 @@ hipEvent_t pool_event(evs_state* s) {
   return e;
 }
 
-// Time one launch when the state's timing is on: `launch` enqueues the kernel.
+// End the open run of timed launches (if any) with an event on its stream.
+hipError_t close_span(evs_state* s) {
+  if (!s->span_a) return hipSuccess;
+  hipEvent_t b = pool_event(s);
+  if (!b) return hipErrorOutOfMemory;
+  const hipError_t e = hipEventRecord(b, s->span_st);
+  if (e != hipSuccess) return e;
+  s->recs.push_back({s->span_a, b, s->span_kc, s->span_bytes, s->span_n});
+  s->span_a = nullptr;
+  return hipSuccess;
+}
+
+// Time a launch when the state's timing is on: `launch` enqueues the kernel.
+// Consecutive launches of one class on one stream share a single event pair
+// (the run closes at the first launch of another class and at the end of the
+// API call), so the events add no gaps inside a run of back-to-back kernels.
 template <typename F>
 hipError_t timed(evs_state* s, int kc, double bytes, hipStream_t st, F&& launch) {
   if (!s->timing) return launch();
-  hipEvent_t a = pool_event(s), b = pool_event(s);
-  if (!a || !b) return hipErrorOutOfMemory;
-  hipError_t e = hipEventRecord(a, st);
+  if (s->span_a && (s->span_kc != kc || s->span_st != st)) {
+    const hipError_t e = close_span(s);
+    if (e != hipSuccess) return e;
+  }
+  if (!s->span_a) {
+    hipEvent_t a = pool_event(s);
+    if (!a) return hipErrorOutOfMemory;
+    const hipError_t e = hipEventRecord(a, st);
+    if (e != hipSuccess) return e;
+    s->span_a = a; s->span_kc = kc; s->span_n = 0; s->span_bytes = 0; s->span_st = st;
+  }
+  const hipError_t e = launch();
   if (e != hipSuccess) return e;
-  e = launch();
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(b, st);
-  if (e != hipSuccess) return e;
-  s->recs.push_back({a, b, kc, bytes});
+  ++s->span_n;
+  s->span_bytes += bytes;
   return hipSuccess;
 }
 #define EVS_TRY(x) do { evs_status _st = (x); if (_st != EVS_OK) return _st; } while (0)
@@ -321,9 +288,6 @@ evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int 
   a.W = reinterpret_cast<const uint4*>(m->base + mat.off);
   a.ksteps = mat.K / m->kstep;
   a.n_groups = mat.n_groups;
-  a.KS = choose_ks(mat.n_groups, a.ksteps, sl.slices);
-  a.kps = (a.ksteps + a.KS - 1) / a.KS;
-  if (a.KS != 1) return EVS_E_UNSUPPORTED;
   // packed layout: [group][k-step][NT][64 lanes]; wave w of a workgroup owns
   // the contiguous k-steps [w * per_wave, (w + 1) * per_wave)
   {
@@ -341,21 +305,9 @@ evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int 
   a.nrm_ld = s->M_max;
   a.fd = (float)m->desc.d_model;
   a.eps = m->desc.norm_eps;
-  a.part = wp<float>(s, s->w_part);
-  a.cnt = wp<int>(s, s->w_cnt);
-  if (a.KS > 1) {
-    if ((size_t)sl.slices * mat.n_groups * a.KS * mat.NT * sl.MT * 256 > s->part_floats) return EVS_E_RANGE;
-    if ((size_t)sl.slices * mat.n_groups > (size_t)GEMM_CNT) return EVS_E_RANGE;
-  }
   // algorithmic bytes: the weights once, the A rows once, the outputs once
   const double bytes = (double)mat.bytes(m->es) + (double)a.M * mat.K * (amode == A_NORM ? 4 : m->es) +
                        (double)a.M * mat.rows_valid * (epi == E_RESID ? 8 : m->es);
-  if (use_sk(mat, a.ksteps, amode, epi, sl)) {
-    if (sk_part_floats(mat) > s->part_floats || (size_t)mat.n_groups > (size_t)GEMM_CNT) return EVS_E_RANGE;
-    const size_t lds = sk_lds(mat, m->es);
-    if (lds > (size_t)SK_LDS_LIMIT) return EVS_E_UNSUPPORTED;
-    return hip_ok(timed(s, EVS_KC_GEMM, bytes, st, [&] { return launch_gemm_sk<T>(mat.NT, amode, epi, a, lds, st); }));
-  }
   const size_t lds = gemm_lds(sl.MT, mat.NT, scratch_floats);
   if (lds > 65536) return EVS_E_UNSUPPORTED;
   return hip_ok(timed(s, EVS_KC_GEMM, bytes, st,
@@ -417,7 +369,7 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
       at.kc = mx.kc; at.vt = mx.vt; at.kv_bs = mx.kv_bs; at.cap = s->cap;
       at.H = p.d.n_heads; at.Dh = p.d.head_dim; at.d = d; at.P = P; at.QTN = (P + 15) / 16; at.S = s->S; at.LS = s->LS;
       at.seq0 = seq0; at.t = t; at.scale = 1.0f / std::sqrt((float)p.d.head_dim);
-      at.part = wp<float>(s, s->w_apart); at.cnt = wp<int>(s, s->w_acnt);
+      at.part = wp<float>(s, s->w_apart);
       if ((size_t)nseq * at.QTN * at.H * at.S * 16 * (at.Dh + 2) > s->apart_floats) return EVS_E_RANGE;
       // algorithmic bytes: K and V rows up to each sequence's block end (bounded
       // here by the capacity-limited length known on the host: the state's
@@ -585,8 +537,6 @@ evs_status evs_state_create(const evs_model* m, int32_t batch, int32_t max_ctx, 
   if (e == hipSuccess) e = launch_fill_i32(sp<int>(s, s->off_ib), 0, batch, st);
   if (e == hipSuccess) e = launch_fill_i32(sp<int>(s, s->off_is), -1, batch, st);
   if (e == hipSuccess) e = launch_fill_i32(sp<int>(s, s->off_err), 0, 1, st);
-  if (e == hipSuccess) e = launch_fill_i32(wp<int>(s, s->w_cnt), 0, GEMM_CNT, st);
-  if (e == hipSuccess) e = launch_fill_i32(wp<int>(s, s->w_acnt), 0, (long long)s->acnt_n, st);
   if (e != hipSuccess) { delete s; return EVS_E_HIP; }
   *out = s;
   return EVS_OK;
@@ -665,6 +615,7 @@ evs_status evs_prefill(evs_model* m, evs_state* s, const int32_t* tokens, const 
       const bool last = a + P == n;
       void* lg = (last && last_logits) ? wp<void>(s, s->w_logit) : nullptr;
       EVS_TRY(forward_any(m, s, b, 1, P, tokens + offs[b] + a, lg, st));
+      HIP_TRY(close_span(s));
       HIP_TRY(launch_commit(sp<int>(s, s->off_t) + b, sp<int>(s, s->off_ib) + b, sp<int>(s, s->off_is) + b,
                             nullptr, P, 1, P, sp<int>(s, s->off_err), st));
       if (lg)
@@ -681,6 +632,7 @@ evs_status evs_block_verify(evs_model* m, evs_state* s, const int32_t* cand, int
   if (gamma < 0 || gamma + 1 > s->max_block) return EVS_E_RANGE;
   s->pending = false;   // a pending block is discarded (rollback to 0 changes nothing on device)
   EVS_TRY(forward_any(m, s, 0, s->B, gamma + 1, cand, logits, reinterpret_cast<hipStream_t>(stream)));
+  HIP_TRY(close_span(s));
   s->pending = true;
   s->pending_P = gamma + 1;
   return EVS_OK;
@@ -715,6 +667,7 @@ evs_status evs_verify_sample(int32_t batch, int32_t gamma, int32_t vocab, const 
 
 evs_status evs_state_timing(evs_state* s, int32_t enable, int64_t context_hint) {
   if (!s) return EVS_E_INVALID;
+  HIP_TRY(close_span(s));
   s->timing = enable != 0;
   s->timing_ctx = context_hint;
   return EVS_OK;
@@ -723,6 +676,7 @@ evs_status evs_state_timing(evs_state* s, int32_t enable, int64_t context_hint) 
 evs_status evs_state_timing_read(evs_state* s, int32_t kernel_class, double* total_ms, int64_t* launches,
                                  double* bytes, void* stream) {
   if (!s || !total_ms || !launches || !bytes) return EVS_E_INVALID;
+  HIP_TRY(close_span(s));
   HIP_TRY(hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)));
   double ms = 0, by = 0;
   int64_t n = 0;
@@ -733,7 +687,7 @@ evs_status evs_state_timing_read(evs_state* s, int32_t kernel_class, double* tot
     HIP_TRY(hipEventElapsedTime(&e, r.a, r.b));
     ms += e;
     by += r.bytes;
-    ++n;
+    n += r.n;
     s->pool.push_back(r.a);
     s->pool.push_back(r.b);
   }

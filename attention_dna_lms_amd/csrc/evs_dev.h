@@ -100,14 +100,11 @@ struct GemmArgs {
   long long tstride;     //   and between consecutive k-steps of one wave
   int ksteps;            // K / KSTEP
   int n_groups;
-  int KS;                // k-splits across workgroups (grid.x = n_groups * KS)
-  int kps;               // k-steps per split
   const void* A;         // A_ACT: T [M, lda]; A_NORM: f32 [M, lda]
   int lda;
   int M;                 // rows in this call
   int rows_per_slice;    // rows per blockIdx.y (a multiple of the positions per sequence)
   const float* nrm_part; int n_part; int nrm_ld; float fd; float eps;      // A_NORM (fd = d)
-  float* part; int* cnt;                                                     // split-K scratch
   // epilogue
   int N;                 // valid output columns (E_STORE)
   void* out; int ldo;    // E_STORE / E_GELU / E_MIXER output (storage type)
@@ -127,7 +124,6 @@ struct AttnArgs {
   const int* t;
   float scale;
   float* part;           // [B_call, QTN, H, S, 16, Dh + 2] split partials
-  int* cnt;              // unused
 };
 
 constexpr int ATTN_CHUNK = 256;   // the KV capacity is a multiple of this many keys
@@ -144,9 +140,6 @@ struct VerifyArgs {
 template <typename T>
 hipError_t launch_gemm(int MT, int NT, int amode, int epi, const GemmArgs& a, int slices,
                        size_t lds_bytes, hipStream_t st);
-template <typename T>
-hipError_t launch_gemm_sk(int NT, int amode, int epi, const GemmArgs& a, size_t lds_bytes, hipStream_t st);
-constexpr int SK_WGS = 256;   // workgroups of a balanced (stream-K) GEMM launch
 template <typename T>
 hipError_t launch_attn(const AttnArgs& a, int n_seq, hipStream_t st);
 template <typename T>

@@ -1,8 +1,6 @@
 // fp32 instantiation of the skinny GEMM (fp32 models: all casts are exact).
 #include "gemm_impl.h"
-#include "gemm_sk.h"
 
 namespace evs {
 template hipError_t launch_gemm<float>(int, int, int, int, const GemmArgs&, int, size_t, hipStream_t);
-template hipError_t launch_gemm_sk<float>(int, int, int, const GemmArgs&, size_t, hipStream_t);
 }  // namespace evs

@@ -5,12 +5,12 @@
 // wave consumes them (each wave reads one contiguous run of memory), the
 // activations ride along from L2, and MFMA does the dot products.
 //
-// Work split: workgroup = (group of NT 16-column tiles, k-split); its 8 waves
-// split the k-range further and are reduced through LDS in a fixed tree, so
-// every output's summation order depends only on K and the launch shape, never
-// on M or on other rows (block verify == sequential decode bit for bit).
-// K-splits across workgroups meet in the last-arriving workgroup, which sums
-// the partials in split order.
+// Work split: workgroup = group of NT 16-column tiles over the whole K; its 8
+// waves split the k-range and are reduced through LDS in a fixed tree, so
+// every output's summation order depends only on K, never on M or on other
+// rows (block verify == sequential decode bit for bit). Splitting K across
+// workgroups as well would need a cross-workgroup reduction whose device-scope
+// round trip costs more than it saves at these sizes.
 //
 // Prologue (A_NORM): RMSNorm of fp32 residual rows, from per-16-column sums of
 // squares the producing epilogue left behind. Epilogues: plain store (LM head),
@@ -348,13 +348,13 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   // wave-uniform values live in scalar registers, so every guard below is a
   // uniform branch and the load/wait schedule stays exact
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = blockIdx.x / a.KS, s = blockIdx.x - g * a.KS;
+  const int g = blockIdx.x;
   const int row0 = blockIdx.y * a.rows_per_slice;
   const int rows = min(a.rows_per_slice, a.M - row0);
   float* rinv = lds;                 // [MT*16]
   float* red = lds + MT * 16;        // reduction buffers, then the epilogue tile + scratch
 
-  const int kb = s * a.kps, ke = min(kb + a.kps, a.ksteps);
+  const int kb = 0, ke = a.ksteps;
   const int per_wave = (ke - kb + C::WAVES - 1) / C::WAVES;
   const int wk0 = min(kb + wave * per_wave, ke), wk1 = min(wk0 + per_wave, ke);
   const int nch = (wk1 - wk0 + CH - 1) / CH;   // chunks of CH k-steps (the last may be partial)
@@ -370,7 +370,7 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   // epilogue inputs first (only the workgroup that runs the epilogue needs
   // them, but which one that is is known only at the end)
   EpiPre pf;
-  if (a.KS == 1) epi_prefetch<T, MT, NT, EPI>(a, pf, g, row0, rows);
+  epi_prefetch<T, MT, NT, EPI>(a, pf, g, row0, rows);
   // each lane feeds activation rows mt*16 + rl (clamped to the last valid row)
   size_t arow[MT];
 #pragma unroll
@@ -569,7 +569,7 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
 template <typename T, int MT>
 static hipError_t launch_gemm_mt(int NT, int amode, int epi, const GemmArgs& a, int slices,
                                  size_t lds, hipStream_t st) {
-  dim3 grid(a.n_groups * a.KS, slices), block(512);
+  dim3 grid(a.n_groups, slices), block(512);
   if (NT == 3 && amode == A_NORM && epi == E_MIXER)
     gemm_kernel<T, MT, 3, A_NORM, E_MIXER><<<grid, block, lds, st>>>(a);
   else if (NT == 1 && amode == A_ACT && epi == E_RESID)

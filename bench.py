@@ -40,7 +40,130 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=8)
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="print the per-round kernel table of a rocprofv3 kernel trace of this bench "
+                         "(pass the same --steps/--warmup as the profiled run) and exit")
+    ap.add_argument("--summarize-counters", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="print the per-launch HBM traffic (JSON) from rocprofv3 FETCH_SIZE / WRITE_SIZE "
+                         "passes of this bench and of --copy-calibration, and exit")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy kernel five times (the "
+                         "known-size reference for scaling the HBM byte counters) and exit")
     return ap.parse_args()
+
+
+GEMM_SOURCES = ("attention_dna_lms_amd/csrc/gemm_impl.h", "attention_dna_lms_amd/csrc/gemm_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_kernel_c3_traffic.json")
+KERNEL_FAMILIES = ("attn_merge_kernel", "gemm_kernel", "attn_kernel", "verify_kernel", "commit_kernel",
+                   "embed_kernel")
+
+
+def gemm_sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_rounds(rows, steps, warmup):
+    """Dispatch rows of the headline pass's timed rounds: the run ends with two
+    passes of warmup + steps rounds, each round closed by one commit kernel."""
+    rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+    commits = [i for i, r in enumerate(rows) if "commit_kernel" in r["Kernel_Name"]]
+    n = warmup + steps
+    if len(commits) < 2 * n + 1:
+        raise SystemExit("trace holds fewer rounds than --steps/--warmup imply")
+    return rows[commits[-n - steps - 1] + 1: commits[-n - 1] + 1]
+
+
+def family(r, split_gemm=False):
+    name = r["Kernel_Name"]
+    for k in KERNEL_FAMILIES:
+        if k in name:
+            return f"{k} (grid {r['Grid_Size'] if 'Grid_Size' in r else r['Grid_Size_X']})" \
+                if split_gemm and k == "gemm_kernel" else k
+    return name[:40]
+
+
+def summarize_trace(path, steps, warmup):
+    import collections
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    for r in rows:
+        r.setdefault("Dispatch_Id", r.get("Correlation_Id", "0"))
+    sel = measured_rounds(rows, steps, warmup)
+    span = (int(sel[-1]["End_Timestamp"]) - int(sel[0]["Start_Timestamp"])) / 1e3 / steps
+    for split in (False, True):
+        g = collections.defaultdict(list)
+        for r in sel:
+            g[family(r, split)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        busy = sum(sum(v) for v in g.values()) / steps
+        if not split:
+            print(f"{steps} rounds; first dispatch to last end: {span:.1f} us per round; "
+                  f"kernel busy time {busy:.1f} us per round\n")
+        print("| kernel | launches/round | avg us | us/round |\n|---|---|---|---|")
+        for k, v in sorted(g.items(), key=lambda kv: -sum(kv[1])):
+            print(f"| {k} | {len(v) / steps:.0f} | {sum(v) / len(v):.2f} | {sum(v) / steps:.1f} |")
+        print()
+
+
+def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, steps, warmup):
+    import collections
+    import csv
+
+    def copy_scale(path, counter):
+        vals = [float(r["Counter_Value"]) * 1024 for r in csv.DictReader(open(path))
+                if "MulFunctor" in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        if not vals:
+            raise SystemExit(f"no copy dispatch in {path}")
+        return (1 << 30) / (sum(vals) / len(vals)), len(vals)
+
+    out = {"sources": list(GEMM_SOURCES), "sources_sha256": gemm_sources_hash(), "steps": steps,
+           "warmup": warmup}
+    for counter, path, cpath in (("FETCH_SIZE", fetch_csv, copy_fetch_csv), ("WRITE_SIZE", write_csv, copy_write_csv)):
+        scale, ncopy = copy_scale(cpath, counter)
+        sel = measured_rounds(list(csv.DictReader(open(path))), steps, warmup)
+        g = collections.defaultdict(list)
+        for r in sel:
+            if r["Counter_Name"] == counter:
+                g[family(r)].append(float(r["Counter_Value"]) * 1024 * scale)
+        key = "fetch" if counter == "FETCH_SIZE" else "write"
+        out[f"{key}_scale_from_copy"] = scale
+        out[f"{key}_copy_launches"] = ncopy
+        out[f"{key}_bytes_per_launch"] = {k: sum(v) / len(v) for k, v in g.items()}
+        out[f"{key}_launches_per_round"] = {k: len(v) / steps for k, v in g.items()}
+    print(json.dumps(out, indent=1))
+
+
+def gemm_traffic():
+    """Measured HBM bytes per gemm_kernel launch (fetch + write) from the
+    committed counter summary, or None if the GEMM sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha256") != gemm_sources_hash():
+        return None
+    return t["fetch_bytes_per_launch"]["gemm_kernel"] + t["write_bytes_per_launch"]["gemm_kernel"]
+
+
+def copy_calibration():
+    """Five launches of a plain elementwise copy (dst = src * 1) over 1 GiB of
+    fp32: 1 GiB read and 1 GiB written per launch."""
+    import torch
+    n = 1 << 28
+    src = torch.empty(n, dtype=torch.float32, device="cuda")
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_kernel": "torch.mul(src, 1.0, out=dst)", "bytes_read_per_launch": n * 4,
+                      "bytes_written_per_launch": n * 4, "launches": 5}), flush=True)
 
 
 def log(msg):
@@ -101,6 +224,15 @@ def cpu_baseline(cfg_full, weights_gpu, ctx, gamma, seed, n_layers):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.steps, args.warmup)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.steps, args.warmup)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the block-verify path is single-GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
@@ -221,7 +353,7 @@ def main():
         "wall_ms_per_step": round(wall_ms / args.steps, 4),
         "roofline": {"bound": "hbm", "kernel": "gemm_kernel (skinny bf16 MFMA weight streamer)",
                      "achieved": round(gemm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gemm_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(gemm_gbps / HBM_PEAK_GBPS, 4), "traffic": gemm_traffic(),
                      "avg_launch_us": round(gemm_avg_us, 3), "launches_per_step": g_n / args.steps,
                      "bytes_per_launch": round(g_bytes / max(g_n, 1)),
                      "share_of_step": round(g_ms / args.steps / ms, 4)},

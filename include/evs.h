@@ -223,11 +223,13 @@ evs_status evs_verify_sample(int32_t batch, int32_t gamma, int32_t vocab, const 
 /* kernel classes for per-launch timing */
 enum { EVS_KC_GEMM = 1, EVS_KC_ATTN = 2 };
 
-/* Measurement aid: with timing enabled, every GEMM and attention launch made
- * for this state is bracketed by a pair of HIP events on the call's stream and
- * its algorithmic bytes are noted (weights + input rows + output rows for a
- * GEMM; K/V rows up to `context_hint` positions + q + o for attention). Adds
- * two event records per launch; leave it off for headline timing. */
+/* Measurement aid: with timing enabled, the GEMM and attention launches made
+ * for this state are timed with HIP events on the call's stream and their
+ * algorithmic bytes are noted (weights + input rows + output rows for a GEMM;
+ * K/V rows up to `context_hint` positions + q + o for attention). Each run of
+ * consecutive launches of one class within one API call shares one event
+ * pair, so a run's time covers its kernels back to back (including the short
+ * gaps between them). Leave it off for headline timing. */
 evs_status evs_state_timing(evs_state* s, int32_t enable, int64_t context_hint);
 
 /* Synchronise `stream`, then sum the recorded launches of one kernel class:
