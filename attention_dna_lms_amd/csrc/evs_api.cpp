@@ -495,12 +495,13 @@ static evs_status state_setup(const evs_model* m, int32_t batch, int32_t max_ctx
   s->cap = (int)align_up((size_t)max_ctx, ATTN_CHUNK);
   // attention splits: contiguous ranges of LS keys (a multiple of 64, so each
   // of a workgroup's 4 waves gets whole 16-key tiles), fixed by the state's
-  // capacity, batch and head count (never by the block): about two
-  // workgroups per CU for a full batch of one query tile, so the launch runs
-  // in a single round
+  // capacity and the head count alone: never by the block or the batch, so a
+  // sequence's attention sums run in the same order whatever shares the
+  // launch. About two workgroups per CU for one sequence and one query tile
+  // (a single resident round); batches add workgroups.
   {
     const int heads = std::max(1, m->max_heads);
-    int s0 = (2 * ATTN_CUS) / std::max(1, heads * batch);
+    int s0 = (2 * ATTN_CUS) / heads;
     s0 = std::min(std::min(64, s0), s->cap / 64);
     s0 = std::max(1, s0);
     s->LS = (int)align_up((size_t)((s->cap + s0 - 1) / s0), 64);

@@ -506,8 +506,8 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   // Reduction of the 8 waves' partial tiles in the fixed tree
   // ((w0 + w4) + (w2 + w6)) + ((w1 + w5) + (w3 + w7)). Small tiles: every wave
   // stores its partial once and each thread sums its elements straight into
-  // the epilogue tile (one barrier). Large tiles: a staged tree through the
-  // BUFS buffers (same association when BUFS = 4).
+  // the epilogue tile (one barrier). Large tiles: the same tree staged through
+  // the BUFS buffers that fit.
   float* ep;
   if constexpr (C::FLAT) {
 #pragma unroll
@@ -529,28 +529,43 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
     }
     __syncthreads();
   } else {
+    // The same tree as pairs (dst += src) level by level, BUFS pairs per LDS
+    // round trip: w0+=w4, w2+=w6, w1+=w5, w3+=w7 | w0+=w2, w1+=w3 | w0+=w1.
+    // The association is the same for any number of buffers, so it does not
+    // depend on how many row tiles (and so how much LDS) the launch has.
+    static_assert(C::WAVES == 8, "the reduction tree is written for 8 waves");
+    constexpr int PDST[7] = {0, 2, 1, 3, 0, 1, 0}, PSRC[7] = {4, 6, 5, 7, 2, 3, 1};
+    constexpr int LV[4] = {0, 4, 6, 7};   // first pair of each level
 #pragma unroll
-    for (int n = C::WAVES; n > 1;) {
-      const int h = (C::BUFS < n / 2) ? C::BUFS : n / 2;
-      if (wave >= n - h && wave < n) {
-        float* b = red + (wave - (n - h)) * RS;
+    for (int lv = 0; lv < 3; ++lv) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+      for (int c0 = LV[lv]; c0 < LV[lv + 1]; c0 += C::BUFS) {
+        const int c1 = min(c0 + C::BUFS, LV[lv + 1]);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            *reinterpret_cast<f32x4*>(b + (nt * MT + mt) * 256 + lane * 4) = acc[nt][mt];
+        for (int c = c0; c < c1; ++c) {
+          if (wave == PSRC[c]) {
+            float* b = red + (c - c0) * RS;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                *reinterpret_cast<f32x4*>(b + (nt * MT + mt) * 256 + lane * 4) = acc[nt][mt];
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = c0; c < c1; ++c) {
+          if (wave == PDST[c]) {
+            const float* b = red + (c - c0) * RS;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                acc[nt][mt] += *reinterpret_cast<const f32x4*>(b + (nt * MT + mt) * 256 + lane * 4);
+          }
+        }
+        __syncthreads();
       }
-      __syncthreads();
-      if (wave >= n - 2 * h && wave < n - h) {
-        const float* b = red + (wave - (n - 2 * h)) * RS;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            acc[nt][mt] += *reinterpret_cast<const f32x4*>(b + (nt * MT + mt) * 256 + lane * 4);
-      }
-      __syncthreads();
-      n -= h;
     }
     // epilogue tile ep[nt][m][n] (m < MT*16, n < 16)
     ep = red;

@@ -1,0 +1,168 @@
+"""GPU parity at the long-context and ragged-batch workloads.
+
+C4: a 262,144-token context (imported state: KV rows, FIR windows and IIR
+modes are synthetic, as a prefill of that length is not needed to exercise
+the path). C5: a batch of eight sequences with ragged contexts drawn from
+1k-32k on the full 32-layer stack, gamma swept over {1, 4, 8, 12, 16}, with
+a rejection-sampling verify on Dirichlet(0.3) target/draft pairs deciding a
+ragged rollback. At the full stack the fp64 oracle is too slow to replay
+every sequence, so C5 checks what holds at any size against a per-sequence
+rerun of the same path (every reduction order is fixed by K alone, so a row's
+result cannot depend on the batch), and the verifier's decisions against the
+oracle verifier bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import evs_synth as es
+from evs_synth.configs import Block, ModelConfig
+from oracle import HybridLM
+from oracle.verifier import verify_sample
+
+from gpu_util import DEV, block_verify, import_state, lengths, make_engine, rollback
+from attention_dna_lms_amd import evs
+
+pytestmark = pytest.mark.gpu
+
+LOGIT_ATOL = 2e-2
+
+
+def logit_err(a, b):
+    """Largest |a - b| beyond one bf16 quantum of b (logits are stored in bf16)."""
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(b))[1] - 8)
+    return float(np.max(np.abs(a - b) - ulp))
+
+
+def run_verify(B, gamma, V, target, kind, q, drafts, u, T=1.0, top_k=0):
+    n_acc = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    nxt = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    keep = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    evs.evs_verify_sample(B, gamma, V, target, kind, torch.as_tensor(q).to(DEV), torch.as_tensor(drafts).to(DEV),
+                          torch.as_tensor(u).to(DEV), T, top_k, 0, n_acc, nxt, keep, err)
+    torch.cuda.synchronize()
+    assert int(err[0]) == 0
+    return n_acc.cpu().numpy(), nxt.cpu().numpy(), keep.cpu().numpy()
+
+
+def kv_rows(state, block, b, lo, hi):
+    """K and V rows [lo, hi) of sequence b as [hi - lo, H, Dh] device tensors."""
+    k = state.tensor(evs.EVS_ST_K, block)[b, :, lo:hi].permute(1, 0, 2)
+    vb = state.tensor(evs.EVS_ST_VT, block)[b]                       # [H, cap/16, Dh, 16]
+    v = vb.permute(1, 3, 0, 2).reshape(-1, vb.shape[0], vb.shape[2])[lo:hi]
+    return k, v
+
+
+# ------------------------------------------------------------------- C4
+def test_c4_attention_block_at_262k_context():
+    """One 32 x 128 attention layer at d = 4096 over 262,144 imported keys
+    (dyadic weights: q, k, v are exact on both sides). Block logits against
+    the fp64 oracle; after a rollback to 5 the committed length and the five
+    appended K/V rows bit for bit; the sampling verifier (Dirichlet(0.5)
+    drafts over ACGT, T = 1, top-k = 4) on the GPU's logits against the
+    oracle verifier."""
+    cfg = ModelConfig("single_attn", 4096, 512, [Block("attn", n_heads=32, head_dim=128)], dtype="bf16")
+    w = es.dyadic_weights(cfg, seed=16)
+    gamma, t0 = 12, 262144
+    P = gamma + 1
+    print(f"C4: importing a {t0}-key cache", flush=True)
+    synth = es.synthetic_state(cfg, t0, seed=17, device=DEV)
+    model, state = make_engine(cfg, w, batch=1, max_ctx=t0 + 64, max_block=P)
+    import_state(state, cfg, synth, t0)
+    q = es.dirichlet_acgt((1, gamma), cfg.vocab, 0.5, seed=18, tag="q")
+    drafts = es.gen.sample_from(q, seed=19)
+    cand = np.concatenate([es.prompt_tokens(cfg, 1, seed=20)[0], drafts[0]]).astype(np.int32)
+    lg, lg_dev = block_verify(model, state, cand[None])
+    print("C4: oracle block", flush=True)
+    orc = HybridLM(cfg, w)
+    pend = orc.block(orc.import_state(t0, synth), cand)
+    del synth
+    err = logit_err(lg[0], pend.logits)
+    assert err < LOGIT_ATOL, err
+    u = es.uniforms((1, gamma + 1), seed=21)
+    a, n, k = run_verify(1, gamma, cfg.vocab, lg_dev, evs.EVS_TARGET_LOGITS_BF16, q, drafts, u, 1.0, 4)
+    assert (a[0], n[0]) == verify_sample(lg[0], q[0], drafts[0], u[0], 1.0, 4)
+    assert k[0] == a[0] + 1
+    rollback(state, [5])
+    assert list(lengths(state)) == [t0 + 5]
+    kd, vd = kv_rows(state, 0, 0, t0, t0 + 5)
+    assert np.array_equal(kd.double().cpu().numpy(), pend.k_new[0][:5])
+    assert np.array_equal(vd.double().cpu().numpy(), pend.v_new[0][:5])
+
+
+# ------------------------------------------------------------------- C5
+def committed_equal(cfg, sa, ba, sb, bb):
+    """Committed state of sequence ba of sa equals that of sequence bb of sb:
+    length, FIR windows, the committed IIR modes, all K/V rows."""
+    t = int(sa.tensor(evs.EVS_ST_T)[ba])
+    if t != int(sb.tensor(evs.EVS_ST_T)[bb]):
+        return False
+    for i, blk in enumerate(cfg.blocks):
+        if blk.kind == "fir":
+            ra, rb = sa.tensor(evs.EVS_ST_FIR_RING, i)[ba], sb.tensor(evs.EVS_ST_FIR_RING, i)[bb]
+            rows = torch.as_tensor(np.arange(t - blk.fir_len + 1, t) % ra.shape[0], device=DEV)
+            if not torch.equal(ra[rows], rb[rows]):
+                return False
+        elif blk.kind == "iir":
+            ia, sla = int(sa.tensor(evs.EVS_ST_IIR_BUF)[ba]), int(sa.tensor(evs.EVS_ST_IIR_SLOT)[ba])
+            ib, slb = int(sb.tensor(evs.EVS_ST_IIR_BUF)[bb]), int(sb.tensor(evs.EVS_ST_IIR_SLOT)[bb])
+            if not torch.equal(sa.tensor(evs.EVS_ST_IIR, i)[ba, ia, sla], sb.tensor(evs.EVS_ST_IIR, i)[bb, ib, slb]):
+                return False
+        elif blk.kind == "attn":
+            ka, va = kv_rows(sa, i, ba, 0, t)
+            kb, vb = kv_rows(sb, i, bb, 0, t)
+            if not (torch.equal(ka, kb) and torch.equal(va, vb)):
+                return False
+    return True
+
+
+def test_c5_ragged_batch_gamma_sweep_full_stack():
+    """The 32-layer 7B-shaped stack, B = 8 with contexts ~ U{1024..32768}
+    (imported state), gamma swept 1, 4, 8, 12, 16 in consecutive rounds. Each
+    round: the ragged block against each sequence run alone (logits bit for
+    bit), the verifier on Dirichlet(0.3) (p, q) pairs against the oracle
+    verifier, a ragged rollback to n_acc + 1, and every sequence's committed
+    state against its solo twin's."""
+    cfg = es.stack_7b()
+    B, gmax = 8, 16
+    ctx = es.gen.rng_for(23, "c5-contexts").integers(1024, 32769, B)
+    print(f"C5: contexts {list(ctx)}", flush=True)
+    w = es.make_weights(cfg, seed=22, device=DEV)
+    model = evs.Model(cfg, w, device=DEV)
+    del w
+    max_ctx = int(ctx.max()) + 5 * (gmax + 1) + 16
+    batch = evs.State(model, B, max_ctx, gmax + 1, device=DEV)
+    solo = [evs.State(model, 1, max_ctx, gmax + 1, device=DEV) for _ in range(B)]
+    for b in range(B):
+        synth = es.synthetic_state(cfg, int(ctx[b]), seed=100 + b, device=DEV)
+        import_state(batch, cfg, synth, int(ctx[b]), b)
+        import_state(solo[b], cfg, synth, int(ctx[b]), 0)
+        del synth
+    torch.cuda.synchronize()
+    for r, gamma in enumerate((1, 4, 8, 12, 16)):
+        P = gamma + 1
+        print(f"C5: round {r}, gamma {gamma}", flush=True)
+        pt = es.dirichlet_acgt((B, P), cfg.vocab, 0.3, seed=30 + r, tag="p")
+        qd = es.dirichlet_acgt((B, gamma), cfg.vocab, 0.3, seed=30 + r, tag="q")
+        drafts = es.gen.sample_from(qd, seed=30 + r)
+        first = es.prompt_tokens(cfg, 1, seed=40 + r, batch=B)
+        cand = np.concatenate([first.reshape(B, 1), drafts], axis=1).astype(np.int32)
+        lg, _ = block_verify(model, batch, cand)
+        for b in range(B):
+            one, _ = block_verify(model, solo[b], cand[b:b + 1])
+            assert np.array_equal(one[0], lg[b]), (gamma, b)
+        u = es.uniforms((B, P), seed=50 + r)
+        a, n, keep = run_verify(B, gamma, cfg.vocab, torch.as_tensor(pt).to(DEV), evs.EVS_TARGET_PROBS_F32,
+                                qd, drafts, u)
+        for b in range(B):
+            assert (a[b], n[b]) == verify_sample(pt[b], qd[b], drafts[b], u[b], target_is_probs=True), (gamma, b)
+        t_before = lengths(batch)
+        rollback(batch, keep)
+        for b in range(B):
+            rollback(solo[b], keep[b:b + 1])
+        assert np.array_equal(lengths(batch), t_before + keep)
+        for b in range(B):
+            assert committed_equal(cfg, batch, b, solo[b], 0), (gamma, b)
+    assert batch.error() == 0 and all(s.error() == 0 for s in solo)
