@@ -186,6 +186,165 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
 
 }
 
+// bf16 models: the same schedule with 32-key tiles, so every K and V load is a
+// full 16-byte-per-lane (1 KB) vector and both products use the 16x16x32 MFMA.
+// The two S^T products of a tile take their key rows in the order
+// 8 * (r / 4) + 4 * half + r % 4 (r = MFMA row), which leaves lane (query q,
+// group g) holding the probabilities of keys 8g .. 8g+7: exactly its P^T
+// operand of O^T += V^T P^T, whose V^T operand (head dimension e, keys 8g ..
+// 8g+7) is 16 contiguous bytes of a 16-key value block.
+template <int DH>
+__global__ void __launch_bounds__(256, 2) attn32_kernel(AttnArgs a) {
+  using T = bf16;
+  constexpr int E = 8, KSTEP = 32, NKS = DH / KSTEP, NDT = DH / 16;
+  constexpr int ROW = DH + 2;
+  __shared__ float wm[4][16], wl[4][16];
+  __shared__ float wo[4][16][DH];
+
+  const int j = blockIdx.x, h = blockIdx.y;
+  const int bl = blockIdx.z / a.QTN, qt = blockIdx.z % a.QTN;
+  const int b = a.seq0 + bl;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qc = lane & 15, g = lane >> 4;
+  const int t = a.t[b], P = a.P;
+  const int kv_len = min(t + P, a.cap);
+  const int pe = min(qt * 16 + qc, P - 1);   // padding queries repeat the last real one
+  const int qpos = t + pe;
+  const int k0 = j * a.LS, k1 = min(k0 + a.LS, kv_len);   // this workgroup's keys
+
+  const T* qm = reinterpret_cast<const T*>(a.q);
+  uint4 qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    qf[ks] = *reinterpret_cast<const uint4*>(qm + act_off<E>(bl * P + pe, h * DH + ks * KSTEP + g * E, a.d));
+
+  const T* K = reinterpret_cast<const T*>(a.kc) + (size_t)b * a.kv_bs + (size_t)h * a.cap * DH;
+  const T* Vb = reinterpret_cast<const T*>(a.vt) + (size_t)b * a.kv_bs + (size_t)h * DH * a.cap;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // this wave's tiles: key0 = k0 + 32 * (wave + 4 * i). One tile buffer,
+  // refilled as soon as it is consumed: the next tile's K loads go out right
+  // after this tile's S^T product, its V loads right after the P V product.
+  // Tiles past the last re-read the last one (inside the cache: the capacity
+  // is a multiple of 32) and are never used.
+  const int nt_all = (k1 > k0) ? (k1 - k0 + 31) / 32 : 0;
+  const int ntile = nt_all > wave ? (nt_all - wave + 3) / 4 : 0;
+  auto tile_key = [&](int i) { return k0 + 32 * (wave + 4 * min(i, max(ntile - 1, 0))); };
+  const int krow = 8 * (qc >> 2) + (qc & 3);   // key of MFMA row qc in the first half
+  uint4 kf[2][NKS], vf[NDT];
+  auto issue_k = [&](int i) {
+    const int key0 = ntile > 0 ? tile_key(i) : 0;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        kf[hf][ks] = *reinterpret_cast<const uint4*>(K + (size_t)(key0 + krow + 4 * hf) * DH + ks * KSTEP + g * E);
+  };
+  auto issue_v = [&](int i) {
+    const int key0 = ntile > 0 ? tile_key(i) : 0;
+    const T* vb = Vb + (size_t)(key0 / 16 + (g >> 1)) * (DH * 16) + 8 * (g & 1);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vf[dt] = *reinterpret_cast<const uint4*>(vb + (dt * 16 + qc) * 16);
+  };
+  issue_k(0);
+  issue_v(0);
+  for (int i = 0; i < ntile; ++i) {
+    const int key0 = tile_key(i);
+    f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      sc[0] = mma_frag(kf[0][ks], qf[ks], sc[0], T());
+      sc[1] = mma_frag(kf[1][ks], qf[ks], sc[1], T());
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    issue_k(i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // lane holds the scores of keys key0 + 8g + 4 * half + r (r < 4) for query qc
+    const int kb = key0 + 8 * g;
+    float sv[8];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int key = kb + q;
+      sv[q] = (key <= qpos && key < k1) ? sc[q >> 2][q & 3] * a.scale : -INFINITY;
+      mt = fmaxf(mt, sv[q]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = (m_new == -INFINITY) ? 1.f : expf(m_run - m_new);
+    float ls = 0.f;
+    bf16x8 pb;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float pv = (sv[q] == -INFINITY) ? 0.f : expf(sv[q] - m_new);
+      ls += pv;
+      pb[q] = (bf16)pv;
+    }
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+    // values of keys past this workgroup's range are zeroed (the cache rows
+    // there may hold anything, and 0 * NaN is NaN)
+    if (kb + 8 > k1) {
+      const int nv = max(0, min(8, k1 - kb));
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        unsigned w[4] = {vf[dt].x, vf[dt].y, vf[dt].z, vf[dt].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (2 * q >= nv) w[q] = 0u;
+          else if (2 * q + 1 >= nv) w[q] &= 0xffffu;
+        }
+        vf[dt] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    // O^T += V^T P^T: A rows = head dims, B columns = queries, k = the tile's keys
+    const uint4 pu = __builtin_bit_cast(uint4, pb);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      o[dt] = o[dt] * alpha;
+      o[dt] = mma_frag(vf[dt], pu, o[dt], T());
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    issue_v(i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // merge the 4 waves (fixed order) into this workgroup's partial
+  if (g == 0) { wm[wave][qc] = m_run; wl[wave][qc] = l_run; }
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wo[wave][qc][dt * 16 + 4 * g + q] = o[dt][q];
+  __syncthreads();
+  const size_t head = (size_t)blockIdx.z * a.H + h;
+  float* part = a.part + head * a.S * 16 * ROW;
+  for (int idx = tid; idx < 16 * ROW; idx += 256) {
+    const int q = idx / ROW, e = idx % ROW;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][q]);
+    float v = 0.f;
+    if (e == DH) {
+      v = M;
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = (wm[w][q] == -INFINITY) ? 0.f : expf(wm[w][q] - M);
+        v += (e < DH ? wo[w][q][e] : wl[w][q]) * f;
+      }
+    }
+    part[((size_t)j * 16 + q) * ROW + e] = v;
+  }
+}
+
 // Merge the S split partials of each (sequence, query tile, head) in range
 // order: one thread per (query, head dimension), all of a thread's partial
 // loads in flight together. A separate launch, so the partials are visible by
@@ -232,12 +391,24 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a) {
 
 template <typename T>
 hipError_t launch_attn(const AttnArgs& a, int n_seq, hipStream_t st) {
-  if (a.S > 64 || a.S < 1 || a.LS < 16 || a.LS % 16) return hipErrorInvalidValue;
+  // whole 16-key tiles per range (32-key tiles for bf16: the capacity is a
+  // multiple of 256, so a range's last tile stays inside the cache)
+  if (a.S > 64 || a.S < 1 || a.LS < 16 || a.LS % 16 || a.cap % 256) return hipErrorInvalidValue;
   dim3 grid(a.S, a.H, n_seq * a.QTN), block(256), mgrid(a.Dh / 16, a.H, n_seq * a.QTN);
+  constexpr bool B16 = sizeof(T) == 2;
   switch (a.Dh) {
-    case 32: attn_kernel<T, 32><<<grid, block, 0, st>>>(a); attn_merge_kernel<T, 32><<<mgrid, block, 0, st>>>(a); break;
-    case 64: attn_kernel<T, 64><<<grid, block, 0, st>>>(a); attn_merge_kernel<T, 64><<<mgrid, block, 0, st>>>(a); break;
-    case 128: attn_kernel<T, 128><<<grid, block, 0, st>>>(a); attn_merge_kernel<T, 128><<<mgrid, block, 0, st>>>(a); break;
+    case 32:
+      if constexpr (B16) attn32_kernel<32><<<grid, block, 0, st>>>(a); else attn_kernel<T, 32><<<grid, block, 0, st>>>(a);
+      attn_merge_kernel<T, 32><<<mgrid, block, 0, st>>>(a);
+      break;
+    case 64:
+      if constexpr (B16) attn32_kernel<64><<<grid, block, 0, st>>>(a); else attn_kernel<T, 64><<<grid, block, 0, st>>>(a);
+      attn_merge_kernel<T, 64><<<mgrid, block, 0, st>>>(a);
+      break;
+    case 128:
+      if constexpr (B16) attn32_kernel<128><<<grid, block, 0, st>>>(a); else attn_kernel<T, 128><<<grid, block, 0, st>>>(a);
+      attn_merge_kernel<T, 128><<<mgrid, block, 0, st>>>(a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

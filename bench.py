@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=8)
+    ap.add_argument("--import-state", action="store_true",
+                    help="fill the committed state with seeded synthetic values at --context tokens "
+                         "(KV rows, FIR windows, IIR modes) instead of prefilling: long-context timing")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="print the per-round kernel table of a rocprofv3 kernel trace of this bench "
                          "(pass the same --steps/--warmup as the profiled run) and exit")
@@ -55,8 +58,8 @@ def parse():
 
 GEMM_SOURCES = ("attention_dna_lms_amd/csrc/gemm_impl.h", "attention_dna_lms_amd/csrc/gemm_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_kernel_c3_traffic.json")
-KERNEL_FAMILIES = ("attn_merge_kernel", "gemm_kernel", "attn_kernel", "verify_kernel", "commit_kernel",
-                   "embed_kernel")
+KERNEL_FAMILIES = ("attn_merge_kernel", "gemm_kernel", "attn32_kernel", "attn_kernel", "verify_kernel",
+                   "commit_kernel", "embed_kernel")
 
 
 def gemm_sources_hash():
@@ -149,6 +152,35 @@ def gemm_traffic():
     if t.get("sources_sha256") != gemm_sources_hash():
         return None
     return t["fetch_bytes_per_launch"]["gemm_kernel"] + t["write_bytes_per_launch"]["gemm_kernel"]
+
+
+def import_synthetic_state(evs, es, cfg, state, t, seed, dev):
+    """Committed state of sequence 0 at length t from evs_synth.synthetic_state
+    (the layouts are those evs_state_tensor describes)."""
+    import numpy as np
+    import torch
+    synth = es.synthetic_state(cfg, t, seed=seed, device=dev)
+    state.tensor(evs.EVS_ST_T)[0] = t
+    state.tensor(evs.EVS_ST_IIR_BUF)[0] = 0
+    state.tensor(evs.EVS_ST_IIR_SLOT)[0] = 0
+    for i, blk in enumerate(cfg.blocks):
+        if blk.kind == "fir":
+            ring = state.tensor(evs.EVS_ST_FIR_RING, i)[0]
+            pos = np.arange(t - (blk.fir_len - 1), t)
+            ok = np.nonzero(pos >= 0)[0]
+            ring[torch.as_tensor(pos[ok] % ring.shape[0], device=dev)] = synth[i]["hist"][torch.as_tensor(ok, device=dev)]
+        elif blk.kind == "iir":
+            state.tensor(evs.EVS_ST_IIR, i)[0, 0, 0] = synth[i]["s"]
+        elif blk.kind == "attn":
+            state.tensor(evs.EVS_ST_K, i)[0, :, :t] = synth[i]["k"].permute(1, 0, 2)
+            vb = state.tensor(evs.EVS_ST_VT, i)[0]                       # [H, cap/16, Dh, 16]
+            nb = (t + 15) // 16
+            v = torch.zeros(nb * 16, vb.shape[0], vb.shape[2], dtype=vb.dtype, device=dev)
+            v[:t] = synth[i]["v"]
+            vb[:, :nb] = v.reshape(nb, 16, vb.shape[0], vb.shape[2]).permute(2, 0, 3, 1)
+            del v
+        synth[i] = None
+    torch.cuda.synchronize()
 
 
 def copy_calibration():
@@ -252,10 +284,16 @@ def main():
     model = evs.Model(cfg, weights, device=dev)
     max_ctx = ctx + 2 * rounds * P + 64
     state = evs.State(model, 1, max_ctx, 144, device=dev)
-    log(f"prefill {ctx} tokens")
-    prompt = torch.from_numpy(es.prompt_tokens(cfg, ctx, seed=args.seed)[0]).to(dev)
     last = torch.empty(1, cfg.vocab, dtype=torch.bfloat16, device=dev)
-    evs.evs_prefill(model, state, prompt, [0, ctx], last)
+    if args.import_state:
+        log(f"importing a synthetic {ctx}-token state")
+        import_synthetic_state(evs, es, cfg, state, ctx, args.seed, dev)
+        last.zero_()
+        last[0, es.ACGT_IDS(cfg.vocab)[0]] = 1.0
+    else:
+        log(f"prefill {ctx} tokens")
+        prompt = torch.from_numpy(es.prompt_tokens(cfg, ctx, seed=args.seed)[0]).to(dev)
+        evs.evs_prefill(model, state, prompt, [0, ctx], last)
     torch.cuda.synchronize()
     snap = state.buf.clone()
 
@@ -393,7 +431,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded random-init weights, uniform ACGT prompt, identity drafter)",
+        "data": "synthetic (seeded random-init weights, " + ("imported synthetic state" if args.import_state
+                 else "uniform ACGT prompt") + ", identity drafter)",
         "config": {"workload": "7B-shaped 32-layer hybrid stack (FIR-7/FIR-128/IIR-16 mixers, attention "
                                "32x128 every 8th layer, gated MLP d_ff=11008, vocab 512, ~13 GB bf16), "
                                f"{ctx}-token context, gamma={gamma}, batch 1, greedy identity drafter; "
@@ -418,7 +457,7 @@ def main():
                       "achieved_gbps": round(a_bytes / (a_ms / 1e3) / 1e9, 1) if a_ms > 0 else 0.0},
     }
     log(f"GPU part done in {time.time() - t_all:.1f}s: {ms:.3f} ms/round")
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.import_state:
         log("CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(cfg, weights, ctx, gamma, args.seed, args.cpu_layers)
     else:
