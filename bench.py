@@ -40,6 +40,12 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=8)
+    ap.add_argument("--soak", type=int, metavar="N",
+                    help="generate N tokens natively and speculatively (~75% drafter) from the "
+                         "prefilled context and check they are identical; one JSON line")
+    ap.add_argument("--batch-sweep", metavar="B1,B2,...",
+                    help="speculative rounds against plain batched decoding at these batch sizes "
+                         "(imported synthetic state; eager and HIP-graph replay), one JSON line each")
     ap.add_argument("--import-state", action="store_true",
                     help="fill the committed state with seeded synthetic values at --context tokens "
                          "(KV rows, FIR windows, IIR modes) instead of prefilling: long-context timing")
@@ -154,26 +160,26 @@ def gemm_traffic():
     return t["fetch_bytes_per_launch"]["gemm_kernel"] + t["write_bytes_per_launch"]["gemm_kernel"]
 
 
-def import_synthetic_state(evs, es, cfg, state, t, seed, dev):
-    """Committed state of sequence 0 at length t from evs_synth.synthetic_state
+def import_synthetic_state(evs, es, cfg, state, t, seed, dev, b=0):
+    """Committed state of sequence b at length t from evs_synth.synthetic_state
     (the layouts are those evs_state_tensor describes)."""
     import numpy as np
     import torch
     synth = es.synthetic_state(cfg, t, seed=seed, device=dev)
-    state.tensor(evs.EVS_ST_T)[0] = t
-    state.tensor(evs.EVS_ST_IIR_BUF)[0] = 0
-    state.tensor(evs.EVS_ST_IIR_SLOT)[0] = 0
+    state.tensor(evs.EVS_ST_T)[b] = t
+    state.tensor(evs.EVS_ST_IIR_BUF)[b] = 0
+    state.tensor(evs.EVS_ST_IIR_SLOT)[b] = 0
     for i, blk in enumerate(cfg.blocks):
         if blk.kind == "fir":
-            ring = state.tensor(evs.EVS_ST_FIR_RING, i)[0]
+            ring = state.tensor(evs.EVS_ST_FIR_RING, i)[b]
             pos = np.arange(t - (blk.fir_len - 1), t)
             ok = np.nonzero(pos >= 0)[0]
             ring[torch.as_tensor(pos[ok] % ring.shape[0], device=dev)] = synth[i]["hist"][torch.as_tensor(ok, device=dev)]
         elif blk.kind == "iir":
-            state.tensor(evs.EVS_ST_IIR, i)[0, 0, 0] = synth[i]["s"]
+            state.tensor(evs.EVS_ST_IIR, i)[b, 0, 0] = synth[i]["s"]
         elif blk.kind == "attn":
-            state.tensor(evs.EVS_ST_K, i)[0, :, :t] = synth[i]["k"].permute(1, 0, 2)
-            vb = state.tensor(evs.EVS_ST_VT, i)[0]                       # [H, cap/16, Dh, 16]
+            state.tensor(evs.EVS_ST_K, i)[b, :, :t] = synth[i]["k"].permute(1, 0, 2)
+            vb = state.tensor(evs.EVS_ST_VT, i)[b]                       # [H, cap/16, Dh, 16]
             nb = (t + 15) // 16
             v = torch.zeros(nb * 16, vb.shape[0], vb.shape[2], dtype=vb.dtype, device=dev)
             v[:t] = synth[i]["v"]
@@ -181,6 +187,220 @@ def import_synthetic_state(evs, es, cfg, state, t, seed, dev):
             del v
         synth[i] = None
     torch.cuda.synchronize()
+
+
+def batch_sweep(args):
+    """Speculative rounds against plain batched decoding over batch sizes, on
+    the 7B-shaped stack with an imported synthetic state per sequence. Prints
+    one JSON line per batch size: native (gamma = 0) step time and tokens/s,
+    identity-drafter round time and tokens/s (eager launches, then the same
+    round captured once as a HIP graph and replayed, the block gathered on the
+    device from each sequence's own position), and the speculative speedup."""
+    import numpy as np
+    import torch
+    import evs_synth as es
+    from attention_dna_lms_amd import evs
+
+    dev = "cuda"
+    gamma, P, ctx = args.gamma, args.gamma + 1, args.context
+    cfg = es.stack_7b()
+    log("generating and packing weights")
+    model = evs.Model(cfg, es.make_weights(cfg, seed=args.seed, device=dev), device=dev)
+    W, K = args.warmup, args.steps
+    rounds = W + K
+    n_nat = 2 * rounds * P + 2          # native tokens per sequence: eager + graph passes
+    for B in [int(x) for x in args.batch_sweep.split(",")]:
+        state = evs.State(model, B, ctx + n_nat + 64, P, device=dev)
+        for b in range(B):
+            import_synthetic_state(evs, es, cfg, state, ctx, args.seed + b, dev, b)
+        snap = state.buf.clone()
+        V = cfg.vocab
+        one = torch.empty(B, 1, V, dtype=torch.bfloat16, device=dev)
+        acc1 = torch.zeros(B, dtype=torch.int32, device=dev)
+        keep1 = torch.zeros(B, dtype=torch.int32, device=dev)
+        nat = torch.zeros(n_nat, B, dtype=torch.int32, device=dev)     # [step, sequence]
+        nat[0] = torch.as_tensor(es.ACGT_IDS(V), dtype=torch.int32, device=dev)[torch.arange(B, device=dev) % 4]
+
+        def native_step(i):
+            evs.evs_block_verify(model, state, nat[i].view(B, 1), 0, one)
+            evs.evs_verify_sample(B, 0, V, one, evs.EVS_TARGET_LOGITS_BF16, None, None, None, 1.0, 0, 1,
+                                  acc1, nat[i + 1], keep1)
+            evs.evs_rollback(state, keep1)
+        for i in range(W):
+            native_step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(W, n_nat - 1):
+            native_step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        t_nat = e0.elapsed_time(e1) / (n_nat - 1 - W)
+        natT = nat.t().contiguous()                                      # [sequence, step]
+
+        lg = torch.empty(B, P, V, dtype=torch.bfloat16, device=dev)
+        acc = torch.zeros(B, dtype=torch.int32, device=dev)
+        nxt = torch.zeros(B, dtype=torch.int32, device=dev)
+        keep = torch.zeros(B, dtype=torch.int32, device=dev)
+        pos = torch.zeros(B, dtype=torch.long, device=dev)
+        ar = torch.arange(P, device=dev)
+        rows = torch.arange(B, device=dev)[:, None]
+
+        def spec_round():
+            cand = natT[rows, pos[:, None] + ar]                         # [B, P] from each sequence's position
+            evs.evs_block_verify(model, state, cand, gamma, lg)
+            evs.evs_verify_sample(B, gamma, V, lg, evs.EVS_TARGET_LOGITS_BF16, None, cand[:, 1:].contiguous(), None,
+                                  1.0, 0, 1, acc, nxt, keep)
+            evs.evs_rollback(state, keep)
+            pos.add_(keep)
+
+        def timed(fn, n):
+            torch.cuda.synchronize()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record()
+            for _ in range(n):
+                fn()
+            a1.record()
+            torch.cuda.synchronize()
+            return a0.elapsed_time(a1) / n
+
+        state.buf.copy_(snap)
+        pos.zero_()
+        for _ in range(W):
+            spec_round()
+        t_eager = timed(spec_round, K)
+        acc_eager = acc.clone()
+        t_after, lg_eager = state.tensor(evs.EVS_ST_T).clone(), lg.clone()
+
+        state.buf.copy_(snap)
+        pos.zero_()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            spec_round()                                                 # warm the allocator on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        state.buf.copy_(snap)
+        pos.zero_()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            spec_round()
+        # capture records without running: replay from the snapshot
+        state.buf.copy_(snap)
+        pos.zero_()
+        torch.cuda.synchronize()
+        for _ in range(W):
+            graph.replay()
+        t_graph = timed(graph.replay, K)
+        same = bool(torch.equal(state.tensor(evs.EVS_ST_T), t_after) and torch.equal(lg, lg_eager)
+                    and torch.equal(acc, acc_eager))
+        assert state.error() == 0
+        print(json.dumps({"batch": B, "gamma": gamma, "context": ctx,
+                          "native_step_ms": round(t_nat, 4), "native_tokens_per_s": round(B * 1e3 / t_nat, 1),
+                          "spec_round_ms": round(t_eager, 4), "spec_tokens_per_s": round(B * P * 1e3 / t_eager, 1),
+                          "spec_round_graph_ms": round(t_graph, 4),
+                          "spec_tokens_per_s_graph": round(B * P * 1e3 / t_graph, 1),
+                          "speedup_identity_drafter": round(P * t_nat / t_eager, 3),
+                          "graph_matches_eager": same,
+                          "all_drafts_accepted": bool((acc_eager == gamma).all())}), flush=True)
+        del state, snap, graph
+        torch.cuda.empty_cache()
+
+
+def soak(args):
+    """Generation at depth: from the 8192-token prefill, N tokens of native
+    greedy decoding, then the same N tokens generated by speculative rounds
+    with the ~75% drafter (drafts gathered on the device from the native
+    continuation at the accepted position, each replaced with p = 0.25 by a
+    different ACGT token). Greedy verification must reproduce the native
+    tokens exactly at every depth. Prints one JSON line."""
+    import numpy as np
+    import torch
+    import evs_synth as es
+    from attention_dna_lms_amd import evs
+
+    dev = "cuda"
+    gamma, P, ctx, N = args.gamma, args.gamma + 1, args.context, args.soak
+    cfg = es.stack_7b()
+    V = cfg.vocab
+    log("generating and packing weights")
+    model = evs.Model(cfg, es.make_weights(cfg, seed=args.seed, device=dev), device=dev)
+    CHECK = 32                          # rounds between host reads of the position
+    M = N + (CHECK + 1) * P             # tokens the rounds can reach before the loop sees pos >= N
+    state = evs.State(model, 1, ctx + M + 2 * P + 64, 144, device=dev)
+    log(f"prefill {ctx} tokens")
+    prompt = torch.from_numpy(es.prompt_tokens(cfg, ctx, seed=args.seed)[0]).to(dev)
+    last = torch.empty(1, V, dtype=torch.bfloat16, device=dev)
+    evs.evs_prefill(model, state, prompt, [0, ctx], last)
+    torch.cuda.synchronize()
+    snap = state.buf.clone()
+    native = torch.zeros(M + P + 1, dtype=torch.int32, device=dev)
+    native[0] = last[0].float().argmax().to(torch.int32)
+    one = torch.empty(1, 1, V, dtype=torch.bfloat16, device=dev)
+    a1 = torch.zeros(1, dtype=torch.int32, device=dev)
+    k1 = torch.zeros(1, dtype=torch.int32, device=dev)
+    log(f"native greedy decoding of {M} tokens")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(M):
+        evs.evs_block_verify(model, state, native[i:i + 1].view(1, 1), 0, one)
+        evs.evs_verify_sample(1, 0, V, one, evs.EVS_TARGET_LOGITS_BF16, None, None, None, 1.0, 0, 1,
+                              a1, native[i + 1:i + 2], k1)
+        evs.evs_rollback(state, k1)
+        if i % 4096 == 4095:
+            torch.cuda.synchronize()
+            log(f"  native {i + 1}")
+    e1.record()
+    torch.cuda.synchronize()
+    t_native = e0.elapsed_time(e1) / 1e3
+
+    log("speculative generation (~75% drafter)")
+    state.buf.copy_(snap)
+    acgt = torch.tensor(es.ACGT_IDS(V), dtype=torch.int32, device=dev)
+    lut = torch.zeros(V, dtype=torch.long, device=dev)
+    lut[acgt.long()] = torch.arange(4, device=dev)
+    max_rounds = N + CHECK              # at least one token per round
+    rng = np.random.default_rng([args.seed, 75, 1])
+    repl = torch.from_numpy(rng.random((max_rounds, gamma)) < 0.25).to(dev)
+    shift = torch.from_numpy(rng.integers(1, 4, (max_rounds, gamma))).to(dev)
+    ar = torch.arange(P, device=dev)
+    pos = torch.zeros(1, dtype=torch.long, device=dev)
+    lg = torch.empty(1, P, V, dtype=torch.bfloat16, device=dev)
+    emitted = torch.zeros(M + P + 1, dtype=torch.int32, device=dev)   # the tokens the rounds produce
+    acc = torch.zeros(1, dtype=torch.int32, device=dev)
+    nxt = torch.zeros(1, dtype=torch.int32, device=dev)
+    keep = torch.zeros(1, dtype=torch.int32, device=dev)
+    rounds = 0
+    e0.record()
+    while True:
+        blk = native[pos + ar]
+        drafts = torch.where(repl[rounds], acgt[(lut[blk[1:].long()] + shift[rounds]) % 4], blk[1:])
+        cand = torch.cat([blk[:1], drafts]).view(1, P)
+        evs.evs_block_verify(model, state, cand, gamma, lg)
+        evs.evs_verify_sample(1, gamma, V, lg, evs.EVS_TARGET_LOGITS_BF16, None, drafts.view(1, gamma), None,
+                              1.0, 0, 1, acc, nxt, keep)
+        evs.evs_rollback(state, keep)
+        # the round emits the accepted drafts and the verifier's token
+        idx = pos + 1 + ar[:gamma]
+        emitted.index_copy_(0, idx, torch.where(ar[:gamma] < acc.long(), drafts, torch.zeros_like(drafts)))
+        emitted.index_copy_(0, pos + 1 + acc.long(), nxt)
+        pos.add_(keep)
+        rounds += 1
+        if rounds % CHECK == 0 and int(pos) >= N:   # a host read every CHECK rounds only
+            break
+    e1.record()
+    torch.cuda.synchronize()
+    t_spec = e0.elapsed_time(e1) / 1e3
+    n_done = int(pos)
+    equal = bool(torch.equal(emitted[1:n_done + 1], native[1:n_done + 1]))
+    assert state.error() == 0
+    print(json.dumps({"soak_tokens": n_done, "context_start": ctx, "rounds": rounds,
+                      "emitted_tokens_per_round": round(n_done / rounds, 3),
+                      "spec_tokens_per_s": round(n_done / t_spec, 1), "native_tokens_per_s": round(M / t_native, 1),
+                      "speedup": round((n_done / t_spec) / (M / t_native), 3),
+                      "speculative_equals_native": equal}), flush=True)
 
 
 def copy_calibration():
@@ -258,6 +478,12 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.soak:
+        soak(args)
+        return
+    if args.batch_sweep:
+        batch_sweep(args)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.steps, args.warmup)
