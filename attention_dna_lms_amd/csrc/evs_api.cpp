@@ -28,8 +28,14 @@ int next_pow2(int x) { int p = 1; while (p < x) p <<= 1; return p; }
 struct Mat {            // one packed matrix
   size_t off = 0;       // byte offset in the packed buffer
   int rows_valid = 0, K = 0, n_groups = 0, NT = 1, map_kind = 0, map_stride = 0;
-  size_t bytes(int es) const { return (size_t)n_groups * NT * 16 * K * es; }
+  bool w8 = false;      // FP8 E4M3 fragments (one byte per weight) + row scales at sc_off
+  size_t sc_off = 0;
+  size_t bytes(int es) const { return (size_t)n_groups * NT * 16 * K * (w8 ? 1 : es); }
+  size_t scale_bytes() const { return w8 ? (size_t)n_groups * NT * 16 * 4 : 0; }
 };
+
+// storage type of activations, states and the non-FP8 tensors
+int storage_dtype(const evs_model_desc* d) { return d->dtype == EVS_F32 ? EVS_F32 : EVS_BF16; }
 
 struct BlockPlan {
   evs_block_desc d{};
@@ -87,7 +93,9 @@ namespace {
 
 bool check_desc(const evs_model_desc* d) {
   if (!d || !d->blocks || d->n_blocks < 0 || d->vocab < 2 || d->d_model < 32 || d->d_model % 32) return false;
-  if (d->dtype != EVS_BF16 && d->dtype != EVS_F32) return false;
+  if (d->dtype != EVS_BF16 && d->dtype != EVS_F32 && d->dtype != EVS_BF16_FP8W) return false;
+  const int kq = d->dtype == EVS_BF16_FP8W ? 64 : 32;   // FP8 fragments hold two 32-wide k-steps
+  if (d->d_model % kq) return false;
   if (!(d->norm_eps >= 0.f)) return false;
   for (int i = 0; i < d->n_blocks; ++i) {
     const evs_block_desc& b = d->blocks[i];
@@ -98,7 +106,7 @@ bool check_desc(const evs_model_desc* d) {
         if (b.head_dim != 32 && b.head_dim != 64 && b.head_dim != 128) return false;
         if (b.n_heads < 1 || (long long)b.n_heads * b.head_dim != d->d_model) return false;
         break;
-      case EVS_MLP: if (b.d_ff < 32 || b.d_ff % 32) return false; break;
+      case EVS_MLP: if (b.d_ff < 32 || b.d_ff % kq) return false; break;
       default: return false;
     }
   }
@@ -110,11 +118,17 @@ void plan_model(const evs_model_desc* desc, evs_model* m) {
   m->desc = *desc;
   m->blocks.assign(desc->blocks, desc->blocks + desc->n_blocks);
   m->desc.blocks = m->blocks.data();
-  m->es = desc->dtype == EVS_BF16 ? 2 : 4;
-  m->kstep = desc->dtype == EVS_BF16 ? 32 : 16;
+  m->es = storage_dtype(desc) == EVS_BF16 ? 2 : 4;
+  m->kstep = storage_dtype(desc) == EVS_BF16 ? 32 : 16;
   const int d = desc->d_model, V = desc->vocab, es = m->es;
+  const bool w8 = desc->dtype == EVS_BF16_FP8W;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  auto place = [&](Mat& mm) {             // block projections: FP8 in the FP8 variant
+    mm.w8 = w8;
+    mm.off = take(mm.bytes(es));
+    if (w8) mm.sc_off = take(mm.scale_bytes());
+  };
   m->embed = take((size_t)V * d * es);
   m->plan.clear();
   m->max_dff = m->max_heads = m->max_dh = 0;
@@ -123,18 +137,18 @@ void plan_model(const evs_model_desc* desc, evs_model* m) {
     p.d = b;
     if (b.kind == EVS_MLP) {
       p.w_gu = Mat{0, 2 * b.d_ff, d, b.d_ff / 16, 2, 1, b.d_ff};
-      p.w_gu.off = take(p.w_gu.bytes(es));
+      place(p.w_gu);
       p.w_down = Mat{0, d, b.d_ff, d / 16, 1, 0, 0};
-      p.w_down.off = take(p.w_down.bytes(es));
+      place(p.w_down);
       m->max_dff = std::max(m->max_dff, b.d_ff);
     } else {
       p.w_in = Mat{0, 3 * d, d, d / 16, 3, 1, d};
-      p.w_in.off = take(p.w_in.bytes(es));
+      place(p.w_in);
       if (b.kind == EVS_FIR) p.taps = take((size_t)d * b.fir_len * 4);
       if (b.kind == EVS_IIR) { p.lam = take((size_t)d * b.iir_states * 4); p.res = take((size_t)d * b.iir_states * 4); }
       if (b.kind == EVS_ATTN) { m->max_heads = std::max(m->max_heads, b.n_heads); m->max_dh = std::max(m->max_dh, b.head_dim); }
       p.w_out = Mat{0, d, d, d / 16, 1, 0, 0};
-      p.w_out.off = take(p.w_out.bytes(es));
+      place(p.w_out);
     }
     m->plan.push_back(p);
   }
@@ -148,7 +162,7 @@ struct Canon { int64_t rows, cols; int dtype; };
 std::vector<Canon> canon_list(const evs_model_desc* d) {
   std::vector<Canon> v;
   const int64_t D = d->d_model;
-  const int mt = d->dtype;
+  const int mt = storage_dtype(d);
   v.push_back({d->vocab, D, mt});
   for (int i = 0; i < d->n_blocks; ++i) {
     const evs_block_desc& b = d->blocks[i];
@@ -286,7 +300,8 @@ evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int 
                      int nseq, int P, GemmArgs a, hipStream_t st, int scratch_floats = 0) {
   const Slicing sl = slicing(nseq, P);
   a.W = reinterpret_cast<const uint4*>(m->base + mat.off);
-  a.ksteps = mat.K / m->kstep;
+  a.ksteps = mat.K / (mat.w8 ? 2 * m->kstep : m->kstep);   // weight steps (FP8: two k-steps each)
+  a.wscale = mat.w8 ? reinterpret_cast<const float*>(m->base + mat.sc_off) : nullptr;
   a.n_groups = mat.n_groups;
   // packed layout: [group][k-step][NT][64 lanes]; wave w of a workgroup owns
   // the contiguous k-steps [w * per_wave, (w + 1) * per_wave)
@@ -306,12 +321,16 @@ evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int 
   a.fd = (float)m->desc.d_model;
   a.eps = m->desc.norm_eps;
   // algorithmic bytes: the weights once, the A rows once, the outputs once
-  const double bytes = (double)mat.bytes(m->es) + (double)a.M * mat.K * (amode == A_NORM ? 4 : m->es) +
+  const double bytes = (double)(mat.bytes(m->es) + mat.scale_bytes()) + (double)a.M * mat.K * (amode == A_NORM ? 4 : m->es) +
                        (double)a.M * mat.rows_valid * (epi == E_RESID ? 8 : m->es);
   const size_t lds = gemm_lds(sl.MT, mat.NT, scratch_floats);
   if (lds > 65536) return EVS_E_UNSUPPORTED;
   return hip_ok(timed(s, EVS_KC_GEMM, bytes, st,
-                      [&] { return launch_gemm<T>(sl.MT, mat.NT, amode, epi, a, sl.slices, lds, st); }));
+                      [&] {
+                        if constexpr (sizeof(T) == 2)
+                          if (mat.w8) return launch_gemm_w8(sl.MT, mat.NT, amode, epi, a, sl.slices, lds, st);
+                        return launch_gemm<T>(sl.MT, mat.NT, amode, epi, a, sl.slices, lds, st);
+                      }));
 }
 
 template <typename T>
@@ -391,7 +410,7 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
 
 evs_status forward_any(evs_model* m, evs_state* s, int seq0, int nseq, int P, const int32_t* tokens, void* logits,
                        hipStream_t st) {
-  if (m->desc.dtype == EVS_BF16) return forward<bf16>(m, s, seq0, nseq, P, tokens, logits, st);
+  if (storage_dtype(&m->desc) == EVS_BF16) return forward<bf16>(m, s, seq0, nseq, P, tokens, logits, st);
   return forward<float>(m, s, seq0, nseq, P, tokens, logits, st);
 }
 
@@ -453,9 +472,17 @@ evs_status evs_pack_weights(evs_model* m, const void* const* canon, void* stream
   for (size_t i = 0; i < list.size(); ++i)
     if (!canon[i] || ((uintptr_t)canon[i] % 16)) return EVS_E_INVALID;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const bool bf = m->desc.dtype == EVS_BF16;
+  const bool bf = storage_dtype(&m->desc) == EVS_BF16;
   auto pack = [&](const void* src, const Mat& mm) -> hipError_t {
     uint4* dst = reinterpret_cast<uint4*>(m->base + mm.off);
+    if (mm.w8) {
+      float* sc = reinterpret_cast<float*>(m->base + mm.sc_off);
+      const bf16* w = reinterpret_cast<const bf16*>(src);
+      const hipError_t e = launch_fp8_scales(w, sc, mm.rows_valid, mm.K, mm.n_groups, mm.NT, mm.map_kind,
+                                             mm.map_stride, st);
+      if (e != hipSuccess) return e;
+      return launch_pack_fp8(w, sc, dst, mm.rows_valid, mm.K, mm.n_groups, mm.NT, mm.map_kind, mm.map_stride, st);
+    }
     if (bf) return launch_pack<bf16>(reinterpret_cast<const bf16*>(src), dst, mm.rows_valid, mm.K, mm.n_groups, mm.NT,
                                      mm.map_kind, mm.map_stride, st);
     return launch_pack<float>(reinterpret_cast<const float*>(src), dst, mm.rows_valid, mm.K, mm.n_groups, mm.NT,
@@ -551,7 +578,7 @@ evs_status evs_state_tensor(const evs_state* s, int32_t what, int32_t block, evs
   std::memset(o, 0, sizeof(*o));
   const evs_model* m = s->m;
   const int B = s->B, d = m->desc.d_model;
-  const int dt = m->desc.dtype;
+  const int dt = storage_dtype(&m->desc);
   auto need_block = [&](int kind) {
     return block >= 0 && (size_t)block < m->blocks.size() && m->blocks[block].kind == kind;
   };

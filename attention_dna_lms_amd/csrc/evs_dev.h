@@ -105,6 +105,7 @@ struct GemmArgs {
   int M;                 // rows in this call
   int rows_per_slice;    // rows per blockIdx.y (a multiple of the positions per sequence)
   const float* nrm_part; int n_part; int nrm_ld; float fd; float eps;      // A_NORM (fd = d)
+  const float* wscale;   // FP8 weights: one scale per packed row ([group][tile][16]); else null
   // epilogue
   int N;                 // valid output columns (E_STORE)
   void* out; int ldo;    // E_STORE / E_GELU / E_MIXER output (storage type)
@@ -137,6 +138,14 @@ struct VerifyArgs {
 };
 
 // ------------------------------------------------------------------ launchers
+// FP8 (E4M3) weights, bf16 activations: fragments of 16 bytes per lane hold
+// two MFMA k-steps; GemmArgs::ksteps counts those 64-wide steps
+hipError_t launch_gemm_w8(int MT, int NT, int amode, int epi, const GemmArgs& a, int slices, size_t lds_bytes,
+                          hipStream_t st);
+hipError_t launch_fp8_scales(const bf16* W, float* scales, int rows_valid, int K, int n_groups, int NT,
+                             int map_kind, int map_stride, hipStream_t st);
+hipError_t launch_pack_fp8(const bf16* W, const float* scales, uint4* out, int rows_valid, int K, int n_groups,
+                           int NT, int map_kind, int map_stride, hipStream_t st);
 template <typename T>
 hipError_t launch_gemm(int MT, int NT, int amode, int epi, const GemmArgs& a, int slices,
                        size_t lds_bytes, hipStream_t st);

@@ -329,18 +329,35 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
 }
 
 // ---------------------------------------------------------------- kernel
-template <typename T, int MT, int NT, int AMODE, int EPI, int WV = 8, int CHO = 0, int MINB = 1>
+// FP8 weight fragment (16 bytes per lane: E4M3 values of two consecutive MFMA
+// k-steps, 8 each) -> the two bf16 operands. E4M3 values are exact in bf16;
+// the row scale is applied to the reduced tile.
+template <bool UPPER>
+__device__ __forceinline__ unsigned fp8x2_to_bf16x2(unsigned x) {   // bytes 0,1 (or 2,3) of x
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, UPPER));
+}
+__device__ __forceinline__ void fp8_to_bf16(uint4 w, uint4& lo, uint4& hi) {
+  lo = make_uint4(fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x), fp8x2_to_bf16x2<false>(w.y),
+                  fp8x2_to_bf16x2<true>(w.y));
+  hi = make_uint4(fp8x2_to_bf16x2<false>(w.z), fp8x2_to_bf16x2<true>(w.z), fp8x2_to_bf16x2<false>(w.w),
+                  fp8x2_to_bf16x2<true>(w.w));
+}
+
+template <typename T, int MT, int NT, int AMODE, int EPI, int WV = 8, int CHO = 0, int MINB = 1, bool W8 = false>
 __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   static_assert(EPI != E_MIXER || WV == 8, "the mixer epilogue assumes 512 threads");
+  static_assert(!W8 || sizeof(T) == 2, "FP8 weights feed the bf16 MFMA");
   using C = GemmCfg<MT, NT, WV>;
   constexpr int E = St<T>::E, KSTEP = St<T>::KSTEP, RS = C::RS;
+  // a weight step: one MFMA k-step, or two for FP8 weights (16 bytes per lane)
+  constexpr int KPW = W8 ? 2 : 1;
   // k-steps per pipeline chunk: one chunk of NT weight fragments and MT
   // activation fragments (8 registers each for fp32 rows feeding bf16, else 4)
   // per step stays within ~64 registers, the two chunks in flight within ~128
   constexpr int AREG = (AMODE == A_NORM && sizeof(T) == 2) ? 2 : 1;
   // (measured at the 7B shapes: 4 steps for single-tile projections, 2 for
   // the gate/up pairs, the register bound for the in-projection triples)
-  constexpr int PER = 16 / (NT + AREG * MT);
+  constexpr int PER = 16 / (NT + KPW * AREG * MT);
   constexpr int CAP = NT == 1 ? 4 : NT == 2 ? 2 : 8;
   constexpr int CH = CHO ? CHO : PER < 1 ? 1 : PER < CAP ? PER : CAP;
   extern __shared__ float lds[];
@@ -378,7 +395,7 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
 
   // two chunk buffers
   uint4 w0[CH][NT], w1[CH][NT];
-  AFrag<T, AMODE> x0[CH][MT], x1[CH][MT];
+  AFrag<T, AMODE> x0[CH][MT][KPW], x1[CH][MT][KPW];
   // steps past wk1 (the tail of the last chunk, or the chunk after it)
   // re-read step wk1 - 1 and are skipped by compute
   auto wstep = [&](int k) { return max(min(k, wk1 - 1) - wk0, 0); };
@@ -388,11 +405,14 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) w[u][nt] = ld_stream(wp + (size_t)wstep(k0 + u) * a.tstride + nt * 64);
   };
-  auto issue_x = [&](AFrag<T, AMODE> (&x)[CH][MT], int k0) {
+  auto issue_x = [&](AFrag<T, AMODE> (&x)[CH][MT][KPW], int k0) {
 #pragma unroll
     for (int u = 0; u < CH; ++u)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) x[u][mt].load(a, arow[mt], max(min(k0 + u, wk1 - 1), 0) * KSTEP + aoff);
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int h = 0; h < KPW; ++h)
+          x[u][mt][h].load(a, arow[mt], (max(min(k0 + u, wk1 - 1), 0) * KPW + h) * KSTEP + aoff);
   };
   f32x4 acc[NT][MT];
 #pragma unroll
@@ -400,15 +420,30 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float rr[MT];   // this lane's RMSNorm scale per row tile (A_NORM)
-  auto compute = [&](uint4 (&w)[CH][NT], AFrag<T, AMODE> (&x)[CH][MT], int k0) {
+  auto compute = [&](uint4 (&w)[CH][NT], AFrag<T, AMODE> (&x)[CH][MT][KPW], int k0) {
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       if (k0 + u >= wk1) break;
+      if constexpr (W8) {
+        uint4 wl[NT], wh[NT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint4 xv = x[u][mt].get(rr[mt]);
+        for (int nt = 0; nt < NT; ++nt) fp8_to_bf16(w[u][nt], wl[nt], wh[nt]);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt][mt] = mma_frag(w[u][nt], xv, acc[nt][mt], T());
+        for (int mt = 0; mt < MT; ++mt) {
+          const uint4 xa = x[u][mt][0].get(rr[mt]), xb = x[u][mt][KPW - 1].get(rr[mt]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            acc[nt][mt] = mma_frag(wl[nt], xa, acc[nt][mt], T());
+            acc[nt][mt] = mma_frag(wh[nt], xb, acc[nt][mt], T());
+          }
+        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const uint4 xv = x[u][mt][0].get(rr[mt]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[nt][mt] = mma_frag(w[u][nt], xv, acc[nt][mt], T());
+        }
       }
     }
   };
@@ -525,7 +560,8 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
       // activation row 16 * mt + l % 16 -> epilogue tile ep[nt][row][column]
       const int ntmt = e >> 8, l = (e >> 2) & 63, i = e & 3;
       const int nt = ntmt / MT, mt = ntmt % MT;
-      ep[((nt * MT * 16 + mt * 16 + (l & 15)) * 16) + 4 * (l >> 4) + i] = v;
+      const float sc = W8 ? a.wscale[(g * NT + nt) * 16 + 4 * (l >> 4) + i] : 1.f;
+      ep[((nt * MT * 16 + mt * 16 + (l & 15)) * 16) + 4 * (l >> 4) + i] = W8 ? v * sc : v;
     }
     __syncthreads();
   } else {
@@ -571,10 +607,14 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
     ep = red;
     if (wave == 0) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt) {
+        f32x4 sc = f32x4{1.f, 1.f, 1.f, 1.f};
+        if constexpr (W8) sc = *reinterpret_cast<const f32x4*>(a.wscale + (g * NT + nt) * 16 + 4 * (lane >> 4));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          *reinterpret_cast<f32x4*>(ep + ((nt * MT * 16 + mt * 16 + rl) * 16 + 4 * (lane >> 4))) = acc[nt][mt];
+          *reinterpret_cast<f32x4*>(ep + ((nt * MT * 16 + mt * 16 + rl) * 16 + 4 * (lane >> 4))) =
+              W8 ? acc[nt][mt] * sc : acc[nt][mt];
+      }
     }
     __syncthreads();
   }
@@ -596,6 +636,41 @@ static hipError_t launch_gemm_mt(int NT, int amode, int epi, const GemmArgs& a, 
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+template <int MT>
+static hipError_t launch_gemm_w8_mt(int NT, int amode, int epi, const GemmArgs& a, int slices, size_t lds,
+                                    hipStream_t st) {
+  dim3 grid(a.n_groups, slices), block(512);
+  if (NT == 3 && amode == A_NORM && epi == E_MIXER)
+    gemm_kernel<bf16, MT, 3, A_NORM, E_MIXER, 8, 0, 1, true><<<grid, block, lds, st>>>(a);
+  else if (NT == 1 && amode == A_ACT && epi == E_RESID)
+    gemm_kernel<bf16, MT, 1, A_ACT, E_RESID, 8, 0, 1, true><<<grid, block, lds, st>>>(a);
+  else if (NT == 2 && amode == A_NORM && epi == E_GELU) {
+    // one row tile: one-step chunks within 128 VGPRs, so two workgroups share a CU
+    if constexpr (MT == 1) gemm_kernel<bf16, MT, 2, A_NORM, E_GELU, 8, 1, 4, true><<<grid, block, lds, st>>>(a);
+    else gemm_kernel<bf16, MT, 2, A_NORM, E_GELU, 8, 0, 1, true><<<grid, block, lds, st>>>(a);
+  }
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+inline hipError_t launch_gemm_w8_impl(int MT, int NT, int amode, int epi, const GemmArgs& a, int slices,
+                                      size_t lds, hipStream_t st) {
+  if (!a.wscale) return hipErrorInvalidValue;
+  switch (MT) {
+    case 1: return launch_gemm_w8_mt<1>(NT, amode, epi, a, slices, lds, st);
+    case 2: return launch_gemm_w8_mt<2>(NT, amode, epi, a, slices, lds, st);
+    case 3: return launch_gemm_w8_mt<3>(NT, amode, epi, a, slices, lds, st);
+    case 4: return launch_gemm_w8_mt<4>(NT, amode, epi, a, slices, lds, st);
+    case 5: return launch_gemm_w8_mt<5>(NT, amode, epi, a, slices, lds, st);
+    case 6: return launch_gemm_w8_mt<6>(NT, amode, epi, a, slices, lds, st);
+    case 7: return launch_gemm_w8_mt<7>(NT, amode, epi, a, slices, lds, st);
+    case 8: return launch_gemm_w8_mt<8>(NT, amode, epi, a, slices, lds, st);
+    case 9: return launch_gemm_w8_mt<9>(NT, amode, epi, a, slices, lds, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <typename T>

@@ -142,6 +142,103 @@ hipError_t launch_pack(const T* W, uint4* out, int rows_valid, int K, int n_grou
 template hipError_t launch_pack<bf16>(const bf16*, uint4*, int, int, int, int, int, int, hipStream_t);
 template hipError_t launch_pack<float>(const float*, uint4*, int, int, int, int, int, int, hipStream_t);
 
+// ---------------------------------------------------------------- FP8 weights
+// Row scales and E4M3 codes of the FP8 weight variant: row n keeps
+// e4m3(W[n, k] / s[n]) with s[n] the smallest power of two such that
+// max_k |W[n, k]| <= 448 * s[n] (then W / s is exact and the only rounding is
+// E4M3's, to nearest with ties to even; OCP FP8 E4M3: 4 exponent bits with
+// bias 7, 3 mantissa bits, largest 448, subnormals k * 2^-9).
+
+// canonical row of packed row r of tile nt of group g (as in pack_kernel)
+__device__ __forceinline__ long long packed_row(int g, int nt, int r, int NT, int map_kind, int map_stride) {
+  return map_kind == 0 ? (long long)(g * NT + nt) * 16 + r : (long long)nt * map_stride + g * 16 + r;
+}
+
+// one wave per packed row: max |w| over K, then the power-of-two scale
+// (from the binary exponent: max = f * 2^e, 448 = 0.875 * 2^9)
+__global__ void fp8_scale_kernel(const bf16* __restrict__ W, float* __restrict__ scales, int rows_valid, int K,
+                                 int n_rows, int NT, int map_kind, int map_stride) {
+  const int pr = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (pr >= n_rows) return;
+  const int g = pr / (NT * 16), nt = (pr / 16) % NT, r = pr % 16;
+  const long long row = packed_row(g, nt, r, NT, map_kind, map_stride);
+  float m = 0.f;
+  if (row < rows_valid)
+    for (int k = lane; k < K; k += 64) m = fmaxf(m, fabsf((float)W[row * (long long)K + k]));
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) {
+    float s = 1.f;
+    if (m > 0.f) {
+      int e;
+      const float f = frexpf(m, &e);
+      s = ldexpf(1.f, f <= 0.875f ? e - 9 : e - 8);
+    }
+    scales[pr] = s;
+  }
+}
+
+// E4M3 code of v (an exact multiple of the row scale's inverse grid): round
+// |v| to a multiple of 2^max(p - 3, -9), p the exponent of its leading bit
+__device__ __forceinline__ unsigned e4m3_code(float v) {
+  const unsigned sign = signbit(v) ? 0x80u : 0u;
+  const float a = fabsf(v);
+  if (!(a > 0.f)) return sign;
+  int e;
+  frexpf(a, &e);                                  // a = f * 2^e, leading bit 2^(e - 1)
+  const int qe = max(e - 4, -9);
+  float q = rintf(ldexpf(a, -qe));                // a / 2^qe, to nearest even
+  if (qe == -9 && q < 8.f) return sign | (unsigned)q;   // subnormal: exponent field 0
+  int p = qe + 3;                                 // value = (q / 8) * 2^p, 8 <= q <= 16
+  if (q >= 16.f) { q = 8.f; p += 1; }
+  if (p > 8 || (p == 8 && q > 14.f)) return sign | 0x7Eu;   // 448 (not reached after scaling)
+  return sign | (unsigned)(((p + 7) << 3) | ((int)q - 8));
+}
+
+// [n_groups][K/64][NT][64 lanes] of 16 bytes: lane l of (group g, step s,
+// tile nt) holds the codes of W[row][64 s + 8 (l / 16) + j] (bytes j = 0..7)
+// and W[row][64 s + 32 + 8 (l / 16) + j] (bytes 8 + j), row = packed row
+// (g, nt, l % 16). Rows past rows_valid are zero.
+__global__ void pack_fp8_kernel(const bf16* __restrict__ W, const float* __restrict__ scales, uint4* __restrict__ out,
+                                int rows_valid, int K, int n_groups, int NT, int map_kind, int map_stride) {
+  const int steps = K / 64;
+  const long long total = (long long)n_groups * steps * NT * 64;
+  for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < total;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const int lane = (int)(idx % 64);
+    long long r1 = idx / 64;
+    const int nt = (int)(r1 % NT);
+    r1 /= NT;
+    const int st = (int)(r1 % steps);
+    const int g = (int)(r1 / steps);
+    const int r = lane % 16, kb = lane / 16;
+    const long long row = packed_row(g, nt, r, NT, map_kind, map_stride);
+    unsigned w[4] = {0u, 0u, 0u, 0u};
+    if (row < rows_valid) {
+      const float inv = 1.f / scales[(g * NT + nt) * 16 + r];   // a power of two: exact
+      const bf16* src = W + row * (long long)K + (long long)st * 64 + kb * 8;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float v = (float)src[(j < 8 ? 0 : 32) + (j & 7)] * inv;
+        w[j >> 2] |= e4m3_code(v) << (8 * (j & 3));
+      }
+    }
+    out[idx] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+hipError_t launch_fp8_scales(const bf16* W, float* scales, int rows_valid, int K, int n_groups, int NT,
+                             int map_kind, int map_stride, hipStream_t st) {
+  const int n_rows = n_groups * NT * 16;
+  fp8_scale_kernel<<<(n_rows + 3) / 4, 256, 0, st>>>(W, scales, rows_valid, K, n_rows, NT, map_kind, map_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_fp8(const bf16* W, const float* scales, uint4* out, int rows_valid, int K, int n_groups,
+                           int NT, int map_kind, int map_stride, hipStream_t st) {
+  pack_fp8_kernel<<<4096, 256, 0, st>>>(W, scales, out, rows_valid, K, n_groups, NT, map_kind, map_stride);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- verifier
 // One workgroup per sequence. Target distributions (softmax over the top-k of
 // logits / T) are built in parallel, one wave per position; the accept scan,

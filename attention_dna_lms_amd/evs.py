@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libevs.so")
 
 EVS_FIR, EVS_IIR, EVS_ATTN, EVS_MLP = 1, 2, 3, 4
-EVS_BF16, EVS_F32, EVS_I32 = 1, 2, 3
+EVS_BF16, EVS_F32, EVS_I32, EVS_BF16_FP8W = 1, 2, 3, 4
 EVS_TARGET_LOGITS_BF16, EVS_TARGET_LOGITS_F32, EVS_TARGET_PROBS_F32 = 1, 2, 3
 EVS_ST_T, EVS_ST_IIR_BUF, EVS_ST_IIR_SLOT, EVS_ST_FIR_RING, EVS_ST_IIR, EVS_ST_K, EVS_ST_VT, EVS_ST_ERROR = range(1, 9)
 EVS_ERR_TOKEN, EVS_ERR_CONTEXT, EVS_ERR_NKEEP, EVS_ERR_DRAFT = 1, 2, 4, 8
@@ -122,14 +122,17 @@ def _aligned_buffer(nbytes, device):
     return raw, raw[off: off + max(int(nbytes), 1)]
 
 
-def model_desc(cfg):
+def model_desc(cfg, fp8_weights=False):
     """ModelDesc from a config with d_model, vocab, dtype ('bf16'|'f32'),
-    norm_eps and blocks (kind, fir_len, iir_states, n_heads, head_dim, d_ff)."""
+    norm_eps and blocks (kind, fir_len, iir_states, n_heads, head_dim, d_ff);
+    fp8_weights selects EVS_BF16_FP8W for a bf16 config."""
     blocks = (BlockDesc * max(len(cfg.blocks), 1))()
     for i, b in enumerate(cfg.blocks):
         blocks[i] = BlockDesc(_KINDS[b.kind], b.fir_len, b.iir_states, b.n_heads, b.head_dim, b.d_ff)
-    d = ModelDesc(cfg.d_model, cfg.vocab, len(cfg.blocks), EVS_BF16 if cfg.dtype == "bf16" else EVS_F32,
-                  float(cfg.norm_eps), blocks)
+    if fp8_weights and cfg.dtype != "bf16":
+        raise ValueError("FP8 weights are a variant of bf16 models")
+    dt = EVS_BF16_FP8W if fp8_weights else (EVS_BF16 if cfg.dtype == "bf16" else EVS_F32)
+    d = ModelDesc(cfg.d_model, cfg.vocab, len(cfg.blocks), dt, float(cfg.norm_eps), blocks)
     d._keep = blocks
     return d
 
@@ -150,12 +153,14 @@ def canonical_order(cfg):
 
 
 class Model:
-    """A packed model on the device (evs_model_create + evs_pack_weights)."""
+    """A packed model on the device (evs_model_create + evs_pack_weights); with
+    fp8_weights the block projections are quantised to FP8 E4M3 at packing."""
 
-    def __init__(self, cfg, weights, device="cuda"):
+    def __init__(self, cfg, weights, device="cuda", fp8_weights=False):
         L = lib()
         self.cfg = cfg
-        self.desc = model_desc(cfg)
+        self.fp8_weights = fp8_weights
+        self.desc = model_desc(cfg, fp8_weights)
         n = c_size_t()
         _check(L.evs_weights_bytes(ctypes.byref(self.desc), ctypes.byref(n)), "evs_weights_bytes")
         self._raw, self.packed = _aligned_buffer(n.value, device)

@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--batch-sweep", metavar="B1,B2,...",
                     help="speculative rounds against plain batched decoding at these batch sizes "
                          "(imported synthetic state; eager and HIP-graph replay), one JSON line each")
+    ap.add_argument("--weights", choices=("bf16", "fp8"), default="bf16",
+                    help="fp8: the block projections held as FP8 E4M3 with per-row scales (bf16 activations); "
+                         "the headline is bf16")
     ap.add_argument("--import-state", action="store_true",
                     help="fill the committed state with seeded synthetic values at --context tokens "
                          "(KV rows, FIR windows, IIR modes) instead of prefilling: long-context timing")
@@ -422,12 +425,23 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def round_bytes(cfg, ctx, gamma):
+def matrix_bytes(cfg, fp8=False):
+    """Bytes of the per-layer matrices: bf16, or one byte per weight plus one
+    fp32 scale per row for FP8 weights."""
+    if not fp8:
+        return cfg.layer_matrix_bytes()
+    d, n = cfg.d_model, 0
+    for b in cfg.blocks:
+        n += (4 * d * d + 4 * d * 4) if b.kind != "mlp" else (3 * d * b.d_ff + (2 * b.d_ff + d) * 4)
+    return n
+
+
+def round_bytes(cfg, ctx, gamma, fp8=False):
     """Algorithmic HBM bytes of one round: every weight once, the K/V rows of
     the attention layers up to the block end, the FIR windows and IIR modes
     read, the per-position IIR modes and KV rows written, embeddings and logits."""
     d, P = cfg.d_model, gamma + 1
-    n = cfg.layer_matrix_bytes() + P * d * 2 + cfg.vocab * d * 2   # layers, embedding rows, LM head
+    n = matrix_bytes(cfg, fp8) + P * d * 2 + cfg.vocab * d * 2   # layers, embedding rows, LM head
     for b in cfg.blocks:
         if b.kind == "attn":
             n += 2 * (ctx + P) * d * 2            # K and V read
@@ -507,7 +521,8 @@ def main():
     t_all = time.time()
     log("generating and packing weights")
     weights = es.make_weights(cfg, seed=args.seed, device=dev)
-    model = evs.Model(cfg, weights, device=dev)
+    fp8 = args.weights == "fp8"
+    model = evs.Model(cfg, weights, device=dev, fp8_weights=fp8)
     max_ctx = ctx + 2 * rounds * P + 64
     state = evs.State(model, 1, max_ctx, 144, device=dev)
     last = torch.empty(1, cfg.vocab, dtype=torch.bfloat16, device=dev)
@@ -640,9 +655,9 @@ def main():
     state.timing(False)
 
     tok_s = P / (ms / 1e3)
-    rb = round_bytes(cfg, ctx + args.warmup * P + args.steps * P // 2, gamma)
+    rb = round_bytes(cfg, ctx + args.warmup * P + args.steps * P // 2, gamma, fp8)
     gbps = rb / (ms / 1e3) / 1e9
-    weight_frac = cfg.layer_matrix_bytes() / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS
+    weight_frac = matrix_bytes(cfg, fp8) / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS
     gemm_avg_us = g_ms * 1e3 / max(g_n, 1)
     gemm_gbps = g_bytes / (g_ms / 1e3) / 1e9 if g_ms > 0 else 0.0
     out = {
@@ -656,10 +671,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if not fp8 else "bf16 activations, fp8 e4m3 weights",
         "data": "synthetic (seeded random-init weights, " + ("imported synthetic state" if args.import_state
                  else "uniform ACGT prompt") + ", identity drafter)",
-        "config": {"workload": "7B-shaped 32-layer hybrid stack (FIR-7/FIR-128/IIR-16 mixers, attention "
+        "config": {"workload": ("FP8-weight variant of the " if fp8 else "") +
+                               "7B-shaped 32-layer hybrid stack (FIR-7/FIR-128/IIR-16 mixers, attention "
                                "32x128 every 8th layer, gated MLP d_ff=11008, vocab 512, ~13 GB bf16), "
                                f"{ctx}-token context, gamma={gamma}, batch 1, greedy identity drafter; "
                                "step = block verify + verify + rollback",
@@ -674,7 +690,7 @@ def main():
         "wall_ms_per_step": round(wall_ms / args.steps, 4),
         "roofline": {"bound": "hbm", "kernel": "gemm_kernel (skinny bf16 MFMA weight streamer)",
                      "achieved": round(gemm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gemm_gbps / HBM_PEAK_GBPS, 4), "traffic": gemm_traffic(),
+                     "frac": round(gemm_gbps / HBM_PEAK_GBPS, 4), "traffic": None if fp8 else gemm_traffic(),
                      "avg_launch_us": round(gemm_avg_us, 3), "launches_per_step": g_n / args.steps,
                      "bytes_per_launch": round(g_bytes / max(g_n, 1)),
                      "share_of_step": round(g_ms / args.steps / ms, 4)},
@@ -683,7 +699,7 @@ def main():
                       "achieved_gbps": round(a_bytes / (a_ms / 1e3) / 1e9, 1) if a_ms > 0 else 0.0},
     }
     log(f"GPU part done in {time.time() - t_all:.1f}s: {ms:.3f} ms/round")
-    if not args.no_cpu_baseline and not args.import_state:
+    if not args.no_cpu_baseline and not args.import_state and not fp8:
         log("CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(cfg, weights, ctx, gamma, args.seed, args.cpu_layers)
     else:

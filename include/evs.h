@@ -54,8 +54,13 @@ typedef enum {
 
 /* block kinds */
 enum { EVS_FIR = 1, EVS_IIR = 2, EVS_ATTN = 3, EVS_MLP = 4 };
-/* storage types */
-enum { EVS_BF16 = 1, EVS_F32 = 2, EVS_I32 = 3 };
+/* storage types; EVS_BF16_FP8W is a model dtype only: a bf16 model whose block
+ * projection matrices (w_in, w_out, w_gu, w_down) are held as OCP FP8 E4M3 with
+ * one power-of-two scale per output row, the smallest s with max|w| <= 448 s
+ * (EvSpark preprint "next" item: FP8 weights). evs_pack_weights quantises the
+ * bf16 canonical tensors (round to nearest, ties to even); activations,
+ * states, embedding and LM head stay bf16 and the accumulation stays fp32. */
+enum { EVS_BF16 = 1, EVS_F32 = 2, EVS_I32 = 3, EVS_BF16_FP8W = 4 };
 /* target kinds for evs_verify_sample */
 enum { EVS_TARGET_LOGITS_BF16 = 1, EVS_TARGET_LOGITS_F32 = 2, EVS_TARGET_PROBS_F32 = 3 };
 /* sticky error-word bits */
@@ -71,7 +76,8 @@ typedef struct {
   int32_t kind, fir_len, iir_states, n_heads, head_dim, d_ff;
 } evs_block_desc;
 
-/* d_model and every d_ff are multiples of 32; vocab >= 2. */
+/* d_model and every d_ff are multiples of 32 (of 64 for EVS_BF16_FP8W);
+ * vocab >= 2. */
 typedef struct {
   int32_t d_model, vocab, n_blocks, dtype;
   float norm_eps;
