@@ -686,7 +686,7 @@ evs_status evs_verify_sample(int32_t batch, int32_t gamma, int32_t vocab, const 
   if (gamma > 0 && !draft) return EVS_E_INVALID;
   if (!greedy && (!u || (gamma > 0 && !q))) return EVS_E_INVALID;
   if (!greedy && kind != EVS_TARGET_PROBS_F32 && !(temperature > 0.f)) return EVS_E_INVALID;
-  if ((long long)(gamma + 2) * vocab > 15872) return EVS_E_UNSUPPORTED;   // LDS: 62 KB of fp32 rows
+  if ((long long)(gamma + 2) * vocab > 15360) return EVS_E_UNSUPPORTED;   // LDS: about 60 KB of fp32 rows
   VerifyArgs a{};
   a.gamma = gamma; a.V = vocab; a.kind = kind; a.top_k = top_k; a.greedy = greedy ? 1 : 0;
   a.temperature = temperature; a.target = target; a.q = q; a.draft = draft; a.u = u;

@@ -240,11 +240,26 @@ hipError_t launch_pack_fp8(const bf16* W, const float* scales, uint4* out, int r
 }
 
 // ---------------------------------------------------------------- verifier
-// One workgroup per sequence. Target distributions (softmax over the top-k of
-// logits / T) are built in parallel, one wave per position; the accept scan,
-// the residual normaliser and the inverse-CDF draw run in one lane in token
-// order, so every fp32 value matches a sequential evaluation exactly
+// One workgroup per sequence, one wave per position (up to 16 positions per
+// round). Target distributions (softmax over the top-k of logits / T) are built
+// in parallel. Every fp32 sum a decision depends on is formed in token order,
+// ((w0 + w1) + w2) + ..., so it equals a sequential evaluation exactly
 // (EvSpark preprint, abstract (iii): exact rejection-sampling verification).
+// Such a chain runs on one lane: the P softmax normalisers on P lanes of one
+// wave side by side, the draw's running sums on one lane, written over the row
+// and then searched by a wave.
+//
+// LDS holds the P target rows and the residual row, Vs floats apart: Vs is V
+// rounded up to a multiple of 4, plus 4 when that is a multiple of 8, so the
+// 16-byte reads of one column by lanes on consecutive rows fall in distinct
+// banks. Entries V .. Vs-1 hold zeros, which leave a running sum unchanged.
+
+constexpr int VERIFY_MAX_WAVES = 16;
+
+__host__ __device__ inline int verify_row_stride(int V) {
+  const int vr = (V + 3) & ~3;
+  return ((vr >> 2) & 1) ? vr : vr + 4;
+}
 
 // total order used by top-k: larger value first, lower id on ties
 __device__ __forceinline__ bool ord_gt(float v1, int i1, float v2, int i2) {
@@ -260,141 +275,243 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   }
 }
 
-__device__ __forceinline__ float load_target(const VerifyArgs& a, size_t off) {
-  if (a.kind == 1) return to_f(reinterpret_cast<const bf16*>(a.target)[off]);
-  return reinterpret_cast<const float*>(a.target)[off];
-}
-
+// the sequence's [P][V] target values into rows Vs apart, 16 loads in flight
+// per thread (NaN logits read as -inf, NaN probabilities as 0); the row and
+// column of a thread's element advance by whole steps of blockDim elements
 template <typename S>
-__device__ __forceinline__ void stage_rows(const S* src, int n, bool logits, float* dst) {
-  const int tid = threadIdx.x;
-  for (int i0 = 0; i0 < n; i0 += 256 * 16) {
+__device__ __forceinline__ void stage_rows(const S* src, int P, int V, int Vs, bool logits, float* dst) {
+  const int nt = blockDim.x, tid = threadIdx.x, n = P * V;
+  const int qn = nt / V, rn = nt - qn * V;
+  int r = tid / V, y = tid - r * V;
+  for (int i0 = 0; i0 < n; i0 += nt * 16) {
     float zv[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) zv[q] = to_f(src[min(i0 + q * 256 + tid, n - 1)]);
+    for (int q = 0; q < 16; ++q) zv[q] = to_f(src[min(i0 + q * nt + tid, n - 1)]);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const int i = i0 + q * 256 + tid;
-      if (i < n) dst[i] = isnan(zv[q]) ? (logits ? -INFINITY : 0.f) : zv[q];
+      if (i0 + q * nt + tid < n) dst[r * Vs + y] = isnan(zv[q]) ? (logits ? -INFINITY : 0.f) : zv[q];
+      y += rn;
+      r += qn;
+      if (y >= V) { y -= V; ++r; }
     }
   }
 }
 
-__device__ int icdf_seq(const float* w, int V, float u, int fallback) {
+// Sum of row[0 .. n) in token order on the calling lane (n a multiple of 4,
+// row 16-byte aligned): batches of eight 16-byte reads, then the dependent adds
+__device__ __forceinline__ float row_sum(const float* row, int n) {
+  const float4* r4 = reinterpret_cast<const float4*>(row);
+  const int n4 = n >> 2;
+  float s = 0.f;
+  int j = 0;
+#pragma unroll 2
+  for (; j + 8 <= n4; j += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = r4[j + k];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      s = s + v[k].x;
+      s = s + v[k].y;
+      s = s + v[k].z;
+      s = s + v[k].w;
+    }
+  }
+  for (; j < n4; ++j) {
+    const float4 v = r4[j];
+    s = s + v.x;
+    s = s + v.y;
+    s = s + v.z;
+    s = s + v.w;
+  }
+  return s;
+}
+
+// Running sums of row[0 .. n) in token order written over the row by the
+// calling lane; returns the total (n a multiple of 4, row 16-byte aligned)
+__device__ __forceinline__ float prefix_in_place(float* row, int n) {
+  float4* r4 = reinterpret_cast<float4*>(row);
+  const int n4 = n >> 2;
   float c = 0.f;
-  int last = -1;
-  for (int y = 0; y < V; ++y) {
-    c = c + w[y];
-    if (w[y] > 0.f) last = y;
-    if (c > u) return y;
+  int j = 0;
+  for (; j + 8 <= n4; j += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = r4[j + k];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      c = c + v[k].x;
+      v[k].x = c;
+      c = c + v[k].y;
+      v[k].y = c;
+      c = c + v[k].z;
+      v[k].z = c;
+      c = c + v[k].w;
+      v[k].w = c;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r4[j + k] = v[k];
   }
-  return last >= 0 ? last : fallback;
+  for (; j < n4; ++j) {
+    float4 v = r4[j];
+    c = c + v.x;
+    v.x = c;
+    c = c + v.y;
+    v.y = c;
+    c = c + v.z;
+    v.z = c;
+    c = c + v.w;
+    v.w = c;
+    r4[j] = v;
+  }
+  return c;
 }
 
-__global__ void __launch_bounds__(256) verify_kernel(VerifyArgs a) {
-  extern __shared__ float sm[];
-  __shared__ int amax_s[64], draft_s[64];
-  __shared__ float qx_s[64], u_s[64];
-  __shared__ int rej_s, nacc_s, next_s;
-  const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int gamma = a.gamma, P = gamma + 1, V = a.V;
-  const bool logits = a.kind != 3;
-  float* prob = sm;            // [P][V]
-  float* w = sm + (size_t)P * V;  // [V]
+struct DrawShared {
+  float sum;
+  int last, first;
+};
 
-  // phase 0: the sequence's [P][V] target values into LDS, all threads, 16
-  // loads in flight per thread (NaN logits read as -inf, NaN probabilities as 0)
-  if (a.kind == 1)
-    stage_rows(reinterpret_cast<const bf16*>(a.target) + (size_t)b * P * V, P * V, logits, prob);
-  else
-    stage_rows(reinterpret_cast<const float*>(a.target) + (size_t)b * P * V, P * V, logits, prob);
-  // the draft tokens (and in sampling mode q(x) and u at each drafted position),
-  // one thread per position, so the accept scan reads only LDS
-  if (tid < gamma) {
-    int x = a.draft[(size_t)b * gamma + tid];
-    if (x < 0 || x >= V) {
-      if (a.err) atomicOr(a.err, 8);
-      x = x < 0 ? 0 : V - 1;
-    }
-    draft_s[tid] = x;
-    if (!a.greedy) {
-      const float qx = a.q[((size_t)b * gamma + tid) * V + x];
-      qx_s[tid] = isnan(qx) ? 0.f : qx;
-      u_s[tid] = a.u[(size_t)b * P + tid];
+// Inverse-CDF draw over row[0 .. V), called by the whole block: the first y
+// whose running sum row[0] + ... + row[y] exceeds t, where t = u * (the row's
+// sum) if scale_u, else u; if none does, the last y with row[y] > 0, else the
+// fallback. The row is overwritten by its running sums; sum gets the total.
+__device__ int draw_row(float* row, int V, int Vr, float u, bool scale_u, int fallback, float& sum,
+                        DrawShared& sh) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    int last = -1;
+    for (int y = tid; y < V; y += 64)
+      if (row[y] > 0.f) last = y;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) last = max(last, __shfl_xor(last, off));
+    if (tid == 0) {
+      sh.last = last;
+      sh.sum = prefix_in_place(row, Vr);
     }
   }
   __syncthreads();
+  const float S = sh.sum;
+  const float t = scale_u ? u * S : u;
+  if (tid < 64) {
+    int first = V;
+    for (int y = tid; y < V; y += 64)
+      if (row[y] > t) { first = y; break; }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) first = min(first, __shfl_xor(first, off));
+    if (tid == 0) sh.first = first;
+  }
+  __syncthreads();
+  const int first = sh.first, last = sh.last;
+  sum = S;
+  __syncthreads();
+  return first < V ? first : (last >= 0 ? last : fallback);
+}
 
-  // phase 1: one wave per position, positions in rounds of 4 (the barriers,
-  // needed only to normalise sampled rows, are uniform across the block)
-  __shared__ float ssum_s[4];
-  const bool any_soft = !a.greedy && logits;
-  for (int i0 = 0; i0 < P; i0 += 4) {
-    const int i = i0 + wave;
-    const bool act = i < P;
-    float* pr = prob + (size_t)(act ? i : 0) * V;
-    const bool soft = act && !a.greedy && logits;
-    if (act) {
-      float bv = -INFINITY;
-      int bi = 0;
-      for (int y = lane; y < V; y += 64) {
-        const float z = pr[y];
-        if (ord_gt(z, y, bv, bi)) { bv = z; bi = y; }
+__global__ void __launch_bounds__(64 * VERIFY_MAX_WAVES) verify_kernel(VerifyArgs a) {
+  extern __shared__ float4 sm4[];
+  __shared__ int amax_s[64], draft_s[64];
+  __shared__ float qx_s[64], u_s[64], ssum_s[64];
+  __shared__ int rej_s, nacc_s, next_s;
+  __shared__ DrawShared draw_s;
+  const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nt = blockDim.x, nw = nt >> 6;
+  const int gamma = a.gamma, P = gamma + 1, V = a.V;
+  const int Vr = (V + 3) & ~3, Vs = verify_row_stride(V);
+  const bool logits = a.kind != 3;
+  float* prob = reinterpret_cast<float*>(sm4);   // [P][Vs]
+  float* w = prob + (size_t)P * Vs;              // [Vs]
+
+  // phase 0: target rows, their zero tails, the residual row's zero tail
+  if (a.kind == 1)
+    stage_rows(reinterpret_cast<const bf16*>(a.target) + (size_t)b * P * V, P, V, Vs, logits, prob);
+  else
+    stage_rows(reinterpret_cast<const float*>(a.target) + (size_t)b * P * V, P, V, Vs, logits, prob);
+  for (int t = tid; t < (P + 1) * 4; t += nt) {
+    const int y = V + (t & 3);
+    if (y < Vs) prob[(size_t)(t >> 2) * Vs + y] = 0.f;
+  }
+  // the draft tokens, and in sampling mode q(x) at each drafted position and
+  // the uniforms, one thread per position, so the accept scan reads only LDS
+  if (tid < P) {
+    if (tid < gamma) {
+      int x = a.draft[(size_t)b * gamma + tid];
+      if (x < 0 || x >= V) {
+        if (a.err) atomicOr(a.err, 8);
+        x = x < 0 ? 0 : V - 1;
       }
-      wave_argmax(bv, bi);
-      if (lane == 0) amax_s[i] = bi;
+      draft_s[tid] = x;
+      if (!a.greedy) {
+        const float qx = a.q[((size_t)b * gamma + tid) * V + x];
+        qx_s[tid] = isnan(qx) ? 0.f : qx;
+      }
     }
-    if (soft) {
-      // z / T, then the top-k threshold (the k-th element in the total order)
-      for (int y = lane; y < V; y += 64) pr[y] = pr[y] / a.temperature;
-      const bool all = a.top_k <= 0 || a.top_k >= V;
-      float tv = -INFINITY;
-      int ti = V;
-      if (!all) {
-        float pvv = INFINITY;
-        int pii = -1;
-        for (int r = 0; r < a.top_k; ++r) {
-          float cv = -INFINITY;
-          int ci = V;
-          for (int y = lane; y < V; y += 64) {
-            const float z = pr[y];
-            if (ord_gt(pvv, pii, z, y) && ord_gt(z, y, cv, ci)) { cv = z; ci = y; }
-          }
-          wave_argmax(cv, ci);
-          pvv = cv;
-          pii = ci;
+    if (!a.greedy) u_s[tid] = a.u[(size_t)b * P + tid];
+  }
+  __syncthreads();
+
+  // phase 1: one wave per position: the argmax, and in sampling mode over
+  // logits the kept entries' exp(z/T - max) (zeros elsewhere)
+  const bool soft = !a.greedy && logits;
+  for (int i = wave; i < P; i += nw) {
+    float* pr = prob + (size_t)i * Vs;
+    float bv = -INFINITY;
+    int bi = 0;
+    for (int y = lane; y < V; y += 64) {
+      const float z = pr[y];
+      if (ord_gt(z, y, bv, bi)) { bv = z; bi = y; }
+    }
+    wave_argmax(bv, bi);
+    if (lane == 0) amax_s[i] = bi;
+    if (!soft) continue;
+    // z / T, then the top-k threshold (the k-th element in the total order)
+    for (int y = lane; y < V; y += 64) pr[y] = pr[y] / a.temperature;
+    const bool all = a.top_k <= 0 || a.top_k >= V;
+    float tv = -INFINITY;
+    int ti = V;
+    if (!all) {
+      float pvv = INFINITY;
+      int pii = -1;
+      for (int r = 0; r < a.top_k; ++r) {
+        float cv = -INFINITY;
+        int ci = V;
+        for (int y = lane; y < V; y += 64) {
+          const float z = pr[y];
+          if (ord_gt(pvv, pii, z, y) && ord_gt(z, y, cv, ci)) { cv = z; ci = y; }
         }
-        tv = pvv;
-        ti = pii;
+        wave_argmax(cv, ci);
+        pvv = cv;
+        pii = ci;
       }
-      float m = -INFINITY;
-      for (int y = lane; y < V; y += 64) {
-        const float z = pr[y];
-        if ((all || !ord_gt(tv, ti, z, y)) && isfinite(z)) m = fmaxf(m, z);
-      }
-      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      for (int y = lane; y < V; y += 64) {
-        const float z = pr[y];
-        const bool keep = (all || !ord_gt(tv, ti, z, y)) && isfinite(z);
-        pr[y] = keep ? (float)exp((double)(z - m)) : 0.f;
-      }
+      tv = pvv;
+      ti = pii;
     }
-    if (!any_soft) continue;
-    __syncthreads();
-    if (soft && lane == 0) {
-      float S = 0.f;
-      for (int y = 0; y < V; ++y) S = S + pr[y];
-      ssum_s[wave] = S;
+    float m = -INFINITY;
+    for (int y = lane; y < V; y += 64) {
+      const float z = pr[y];
+      if ((all || !ord_gt(tv, ti, z, y)) && isfinite(z)) m = fmaxf(m, z);
     }
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    for (int y = lane; y < V; y += 64) {
+      const float z = pr[y];
+      const bool keep = (all || !ord_gt(tv, ti, z, y)) && isfinite(z);
+      pr[y] = keep ? (float)exp((double)(z - m)) : 0.f;
+    }
+  }
+  __syncthreads();
+  if (soft) {
+    // the normalisers, lane i summing row i in token order; then p = e / S
+    if (wave == 0 && lane < P) ssum_s[lane] = row_sum(prob + (size_t)lane * Vs, Vr);
     __syncthreads();
-    if (soft) {
-      const float S = ssum_s[wave];
+    for (int i = wave; i < P; i += nw) {
+      float* pr = prob + (size_t)i * Vs;
+      const float S = ssum_s[i];
       for (int y = lane; y < V; y += 64) pr[y] = (S > 0.f) ? pr[y] / S : 0.f;
     }
     __syncthreads();
   }
-  __syncthreads();
 
+  // phase 2: the accept scan, one lane, stopping at the first rejection
   if (tid == 0) {
     int n_acc = gamma, nxt = -1, rej = -1;
     for (int i = 0; i < gamma; ++i) {
@@ -402,7 +519,7 @@ __global__ void __launch_bounds__(256) verify_kernel(VerifyArgs a) {
       if (a.greedy) {
         if (x != amax_s[i]) { n_acc = i; nxt = amax_s[i]; break; }
       } else {
-        const float px = prob[(size_t)i * V + x];
+        const float px = prob[(size_t)i * Vs + x];
         const float qx = qx_s[i];
         const bool ok = qx > 0.f ? (u_s[i] < px / qx) : (px > 0.f);
         if (!ok) { n_acc = i; rej = i; break; }
@@ -422,30 +539,28 @@ __global__ void __launch_bounds__(256) verify_kernel(VerifyArgs a) {
     }
     return;
   }
+
+  // phase 3: the draw, from the residual max(0, p - q) at a rejection (from p
+  // when the residual sums to zero), else from the last position's p
   const int rej = rej_s;
+  const float uf = u_s[gamma];
+  float S;
+  int nxt;
   if (rej >= 0) {
-    const float* pr = prob + (size_t)rej * V;
+    const float* pr = prob + (size_t)rej * Vs;
     const float* qr = a.q + ((size_t)b * gamma + rej) * V;
-    for (int y = tid; y < V; y += 256) {
+    for (int y = tid; y < V; y += nt) {
       float qv = qr[y];
       if (isnan(qv)) qv = 0.f;
       w[y] = fmaxf(0.f, pr[y] - qv);
     }
+    __syncthreads();
+    nxt = draw_row(w, V, Vr, uf, true, amax_s[rej], S, draw_s);
+    if (!(S > 0.f)) nxt = draw_row(prob + (size_t)rej * Vs, V, Vr, uf, false, amax_s[rej], S, draw_s);
+  } else {
+    nxt = draw_row(prob + (size_t)gamma * Vs, V, Vr, uf, false, amax_s[gamma], S, draw_s);
   }
-  __syncthreads();
   if (tid == 0) {
-    const float uf = a.u[(size_t)b * P + gamma];
-    int nxt;
-    if (rej >= 0) {
-      float S = 0.f;
-      for (int y = 0; y < V; ++y) S = S + w[y];
-      if (S > 0.f)
-        nxt = icdf_seq(w, V, uf * S, amax_s[rej]);
-      else
-        nxt = icdf_seq(prob + (size_t)rej * V, V, uf, amax_s[rej]);
-    } else {
-      nxt = icdf_seq(prob + (size_t)gamma * V, V, uf, amax_s[gamma]);
-    }
     a.n_acc[b] = nacc_s;
     a.next[b] = nxt;
     if (a.n_keep) a.n_keep[b] = nacc_s + 1;
@@ -453,8 +568,10 @@ __global__ void __launch_bounds__(256) verify_kernel(VerifyArgs a) {
 }
 
 hipError_t launch_verify(const VerifyArgs& a, int B, hipStream_t st) {
-  const size_t lds = ((size_t)(a.gamma + 2) * a.V) * sizeof(float);
-  verify_kernel<<<B, 256, lds, st>>>(a);
+  const int P = a.gamma + 1;
+  const int waves = P < VERIFY_MAX_WAVES ? P : VERIFY_MAX_WAVES;
+  const size_t lds = (size_t)(P + 1) * verify_row_stride(a.V) * sizeof(float);
+  verify_kernel<<<B, 64 * waves, lds, st>>>(a);
   return hipGetLastError();
 }
 

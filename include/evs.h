@@ -217,7 +217,7 @@ evs_status evs_rollback(evs_state* s, const int32_t* n_keep_dev, void* stream);
  * the argmax at the first mismatch or after the last row.
  * Outputs (i32 [B]): n_accepted, next_token, and n_keep = n_accepted + 1 (may
  * be NULL). Draft ids out of range are clamped and set EVS_ERR_DRAFT in
- * *error_dev if given. Requires gamma <= 63 and (gamma + 2) * V <= 15872. */
+ * *error_dev if given. Requires gamma <= 63 and (gamma + 2) * V <= 15360. */
 evs_status evs_verify_sample(int32_t batch, int32_t gamma, int32_t vocab, const void* target_dev,
                              int32_t target_kind, const float* q_dev, const int32_t* draft_dev,
                              const float* u_dev, float temperature, int32_t top_k, int32_t greedy,

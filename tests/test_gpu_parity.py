@@ -9,7 +9,7 @@ import torch
 import evs_synth as es
 from evs_synth.configs import Block, ModelConfig
 from oracle import HybridLM
-from oracle.verifier import argmax_lowest, verify_greedy, verify_sample
+from oracle.verifier import argmax_lowest, target_probs, verify_greedy, verify_sample
 
 from gpu_util import (DEV, block_verify, import_state, lengths, make_engine, max_rel, pending_iir, prefill,
                       rel_close, rollback, snapshot)
@@ -354,5 +354,37 @@ def test_verify_greedy_bitexact_with_ties():
     drafts = drafts.astype(np.int32)
     logits = torch.from_numpy(lf).to(torch.bfloat16).to(DEV)
     a, n = _run_verify(B, gamma, V, logits, evs.EVS_TARGET_LOGITS_BF16, None, drafts, None, greedy=1)
+    for b in range(B):
+        assert (a[b], n[b]) == verify_greedy(lf[b], drafts[b]), b
+
+
+@pytest.mark.parametrize("V,gamma", [(2, 0), (5, 30), (37, 20), (100, 3), (1000, 13)])
+def test_verify_odd_vocab_deep_blocks_and_degenerate_rows(V, gamma):
+    """Vocabularies that are not multiples of 4 or 8 (the kernel pads its LDS
+    rows with zeros) and blocks of more than 16 positions (several rounds of
+    waves), fp32 logits at T = 0.9 and top-k = 3, sampling and greedy. Rows
+    that exercise the fallbacks: all-NaN logits (p all zero: the draw falls
+    back to the argmax), a draft distribution twice the target with a forced
+    rejection (zero residual: the draw falls back to p), a zero draft
+    probability at the drafted token."""
+    B, T, top_k = 6, 0.9, 3
+    rng = np.random.default_rng(V * 100 + gamma)
+    lf = rng.normal(0, 2.0, (B, gamma + 1, V)).astype(np.float32)
+    lf[1, 0] = np.nan
+    q = es.draft_probs_softmax((B, gamma), V, seed=V + gamma)
+    drafts = es.gen.sample_from(q, seed=V + gamma + 1) if gamma else np.zeros((B, 0), np.int32)
+    for b in range(0, B, 2):
+        drafts[b, :(2 * gamma) // 3] = lf[b, :(2 * gamma) // 3].argmax(-1)
+    u = es.uniforms((B, gamma + 1), seed=V + gamma + 2)
+    if gamma:
+        q[3, 0] = 2.0 * target_probs(lf[3, 0], T, top_k)
+        drafts[3, 0] = argmax_lowest(lf[3, 0])
+        u[3, 0] = 0.75
+        q[5, 0, drafts[5, 0]] = 0.0
+    logits = torch.from_numpy(lf).to(DEV)
+    a, n = _run_verify(B, gamma, V, logits, evs.EVS_TARGET_LOGITS_F32, q, drafts, u, T, top_k)
+    for b in range(B):
+        assert (a[b], n[b]) == verify_sample(lf[b], q[b], drafts[b], u[b], T, top_k), b
+    a, n = _run_verify(B, gamma, V, logits, evs.EVS_TARGET_LOGITS_F32, None, drafts, None, greedy=1)
     for b in range(B):
         assert (a[b], n[b]) == verify_greedy(lf[b], drafts[b]), b
