@@ -42,6 +42,10 @@ class ModelConfig:
     blocks: List[Block] = field(default_factory=list)
     dtype: str = "bf16"          # storage type of weights/activations/KV/logits
     norm_eps: float = 1e-6
+    # drafter form (0 = a plain model): width of the injected target hidden
+    # state and the number of parallel draft slots (position embeddings)
+    inject_dim: int = 0
+    max_slots: int = 0
 
     def weight_bytes(self) -> int:
         """Bytes of the dense matrices (embedding, projections, MLP, LM head)."""
@@ -120,3 +124,12 @@ def small_stack(d: int = 256, d_ff: int = 672, vocab: int = 512, head_dim: int =
                    fir_medium=fir_medium, name=f"small_stack_d{d}")
     cfg.dtype = dtype
     return cfg
+
+
+def drafter_1024(vocab: int = 512, inject_dim: int = 4096, max_slots: int = 16) -> ModelConfig:
+    """The gamma-parallel drafter: width 1024, one pre-norm attention (8 x 128)
+    + gated-MLP layer (d_ff = 2752, the target's d_ff / d_model ratio of
+    2.6875), injected with a ``inject_dim``-wide target hidden state."""
+    return ModelConfig("drafter_1024", 1024, vocab, [Block(ATTN, n_heads=8, head_dim=128), Block(MLP, d_ff=2752)],
+                       dtype="bf16", inject_dim=inject_dim, max_slots=max_slots)
+

@@ -23,6 +23,7 @@ from .configs import ModelConfig, ACGT_IDS, FIR, IIR, ATTN, MLP
 
 WEIGHT_STD = 0.02
 RESIDUE_STD = 0.1
+MARKOV_STD = 1.0      # drafter transition logits (fp32)
 POLE_LO, POLE_HI = 0.5, 0.99
 
 
@@ -66,6 +67,8 @@ def weight_names(cfg: ModelConfig):
         else:
             raise ValueError(b.kind)
     out.append(("lm_head", (V, d)))
+    if cfg.inject_dim:
+        out += [("inject", (d, cfg.inject_dim)), ("pos", (cfg.max_slots, d)), ("markov", (V, V))]
     return out
 
 
@@ -88,6 +91,8 @@ def make_weights(cfg: ModelConfig, seed: int = 0, device="cpu") -> Dict[str, tor
             out[name] = _normal(shape, RESIDUE_STD, device, seed, name, torch.float32)
         elif name.endswith(".taps"):
             out[name] = _normal(shape, WEIGHT_STD, device, seed, name, mat_dtype).float()
+        elif name == "markov":
+            out[name] = _normal(shape, MARKOV_STD, device, seed, name, torch.float32)
         else:
             out[name] = _normal(shape, WEIGHT_STD, device, seed, name, mat_dtype)
     return out
@@ -177,7 +182,7 @@ def dyadic_weights(cfg: ModelConfig, seed: int = 0, device="cpu", step_log2: int
     mat_dtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     out = {}
     for name, shape in weight_names(cfg):
-        if name.endswith((".lam", ".res", ".taps")):
+        if name.endswith((".lam", ".res", ".taps")) or name == "markov":
             out[name] = base[name]
             continue
         g = _torch_gen(device, seed, "dyadic", name)

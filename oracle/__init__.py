@@ -14,6 +14,9 @@ Contents
   verifier  — exact rejection-sampling and greedy verification (fp32, the
               precision the GPU decides in).
   spec      — one speculative round and the snapshot-and-replay reference.
+  drafter   — the gamma-parallel drafter: hidden-state prefix, trunk, Markov
+              head and the sequential draws.
+  fp8       — the FP8 (E4M3) weight variant's quantiser.
 
 Precision: fp64 throughout, with values rounded to the model's storage type at
 the points the bf16 path stores them (projection outputs, mixer outputs, KV
@@ -27,8 +30,9 @@ from .numerics import round_bf16, gelu, rmsnorm
 from .hybrid import HybridLM, SeqState, Pending, fir_conv, iir_scan, causal_attention
 from .verifier import target_probs, verify_sample, verify_greedy, icdf
 from .spec import spec_round, native_greedy, replay
+from .drafter import Drafter
 
 __all__ = ["round_bf16", "gelu", "rmsnorm", "HybridLM", "SeqState", "Pending", "fir_conv",
            "iir_scan", "causal_attention",
            "target_probs", "verify_sample", "verify_greedy", "icdf", "spec_round",
-           "native_greedy", "replay"]
+           "native_greedy", "replay", "Drafter"]

@@ -231,8 +231,15 @@ class HybridLM:
         logits for every position and the per-position state. ``state`` is
         not modified."""
         tokens = np.asarray(tokens, dtype=np.int64)
-        pend = Pending(base=state, tokens=tokens, logits=None)
-        X = self.W["embed"][tokens].copy()                       # [P, d]
+        return self.block_rows(state, self.W["embed"][tokens].copy(), tokens, keep_x)
+
+    def block_rows(self, state: SeqState, X, tokens=None, keep_x: bool = False) -> Pending:
+        """The block forward from given input rows X [P, d] (the embedded
+        candidates, or a drafter's slot rows)."""
+        X = np.array(X, dtype=np.float64)
+        if tokens is None:
+            tokens = np.zeros(X.shape[0], dtype=np.int64)
+        pend = Pending(base=state, tokens=np.asarray(tokens, dtype=np.int64), logits=None)
         for i, b in enumerate(self.cfg.blocks):
             X = self.block_layer(i, b, state, X, pend)
             if keep_x:
