@@ -52,6 +52,8 @@ struct evs_model {
   char* base = nullptr;
   size_t embed = 0, total = 0;
   Mat lm;
+  Mat inj;                          // drafter: the hidden-state injection [d, inject_dim]
+  size_t pos = 0, markov = 0;       // drafter: position embeddings, Markov matrix (f32)
   int es = 2, kstep = 32;
   int max_dff = 0, max_heads = 0, max_dh = 0;
 };
@@ -68,6 +70,10 @@ struct evs_state {
   // workspace
   size_t w_x = 0, w_nrm = 0, w_o = 0, w_q = 0, w_h = 0, w_logit = 0, w_apart = 0, ws_total = 0;
   size_t apart_floats = 0;
+  size_t w_inj_x = 0, w_inj_nrm = 0, w_z = 0;   // drafter: injected rows, their norm partials, the prefix z
+  int inj_ld = 0;
+  int export_block = -1;                        // hidden-state export after this block (evs_block_verify)
+  float* export_dst = nullptr;
   bool pending = false;
   int pending_P = 0;
   // per-kernel timing (measurement aid): one event pair around each run of
@@ -97,6 +103,12 @@ bool check_desc(const evs_model_desc* d) {
   const int kq = d->dtype == EVS_BF16_FP8W ? 64 : 32;   // FP8 fragments hold two 32-wide k-steps
   if (d->d_model % kq) return false;
   if (!(d->norm_eps >= 0.f)) return false;
+  if (d->inject_dim < 0 || d->max_slots < 0) return false;
+  if (d->inject_dim > 0) {
+    if (d->dtype == EVS_BF16_FP8W || d->inject_dim % 32 || d->max_slots < 1 || d->max_slots > 64) return false;
+  } else if (d->max_slots != 0) {
+    return false;
+  }
   for (int i = 0; i < d->n_blocks; ++i) {
     const evs_block_desc& b = d->blocks[i];
     switch (b.kind) {
@@ -154,6 +166,12 @@ void plan_model(const evs_model_desc* desc, evs_model* m) {
   }
   m->lm = Mat{0, V, d, (V + 15) / 16, 1, 0, 0};
   m->lm.off = take(m->lm.bytes(es));
+  if (desc->inject_dim > 0) {
+    m->inj = Mat{0, d, desc->inject_dim, d / 16, 1, 0, 0};
+    m->inj.off = take(m->inj.bytes(es));
+    m->pos = take((size_t)desc->max_slots * d * es);
+    m->markov = take((size_t)V * V * 4);
+  }
   m->total = off;
 }
 
@@ -174,6 +192,11 @@ std::vector<Canon> canon_list(const evs_model_desc* d) {
     else { v.push_back({2LL * b.d_ff, D, mt}); v.push_back({D, b.d_ff, mt}); }
   }
   v.push_back({d->vocab, D, mt});
+  if (d->inject_dim > 0) {
+    v.push_back({D, d->inject_dim, mt});
+    v.push_back({d->max_slots, D, mt});
+    v.push_back({d->vocab, d->vocab, EVS_F32});
+  }
   return v;
 }
 
@@ -240,6 +263,13 @@ void layout_state(evs_state* s) {
   s->qtn_max = (s->max_block + 15) / 16;
   s->apart_floats = (size_t)B * s->qtn_max * H * s->S * 16 * (DHm + 2);
   s->w_apart = take(s->apart_floats * 4);
+  if (m->desc.inject_dim > 0) {
+    const size_t B16 = align_up((size_t)B, 16);
+    s->inj_ld = (int)B16;
+    s->w_inj_x = take(B16 * m->desc.inject_dim * 4);
+    s->w_inj_nrm = take((size_t)(m->desc.inject_dim / 16) * B16 * 4);
+    s->w_z = take(B16 * d * es);
+  }
   s->ws_total = off;
 }
 
@@ -295,9 +325,18 @@ hipError_t timed(evs_state* s, int kc, double bytes, hipStream_t st, F&& launch)
 #define HIP_TRY(x) do { if ((x) != hipSuccess) return EVS_E_HIP; } while (0)
 
 // ------------------------------------------------------------------ forward
+// where a normed GEMM finds its input rows' per-16-column sums of squares
+// (default: the forward's residual rows)
+struct NormSrc {
+  const float* part;
+  int n_part, ld;
+  float fd;
+};
+
 template <typename T>
 evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int epi, const void* A, int lda,
-                     int nseq, int P, GemmArgs a, hipStream_t st, int scratch_floats = 0) {
+                     int nseq, int P, GemmArgs a, hipStream_t st, int scratch_floats = 0,
+                     const NormSrc* ns = nullptr) {
   const Slicing sl = slicing(nseq, P);
   a.W = reinterpret_cast<const uint4*>(m->base + mat.off);
   a.ksteps = mat.K / (mat.w8 ? 2 * m->kstep : m->kstep);   // weight steps (FP8: two k-steps each)
@@ -315,10 +354,10 @@ evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int 
   a.lda = lda;
   a.M = nseq * P;
   a.rows_per_slice = sl.rows_per_slice;
-  a.nrm_part = wp<float>(s, s->w_nrm);
-  a.n_part = m->desc.d_model / 16;
-  a.nrm_ld = s->M_max;
-  a.fd = (float)m->desc.d_model;
+  a.nrm_part = ns ? ns->part : wp<float>(s, s->w_nrm);
+  a.n_part = ns ? ns->n_part : m->desc.d_model / 16;
+  a.nrm_ld = ns ? ns->ld : s->M_max;
+  a.fd = ns ? ns->fd : (float)m->desc.d_model;
   a.eps = m->desc.norm_eps;
   // algorithmic bytes: the weights once, the A rows once, the outputs once
   const double bytes = (double)(mat.bytes(m->es) + mat.scale_bytes()) + (double)a.M * mat.K * (amode == A_NORM ? 4 : m->es) +
@@ -333,17 +372,24 @@ evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int 
                       }));
 }
 
+// The forward over nseq sequences of P positions: the embedding of `tokens`
+// (or, with tokens null, input rows the caller already wrote into the
+// residual buffer with their norm partials), every block, and the LM head
+// into `logits` (if not null). With export_dst, the residual rows after block
+// s->export_block are also written out row-major.
 template <typename T>
 evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const int32_t* tokens, void* logits,
-                   hipStream_t st) {
+                   hipStream_t st, float* export_dst = nullptr) {
   const int d = m->desc.d_model, M = nseq * P;
   float* x = wp<float>(s, s->w_x);
   float* nrm = wp<float>(s, s->w_nrm);
   int* t = sp<int>(s, s->off_t);
   int* err = sp<int>(s, s->off_err);
-  HIP_TRY(launch_embed<T>(tokens, reinterpret_cast<const T*>(m->base + m->embed), x, nrm, s->M_max, M, d,
-                          m->desc.vocab, P, seq0, t, s->max_ctx, err, st));
+  if (tokens)
+    HIP_TRY(launch_embed<T>(tokens, reinterpret_cast<const T*>(m->base + m->embed), x, nrm, s->M_max, M, d,
+                            m->desc.vocab, P, seq0, t, s->max_ctx, err, st));
   for (size_t i = 0; i < m->plan.size(); ++i) {
+    if (i > 0 && export_dst && (int)i - 1 == s->export_block) HIP_TRY(launch_export_rows<T>(x, export_dst, M, d, st));
     const BlockPlan& p = m->plan[i];
     GemmArgs a{};
     if (p.d.kind == EVS_MLP) {
@@ -400,6 +446,7 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
     b.x = x; b.ldx = d; b.nrm_out = nrm;
     EVS_TRY(gemm_call<T>(m, s, p.w_out, A_ACT, E_RESID, wp<void>(s, s->w_o), d, nseq, P, b, st));
   }
+  if (export_dst && s->export_block == (int)m->plan.size() - 1) HIP_TRY(launch_export_rows<T>(x, export_dst, M, d, st));
   if (logits) {
     GemmArgs a{};
     a.N = m->desc.vocab; a.out = logits; a.ldo = m->desc.vocab;
@@ -409,9 +456,36 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
 }
 
 evs_status forward_any(evs_model* m, evs_state* s, int seq0, int nseq, int P, const int32_t* tokens, void* logits,
-                       hipStream_t st) {
-  if (storage_dtype(&m->desc) == EVS_BF16) return forward<bf16>(m, s, seq0, nseq, P, tokens, logits, st);
-  return forward<float>(m, s, seq0, nseq, P, tokens, logits, st);
+                       hipStream_t st, float* export_dst = nullptr) {
+  if (storage_dtype(&m->desc) == EVS_BF16) return forward<bf16>(m, s, seq0, nseq, P, tokens, logits, st, export_dst);
+  return forward<float>(m, s, seq0, nseq, P, tokens, logits, st, export_dst);
+}
+
+// The drafter's pass (evs_draft): injected prefix, slot rows, the drafter's
+// blocks and head over the slots, then the Markov head and draws.
+template <typename T>
+evs_status draft_pass(evs_model* m, evs_state* s, int B, const float* hidden, int hidden_rows, const int32_t* hidx,
+                      const int32_t* last, int gamma, const float* u, float temperature, int top_k, int greedy,
+                      void* logits, int32_t* drafts, float* q, hipStream_t st) {
+  const int d = m->desc.d_model, K = m->desc.inject_dim, V = m->desc.vocab;
+  int* err = sp<int>(s, s->off_err);
+  float* xin = wp<float>(s, s->w_inj_x);
+  float* inrm = wp<float>(s, s->w_inj_nrm);
+  T* z = wp<T>(s, s->w_z);
+  HIP_TRY(launch_inject_prep<T>(hidden, hidden_rows, hidx, B, K, xin, inrm, s->inj_ld, err, st));
+  GemmArgs a{};
+  a.N = d; a.out = z; a.ldo = d;
+  const NormSrc ns{inrm, K / 16, s->inj_ld, (float)K};
+  EVS_TRY(gemm_call<T>(m, s, m->inj, A_NORM, E_STORE, xin, K, B, 1, a, st, 0, &ns));
+  HIP_TRY(launch_slots<T>(reinterpret_cast<const T*>(m->base + m->embed), reinterpret_cast<const T*>(m->base + m->pos),
+                          z, last, B, gamma, d, V, wp<float>(s, s->w_x), wp<float>(s, s->w_nrm), s->M_max, err, st));
+  EVS_TRY(forward<T>(m, s, 0, B, gamma, nullptr, logits, st));
+  DraftArgs da{};
+  da.logits = logits; da.markov = reinterpret_cast<const float*>(m->base + m->markov); da.last = last; da.u = u;
+  da.gamma = gamma; da.V = V; da.top_k = top_k; da.greedy = greedy ? 1 : 0; da.temperature = temperature;
+  da.drafts = drafts; da.q = q; da.err = err;
+  HIP_TRY(launch_draft<T>(da, B, st));
+  return EVS_OK;
 }
 
 }  // namespace
@@ -509,6 +583,11 @@ evs_status evs_pack_weights(evs_model* m, const void* const* canon, void* stream
     HIP_TRY(pack(canon[k++], p.w_out));
   }
   HIP_TRY(pack(canon[k++], m->lm));
+  if (m->desc.inject_dim > 0) {
+    HIP_TRY(pack(canon[k++], m->inj));
+    HIP_TRY(copy(canon[k++], m->pos, (size_t)m->desc.max_slots * d * m->es));
+    HIP_TRY(copy(canon[k++], m->markov, (size_t)m->desc.vocab * m->desc.vocab * 4));
+  }
   return EVS_OK;
 }
 
@@ -660,7 +739,8 @@ evs_status evs_block_verify(evs_model* m, evs_state* s, const int32_t* cand, int
   if (!m || !s || !cand || !logits || s->m != m) return EVS_E_INVALID;
   if (gamma < 0 || gamma + 1 > s->max_block) return EVS_E_RANGE;
   s->pending = false;   // a pending block is discarded (rollback to 0 changes nothing on device)
-  EVS_TRY(forward_any(m, s, 0, s->B, gamma + 1, cand, logits, reinterpret_cast<hipStream_t>(stream)));
+  EVS_TRY(forward_any(m, s, 0, s->B, gamma + 1, cand, logits, reinterpret_cast<hipStream_t>(stream),
+                      s->export_block >= 0 ? s->export_dst : nullptr));
   HIP_TRY(close_span(s));
   s->pending = true;
   s->pending_P = gamma + 1;
@@ -692,6 +772,41 @@ evs_status evs_verify_sample(int32_t batch, int32_t gamma, int32_t vocab, const 
   a.temperature = temperature; a.target = target; a.q = q; a.draft = draft; a.u = u;
   a.n_acc = n_acc; a.next = next; a.n_keep = n_keep; a.err = err;
   return hip_ok(launch_verify(a, batch, reinterpret_cast<hipStream_t>(stream)));
+}
+
+evs_status evs_state_export(evs_state* s, int32_t block, float* dst) {
+  if (!s) return EVS_E_INVALID;
+  if (block < 0 || !dst) {
+    s->export_block = -1;
+    s->export_dst = nullptr;
+    return EVS_OK;
+  }
+  if (block >= (int)s->m->plan.size() || ((uintptr_t)dst % 16)) return EVS_E_INVALID;
+  s->export_block = block;
+  s->export_dst = dst;
+  return EVS_OK;
+}
+
+evs_status evs_draft(evs_model* m, evs_state* s, int32_t batch, const float* hidden, int32_t hidden_rows,
+                     const int32_t* hidden_index, const int32_t* last, int32_t gamma, const float* u,
+                     float temperature, int32_t top_k, int32_t greedy, void* logits, int32_t* drafts, float* q,
+                     void* stream) {
+  if (!m || !s || s->m != m || m->desc.inject_dim <= 0) return EVS_E_INVALID;
+  if (!hidden || hidden_rows < 1 || !last || !logits || !drafts || (!greedy && !u)) return EVS_E_INVALID;
+  if (!(temperature > 0.f)) return EVS_E_INVALID;
+  if (batch < 1 || batch > s->B || gamma < 1 || gamma > m->desc.max_slots) return EVS_E_RANGE;
+  if (gamma > s->max_block) return EVS_E_RANGE;
+  if (m->desc.vocab > 15360) return EVS_E_UNSUPPORTED;   // one fp32 row in LDS
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  evs_status r;
+  if (storage_dtype(&m->desc) == EVS_BF16)
+    r = draft_pass<bf16>(m, s, batch, hidden, hidden_rows, hidden_index, last, gamma, u, temperature, top_k, greedy,
+                         logits, drafts, q, st);
+  else
+    r = draft_pass<float>(m, s, batch, hidden, hidden_rows, hidden_index, last, gamma, u, temperature, top_k, greedy,
+                          logits, drafts, q, st);
+  HIP_TRY(close_span(s));
+  return r;
 }
 
 evs_status evs_state_timing(evs_state* s, int32_t enable, int64_t context_hint) {

@@ -163,4 +163,24 @@ hipError_t launch_pack(const T* W, uint4* out, int rows_valid, int K, int n_grou
 hipError_t launch_copy_row(const void* src, void* dst, size_t bytes, hipStream_t st);
 hipError_t launch_verify(const VerifyArgs& a, int B, hipStream_t st);
 
+struct DraftArgs {
+  const void* logits;    // [B, gamma, V] storage type: the drafter head's logits
+  const float* markov;   // [V, V]
+  const int* last;       // [B]
+  const float* u;        // [B, gamma] (unused when greedy)
+  int gamma, V, top_k, greedy;
+  float temperature;
+  int* drafts;           // [B, gamma]
+  float* q;              // [B, gamma, V] or null
+  int* err;
+};
+template <typename T> hipError_t launch_export_rows(const float* x, float* dst, int M, int d, hipStream_t st);
+template <typename T>
+hipError_t launch_inject_prep(const float* hidden, int rows, const int* index, int B, int K, float* xin, float* nrm,
+                              int nrm_ld, int* err, hipStream_t st);
+template <typename T>
+hipError_t launch_slots(const T* E, const T* pos, const T* z, const int* last, int B, int gamma, int d, int V,
+                        float* x, float* nrm, int nrm_ld, int* err, hipStream_t st);
+template <typename T> hipError_t launch_draft(const DraftArgs& a, int B, hipStream_t st);
+
 }  // namespace evs

@@ -275,6 +275,57 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   }
 }
 
+// One wave over one row of V values (NaN logits already read as -inf): returns
+// the argmax (lowest id among maxima); with soft, the row is replaced by the
+// softmax numerators of the top_k largest of z / T (ties in the cut to the
+// lower id; top_k of 0 or >= V keeps all): exp(z/T - max) for kept finite
+// entries, 0 elsewhere.
+__device__ int wave_target_row(float* pr, int V, float temperature, int top_k, bool soft) {
+  const int lane = threadIdx.x & 63;
+  float bv = -INFINITY;
+  int bi = 0;
+  for (int y = lane; y < V; y += 64) {
+    const float z = pr[y];
+    if (ord_gt(z, y, bv, bi)) { bv = z; bi = y; }
+  }
+  wave_argmax(bv, bi);
+  if (!soft) return bi;
+  // z / T, then the top-k threshold (the k-th element in the total order)
+  for (int y = lane; y < V; y += 64) pr[y] = pr[y] / temperature;
+  const bool all = top_k <= 0 || top_k >= V;
+  float tv = -INFINITY;
+  int ti = V;
+  if (!all) {
+    float pvv = INFINITY;
+    int pii = -1;
+    for (int r = 0; r < top_k; ++r) {
+      float cv = -INFINITY;
+      int ci = V;
+      for (int y = lane; y < V; y += 64) {
+        const float z = pr[y];
+        if (ord_gt(pvv, pii, z, y) && ord_gt(z, y, cv, ci)) { cv = z; ci = y; }
+      }
+      wave_argmax(cv, ci);
+      pvv = cv;
+      pii = ci;
+    }
+    tv = pvv;
+    ti = pii;
+  }
+  float m = -INFINITY;
+  for (int y = lane; y < V; y += 64) {
+    const float z = pr[y];
+    if ((all || !ord_gt(tv, ti, z, y)) && isfinite(z)) m = fmaxf(m, z);
+  }
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  for (int y = lane; y < V; y += 64) {
+    const float z = pr[y];
+    const bool keep = (all || !ord_gt(tv, ti, z, y)) && isfinite(z);
+    pr[y] = keep ? (float)exp((double)(z - m)) : 0.f;
+  }
+  return bi;
+}
+
 // the sequence's [P][V] target values into rows Vs apart, 16 loads in flight
 // per thread (NaN logits read as -inf, NaN probabilities as 0); the row and
 // column of a thread's element advance by whole steps of blockDim elements
@@ -454,49 +505,8 @@ __global__ void __launch_bounds__(64 * VERIFY_MAX_WAVES) verify_kernel(VerifyArg
   // logits the kept entries' exp(z/T - max) (zeros elsewhere)
   const bool soft = !a.greedy && logits;
   for (int i = wave; i < P; i += nw) {
-    float* pr = prob + (size_t)i * Vs;
-    float bv = -INFINITY;
-    int bi = 0;
-    for (int y = lane; y < V; y += 64) {
-      const float z = pr[y];
-      if (ord_gt(z, y, bv, bi)) { bv = z; bi = y; }
-    }
-    wave_argmax(bv, bi);
+    const int bi = wave_target_row(prob + (size_t)i * Vs, V, a.temperature, a.top_k, soft);
     if (lane == 0) amax_s[i] = bi;
-    if (!soft) continue;
-    // z / T, then the top-k threshold (the k-th element in the total order)
-    for (int y = lane; y < V; y += 64) pr[y] = pr[y] / a.temperature;
-    const bool all = a.top_k <= 0 || a.top_k >= V;
-    float tv = -INFINITY;
-    int ti = V;
-    if (!all) {
-      float pvv = INFINITY;
-      int pii = -1;
-      for (int r = 0; r < a.top_k; ++r) {
-        float cv = -INFINITY;
-        int ci = V;
-        for (int y = lane; y < V; y += 64) {
-          const float z = pr[y];
-          if (ord_gt(pvv, pii, z, y) && ord_gt(z, y, cv, ci)) { cv = z; ci = y; }
-        }
-        wave_argmax(cv, ci);
-        pvv = cv;
-        pii = ci;
-      }
-      tv = pvv;
-      ti = pii;
-    }
-    float m = -INFINITY;
-    for (int y = lane; y < V; y += 64) {
-      const float z = pr[y];
-      if ((all || !ord_gt(tv, ti, z, y)) && isfinite(z)) m = fmaxf(m, z);
-    }
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    for (int y = lane; y < V; y += 64) {
-      const float z = pr[y];
-      const bool keep = (all || !ord_gt(tv, ti, z, y)) && isfinite(z);
-      pr[y] = keep ? (float)exp((double)(z - m)) : 0.f;
-    }
   }
   __syncthreads();
   if (soft) {
@@ -574,5 +584,179 @@ hipError_t launch_verify(const VerifyArgs& a, int B, hipStream_t st) {
   verify_kernel<<<B, 64 * waves, lds, st>>>(a);
   return hipGetLastError();
 }
+
+// ---------------------------------------------------------------- drafter
+// The drafter path around the shared block forward (EvSpark preprint, abstract
+// (ii): gamma-parallel trunk, target hidden-state prefix, full-matrix Markov
+// head; model card, "Drafter checkpoints": one width-1024 layer injected from
+// target layer 27, any gamma' <= gamma an exact causal prefix).
+
+// Hidden-state export: fp32 residual rows from the forward's operand-order
+// layout to row-major [M, d], four columns per thread (the layout keeps runs of
+// E >= 4 columns of a row contiguous).
+template <int E>
+__global__ void export_rows_kernel(const float* __restrict__ x, float* __restrict__ dst, int M, int d) {
+  const int n4 = d >> 2;
+  const long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  if (idx >= (long long)M * n4) return;
+  const int m = (int)(idx / n4), c = (int)(idx % n4) * 4;
+  *reinterpret_cast<float4*>(dst + (size_t)m * d + c) = *reinterpret_cast<const float4*>(x + act_off<E>(m, c, d));
+}
+
+template <typename T>
+hipError_t launch_export_rows(const float* x, float* dst, int M, int d, hipStream_t st) {
+  const long long n = (long long)M * (d / 4);
+  export_rows_kernel<St<T>::E><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(x, dst, M, d);
+  return hipGetLastError();
+}
+template hipError_t launch_export_rows<bf16>(const float*, float*, int, int, hipStream_t);
+template hipError_t launch_export_rows<float>(const float*, float*, int, int, hipStream_t);
+
+// The injected rows: sequence b's hidden row hidden[b, index[b], :] into the
+// operand-order layout the normed GEMM reads, with its per-16-column sums of
+// squares (same order as the embedding's). Indices out of range are clamped
+// and flagged.
+template <typename T>
+__global__ void inject_prep_kernel(const float* __restrict__ hidden, int rows, const int* __restrict__ index,
+                                   int B, int K, float* xin, float* nrm, int nrm_ld, int* err) {
+  const int ntile = K / 16;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= B * ntile) return;
+  const int b = idx / ntile, tile = idx % ntile;
+  int r = index ? index[b] : 0;
+  if (r < 0 || r >= rows) {
+    if (tile == 0) atomicOr(err, 16);
+    r = r < 0 ? 0 : rows - 1;
+  }
+  const float* src = hidden + ((size_t)b * rows + r) * K + tile * 16;
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float* xr = xin + act_off<St<T>::E>(b, tile * 16 + 4 * q, K);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const float v = src[4 * q + n];
+      xr[n] = v;
+      ss = fmaf(v, v, ss);
+    }
+  }
+  nrm[(size_t)tile * nrm_ld + b] = ss;
+}
+
+template <typename T>
+hipError_t launch_inject_prep(const float* hidden, int rows, const int* index, int B, int K, float* xin, float* nrm,
+                              int nrm_ld, int* err, hipStream_t st) {
+  const int n = B * (K / 16);
+  inject_prep_kernel<T><<<(n + 255) / 256, 256, 0, st>>>(hidden, rows, index, B, K, xin, nrm, nrm_ld, err);
+  return hipGetLastError();
+}
+template hipError_t launch_inject_prep<bf16>(const float*, int, const int*, int, int, float*, float*, int, int*,
+                                             hipStream_t);
+template hipError_t launch_inject_prep<float>(const float*, int, const int*, int, int, float*, float*, int, int*,
+                                              hipStream_t);
+
+// The slot rows: x[b * gamma + i] = (embed[last_b] + pos[i]) + z[b] in fp32,
+// in the forward's layout, with their per-16-column sums of squares.
+template <typename T>
+__global__ void slots_kernel(const T* __restrict__ E, const T* __restrict__ pos, const T* __restrict__ z,
+                             const int* __restrict__ last, int B, int gamma, int d, int V, float* x, float* nrm,
+                             int nrm_ld, int* err) {
+  const int ntile = d / 16;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= B * gamma * ntile) return;
+  const int m = idx / ntile, tile = idx % ntile, b = m / gamma, i = m % gamma;
+  int tok = last[b];
+  if (tok < 0 || tok >= V) {
+    if (tile == 0 && i == 0) atomicOr(err, 1);
+    tok = 0;
+  }
+  const T* e = E + (size_t)tok * d + tile * 16;
+  const T* p = pos + (size_t)i * d + tile * 16;
+  const T* zz = z + (size_t)b * d + tile * 16;
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float* xr = x + act_off<St<T>::E>(m, tile * 16 + 4 * q, d);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int c = 4 * q + n;
+      const float v = (to_f(e[c]) + to_f(p[c])) + to_f(zz[c]);
+      xr[n] = v;
+      ss = fmaf(v, v, ss);
+    }
+  }
+  nrm[(size_t)tile * nrm_ld + m] = ss;
+}
+
+template <typename T>
+hipError_t launch_slots(const T* E, const T* pos, const T* z, const int* last, int B, int gamma, int d, int V,
+                        float* x, float* nrm, int nrm_ld, int* err, hipStream_t st) {
+  const int n = B * gamma * (d / 16);
+  slots_kernel<T><<<(n + 255) / 256, 256, 0, st>>>(E, pos, z, last, B, gamma, d, V, x, nrm, nrm_ld, err);
+  return hipGetLastError();
+}
+template hipError_t launch_slots<bf16>(const bf16*, const bf16*, const bf16*, const int*, int, int, int, int, float*,
+                                       float*, int, int*, hipStream_t);
+template hipError_t launch_slots<float>(const float*, const float*, const float*, const int*, int, int, int, int,
+                                        float*, float*, int, int*, hipStream_t);
+
+// Markov head and draws: one wave per sequence, the slots one after another
+// (each adds the Markov row of the previous draft). Per slot: l' = fp32(l) +
+// markov[prev] (NaN read as -inf), its argmax and top-k softmax numerators
+// (wave_target_row), the normaliser summed by one lane in token order, q = e /
+// S, then the draw: the argmax in greedy mode, else the inverse CDF of q with
+// the slot's uniform (running sums by one lane, searched by the wave).
+template <typename T>
+__global__ void __launch_bounds__(64) draft_kernel(DraftArgs a) {
+  extern __shared__ float4 dsm4[];
+  float* row = reinterpret_cast<float*>(dsm4);   // [Vr]
+  __shared__ DrawShared draw_s;
+  __shared__ float ssum_s;
+  const int b = blockIdx.x, lane = threadIdx.x, V = a.V, Vr = (V + 3) & ~3;
+  const T* lg = reinterpret_cast<const T*>(a.logits);
+  int prev = a.last[b];
+  if (prev < 0 || prev >= V) {
+    if (lane == 0) atomicOr(a.err, 1);
+    prev = 0;
+  }
+  for (int i = 0; i < a.gamma; ++i) {
+    const size_t ro = ((size_t)b * a.gamma + i) * V;
+    const float* mk = a.markov + (size_t)prev * V;
+    for (int y = lane; y < V; y += 64) {
+      const float v = to_f(lg[ro + y]) + mk[y];
+      row[y] = isnan(v) ? -INFINITY : v;
+    }
+    for (int y = V + lane; y < Vr; y += 64) row[y] = 0.f;   // the previous draw left running sums there
+    __syncthreads();
+    const int amax = wave_target_row(row, V, a.temperature, a.top_k, true);
+    __syncthreads();
+    if (lane == 0) ssum_s = row_sum(row, Vr);
+    __syncthreads();
+    const float S = ssum_s;
+    for (int y = lane; y < V; y += 64) {
+      const float p = (S > 0.f) ? row[y] / S : 0.f;
+      row[y] = p;
+      if (a.q) a.q[ro + y] = p;
+    }
+    __syncthreads();
+    int d = amax;
+    if (!a.greedy) {
+      float tot;
+      d = draw_row(row, V, Vr, a.u[(size_t)b * a.gamma + i], false, amax, tot, draw_s);
+    }
+    if (lane == 0) a.drafts[(size_t)b * a.gamma + i] = d;
+    prev = d;
+    __syncthreads();
+  }
+}
+
+template <typename T>
+hipError_t launch_draft(const DraftArgs& a, int B, hipStream_t st) {
+  const size_t lds = (size_t)((a.V + 3) & ~3) * sizeof(float);
+  draft_kernel<T><<<B, 64, lds, st>>>(a);
+  return hipGetLastError();
+}
+template hipError_t launch_draft<bf16>(const DraftArgs&, int, hipStream_t);
+template hipError_t launch_draft<float>(const DraftArgs&, int, hipStream_t);
 
 }  // namespace evs

@@ -21,7 +21,7 @@ EVS_FIR, EVS_IIR, EVS_ATTN, EVS_MLP = 1, 2, 3, 4
 EVS_BF16, EVS_F32, EVS_I32, EVS_BF16_FP8W = 1, 2, 3, 4
 EVS_TARGET_LOGITS_BF16, EVS_TARGET_LOGITS_F32, EVS_TARGET_PROBS_F32 = 1, 2, 3
 EVS_ST_T, EVS_ST_IIR_BUF, EVS_ST_IIR_SLOT, EVS_ST_FIR_RING, EVS_ST_IIR, EVS_ST_K, EVS_ST_VT, EVS_ST_ERROR = range(1, 9)
-EVS_ERR_TOKEN, EVS_ERR_CONTEXT, EVS_ERR_NKEEP, EVS_ERR_DRAFT = 1, 2, 4, 8
+EVS_ERR_TOKEN, EVS_ERR_CONTEXT, EVS_ERR_NKEEP, EVS_ERR_DRAFT, EVS_ERR_INDEX = 1, 2, 4, 8, 16
 STATUS = {0: "EVS_OK", -1: "EVS_E_INVALID", -2: "EVS_E_RANGE", -3: "EVS_E_STATE", -4: "EVS_E_HIP",
           -5: "EVS_E_UNSUPPORTED"}
 _KINDS = {"fir": EVS_FIR, "iir": EVS_IIR, "attn": EVS_ATTN, "mlp": EVS_MLP}
@@ -31,7 +31,8 @@ _TORCH_DT = {EVS_BF16: torch.bfloat16, EVS_F32: torch.float32, EVS_I32: torch.in
 EXPORTS = ("evs_status_string", "evs_canonical_count", "evs_canonical_shape", "evs_weights_bytes",
            "evs_model_create", "evs_pack_weights", "evs_model_destroy", "evs_state_bytes", "evs_state_create",
            "evs_state_destroy", "evs_state_tensor", "evs_state_error", "evs_prefill", "evs_block_verify",
-           "evs_rollback", "evs_verify_sample", "evs_state_timing", "evs_state_timing_read")
+           "evs_rollback", "evs_verify_sample", "evs_state_export", "evs_draft", "evs_state_timing",
+           "evs_state_timing_read")
 EVS_KC_GEMM, EVS_KC_ATTN = 1, 2
 
 
@@ -48,7 +49,8 @@ class BlockDesc(ctypes.Structure):
 
 class ModelDesc(ctypes.Structure):
     _fields_ = [("d_model", c_int32), ("vocab", c_int32), ("n_blocks", c_int32), ("dtype", c_int32),
-                ("norm_eps", c_float), ("blocks", POINTER(BlockDesc))]
+                ("norm_eps", c_float), ("blocks", POINTER(BlockDesc)), ("inject_dim", c_int32),
+                ("max_slots", c_int32)]
 
 
 class TensorDesc(ctypes.Structure):
@@ -87,6 +89,9 @@ def lib():
                                   POINTER(ctypes.c_double), c_void_p],
         "evs_verify_sample": [c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_float,
                               c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
+        "evs_state_export": [c_void_p, c_int32, c_void_p],
+        "evs_draft": [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p,
+                      c_float, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -132,7 +137,8 @@ def model_desc(cfg, fp8_weights=False):
     if fp8_weights and cfg.dtype != "bf16":
         raise ValueError("FP8 weights are a variant of bf16 models")
     dt = EVS_BF16_FP8W if fp8_weights else (EVS_BF16 if cfg.dtype == "bf16" else EVS_F32)
-    d = ModelDesc(cfg.d_model, cfg.vocab, len(cfg.blocks), dt, float(cfg.norm_eps), blocks)
+    d = ModelDesc(cfg.d_model, cfg.vocab, len(cfg.blocks), dt, float(cfg.norm_eps), blocks,
+                  int(getattr(cfg, "inject_dim", 0)), int(getattr(cfg, "max_slots", 0)))
     d._keep = blocks
     return d
 
@@ -149,7 +155,10 @@ def canonical_order(cfg):
             names += [f"b{i}.w_in", f"b{i}.w_out"]
         else:
             names += [f"b{i}.w_gu", f"b{i}.w_down"]
-    return names + ["lm_head"]
+    names.append("lm_head")
+    if getattr(cfg, "inject_dim", 0):
+        names += ["inject", "pos", "markov"]
+    return names
 
 
 class Model:
@@ -267,6 +276,19 @@ def evs_verify_sample(batch, gamma, vocab, target, target_kind, q, draft, u, tem
                                    _ptr(draft), _ptr(u), float(temperature), int(top_k), int(greedy),
                                    _ptr(n_accepted), _ptr(next_token), _ptr(n_keep), _ptr(error), _stream()),
            "evs_verify_sample")
+
+
+def evs_state_export(state: State, block: int, dst=None):
+    """Export the residual rows after `block` during evs_block_verify into dst
+    (f32 [B, max_block, d]); block -1 turns the export off."""
+    _check(lib().evs_state_export(state.handle, int(block), _ptr(dst)), "evs_state_export")
+
+
+def evs_draft(drafter: Model, dstate: State, batch, hidden, hidden_rows, hidden_index, last, gamma, u,
+              temperature, top_k, greedy, logits, drafts, q=None):
+    _check(lib().evs_draft(drafter.handle, dstate.handle, int(batch), _ptr(hidden), int(hidden_rows),
+                           _ptr(hidden_index), _ptr(last), int(gamma), _ptr(u), float(temperature), int(top_k),
+                           int(greedy), _ptr(logits), _ptr(drafts), _ptr(q), _stream()), "evs_draft")
 
 
 def status_string(status: int) -> str:

@@ -64,7 +64,7 @@ enum { EVS_BF16 = 1, EVS_F32 = 2, EVS_I32 = 3, EVS_BF16_FP8W = 4 };
 /* target kinds for evs_verify_sample */
 enum { EVS_TARGET_LOGITS_BF16 = 1, EVS_TARGET_LOGITS_F32 = 2, EVS_TARGET_PROBS_F32 = 3 };
 /* sticky error-word bits */
-enum { EVS_ERR_TOKEN = 1, EVS_ERR_CONTEXT = 2, EVS_ERR_NKEEP = 4, EVS_ERR_DRAFT = 8 };
+enum { EVS_ERR_TOKEN = 1, EVS_ERR_CONTEXT = 2, EVS_ERR_NKEEP = 4, EVS_ERR_DRAFT = 8, EVS_ERR_INDEX = 16 };
 
 /* One residual block (pre-norm). FIR: causal depthwise filter of fir_len
  * taps on h = k*v (state: the last fir_len-1 inputs). IIR: diagonal real modal
@@ -77,11 +77,17 @@ typedef struct {
 } evs_block_desc;
 
 /* d_model and every d_ff are multiples of 32 (of 64 for EVS_BF16_FP8W);
- * vocab >= 2. */
+ * vocab >= 2. inject_dim > 0 makes the model a drafter (EvSpark preprint,
+ * abstract (ii); model card, "Drafter checkpoints"): its input rows are built
+ * from an injected target hidden state of inject_dim (a multiple of 32)
+ * columns, a token embedding and max_slots (1..64) position embeddings, and a
+ * full [V, V] Markov matrix follows its head (see evs_draft). Drafters are
+ * EVS_BF16 or EVS_F32. inject_dim = max_slots = 0 for a plain model. */
 typedef struct {
   int32_t d_model, vocab, n_blocks, dtype;
   float norm_eps;
   const evs_block_desc* blocks;
+  int32_t inject_dim, max_slots;
 } evs_model_desc;
 
 typedef struct evs_model evs_model;
@@ -123,8 +129,9 @@ const char* evs_status_string(evs_status s);
  *              IIR  w_in [3d, d], lam [d, N] (f32), res [d, N] (f32), w_out [d, d];
  *              ATTN w_in [3d, d] (rows: q, k, v), w_out [d, d];
  *              MLP  w_gu [2 d_ff, d] (gate rows first), w_down [d, d_ff];
- *   lm_head [V, d].
- * Matrices are in the storage type; taps/lam/res are always f32. */
+ *   lm_head [V, d];
+ *   drafters only: inject [d, inject_dim], pos [max_slots, d], markov [V, V] (f32).
+ * Matrices are in the storage type; taps/lam/res/markov are always f32. */
 evs_status evs_canonical_count(const evs_model_desc* desc, int32_t* count);
 evs_status evs_canonical_shape(const evs_model_desc* desc, int32_t i, int64_t* rows,
                                int64_t* cols, int32_t* dtype);
@@ -223,6 +230,45 @@ evs_status evs_verify_sample(int32_t batch, int32_t gamma, int32_t vocab, const 
                              const float* u_dev, float temperature, int32_t top_k, int32_t greedy,
                              int32_t* n_accepted_dev, int32_t* next_token_dev,
                              int32_t* n_keep_dev, int32_t* error_dev, void* stream);
+
+/* ---------------------------------------------------------------- drafter */
+
+/* Hidden-state export for a drafter's prefix (EvSpark preprint, abstract
+ * (ii): the drafter reads the target's hidden state; model card, "Drafter
+ * checkpoints": injected from layer 27). From now on, every evs_block_verify
+ * on `s` also writes the fp32 residual rows after block `block` (0-based
+ * index into the descriptor's blocks; for a [mixer, MLP] layer stack, layer L
+ * ends at block 2L + 1) to dst_dev [B, gamma+1, d] (row-major f32; row i of
+ * sequence b is candidate position i). block = -1 (dst_dev NULL) turns it off.
+ * dst_dev must hold B * max_block * d floats and outlive its use. */
+evs_status evs_state_export(evs_state* s, int32_t block, float* dst_dev);
+
+/* Draft gamma tokens for each of B sequences with a drafter model (inject_dim
+ * > 0) and its own state `ds` (created for this drafter with batch >= B and
+ * max_block >= gamma; never committed: the slots always start at position 0).
+ * Steps:
+ *   h_b   = hidden_dev[b, idx_b, :] (f32 [B, hidden_rows, inject_dim];
+ *           idx_b = hidden_index_dev[b], or 0 if that is NULL; an index outside
+ *           0 .. hidden_rows-1 is clamped and sets EVS_ERR_INDEX);
+ *   z_b   = rmsnorm(h_b) inject^T, rounded to the storage type;
+ *   x_b,i = (embed[last_b] + pos[i]) + z_b for the slots i = 0 .. gamma-1
+ *           (last_dev [B] i32: the token each sequence continues from; out of
+ *           range reads as 0 and sets EVS_ERR_TOKEN);
+ *   the drafter's blocks over the slots (causal), final norm and head -> l_b,i
+ *   (written to logits_dev [B, gamma, V], storage type);
+ *   Markov head and draws, one slot after another: l' = fp32(l_b,i) +
+ *   markov[prev], prev = last_b then each draft; q_b,i = softmax of the top_k
+ *   largest of l' / temperature (ties to the lower id; 0 keeps all) with the
+ *   verifier's fp32 arithmetic; the draft is the inverse-CDF draw of q_b,i
+ *   with u_dev[b, i] (f32 [B, gamma]; the argmax of l' if q has no positive
+ *   entry), or the argmax of l' (lowest id) when greedy != 0 (u unused).
+ * Outputs: drafts_dev [B, gamma] i32, q_dev [B, gamma, V] f32 (may be NULL).
+ * 1 <= gamma <= max_slots; V <= 15360; errors go to the drafter state's word.
+ * The drafter state's timing covers its GEMM and attention launches. */
+evs_status evs_draft(evs_model* drafter, evs_state* ds, int32_t batch, const float* hidden_dev,
+                     int32_t hidden_rows, const int32_t* hidden_index_dev, const int32_t* last_dev,
+                     int32_t gamma, const float* u_dev, float temperature, int32_t top_k, int32_t greedy,
+                     void* logits_dev, int32_t* drafts_dev, float* q_dev, void* stream);
 
 /* ------------------------------------------------------------ measurement */
 

@@ -1,0 +1,138 @@
+"""GPU parity of the drafter path: the target's hidden-state export, the
+drafter's injected prefix, slots, trunk and head (evs_draft) against the
+oracle drafter, the Markov draws bit for bit on the same logits, the exact
+causal prefix, and the device-side index check."""
+import numpy as np
+import pytest
+import torch
+
+import evs_synth as es
+from oracle import HybridLM
+from oracle.drafter import Drafter
+
+from gpu_util import DEV, block_verify, make_engine, prefill, rollback
+from attention_dna_lms_amd import evs
+
+pytestmark = pytest.mark.gpu
+
+LOGIT_ATOL = 2e-2
+
+
+def logit_err(a, b):
+    """Largest |a - b| beyond one bf16 quantum of b (values are stored in bf16)."""
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(b))[1] - 8)
+    return float(np.max(np.abs(a - b) - ulp))
+
+
+def test_hidden_export_matches_oracle_and_sequential_steps():
+    """Residual rows after block 11 (layer 5's MLP) of the 8-layer stack,
+    exported during a 13-candidate block verify: against the oracle's block
+    form, and bit for bit against the same rows exported by 13 single-token
+    verifies (the forward is batch invariant)."""
+    cfg = es.small_stack()
+    w = es.make_weights(cfg, seed=51)
+    prompt = es.prompt_tokens(cfg, 40, seed=52)[0]
+    cand = es.prompt_tokens(cfg, 13, seed=53)[0]
+    blk = 11
+    model, state = make_engine(cfg, w, batch=1, max_ctx=128, max_block=16)
+    prefill(model, state, [prompt])
+    dst = torch.full((1, 16, cfg.d_model), float("nan"), device=DEV)
+    evs.evs_state_export(state, blk, dst)
+    block_verify(model, state, cand[None])
+    ex = dst[0, :13].double().cpu().numpy()
+    orc = HybridLM(cfg, w)
+    _, ost = orc.prefill(prompt, chunk=16)
+    ref = orc.block(ost, cand, keep_x=True).x_out[blk]
+    assert np.max(np.abs(ex - ref)) < LOGIT_ATOL * max(1.0, float(np.max(np.abs(ref)))), np.max(np.abs(ex - ref))
+    m2, s2 = make_engine(cfg, w, batch=1, max_ctx=128, max_block=16)
+    prefill(m2, s2, [prompt])
+    one = torch.full((1, 16, cfg.d_model), float("nan"), device=DEV)
+    evs.evs_state_export(s2, blk, one)
+    for k in range(13):
+        block_verify(m2, s2, cand[None, k:k + 1])
+        assert torch.equal(one[0, 0], dst[0, k]), k
+        rollback(s2, [1])
+    evs.evs_state_export(s2, -1)
+    assert state.error() == 0 and s2.error() == 0
+
+
+def _drafter(seed=61, B=2):
+    cfg = es.drafter_1024()
+    w = es.make_weights(cfg, seed=seed)
+    model = evs.Model(cfg, w, device=DEV)
+    state = evs.State(model, B, cfg.max_slots, cfg.max_slots, device=DEV)
+    torch.cuda.synchronize()
+    return cfg, w, model, state
+
+
+def _hidden(B, rows, K, seed):
+    h = es.rng_for(seed, "hidden").standard_normal((B, rows, K)).astype(np.float32)
+    h[1] *= 1e11                 # the residual scale the pages report for the last target blocks
+    return h
+
+
+def _run(model, state, B, h, idx, last, gamma, u, T, top_k, greedy):
+    V = model.cfg.vocab
+    lg = torch.empty(B, gamma, V, dtype=torch.bfloat16, device=DEV)
+    dr = torch.full((B, gamma), -7, dtype=torch.int32, device=DEV)
+    q = torch.full((B, gamma, V), float("nan"), device=DEV)
+    evs.evs_draft(model, state, B, torch.as_tensor(h).to(DEV), h.shape[1],
+                  None if idx is None else torch.as_tensor(np.asarray(idx, np.int32)).to(DEV),
+                  torch.as_tensor(np.asarray(last, np.int32)).to(DEV), gamma,
+                  None if u is None else torch.as_tensor(u).to(DEV), T, top_k, greedy, lg, dr, q)
+    torch.cuda.synchronize()
+    return lg.double().cpu().numpy(), dr.cpu().numpy(), q.cpu().numpy()
+
+
+def test_drafter_matches_oracle_and_draws_bitexact():
+    """d = 1024 drafter (one attention 8 x 128 + gated-MLP layer), a 4096-wide
+    injected prefix (one sequence's hidden row at 1e11 scale), gamma = 12:
+    head logits against the oracle drafter; drafts and q bit for bit against
+    the oracle's Markov head and draws on the GPU's own logits (sampling at
+    T = 1 with top-4, and greedy)."""
+    B, gamma = 2, 12
+    cfg, w, model, state = _drafter()
+    h = _hidden(B, 3, cfg.inject_dim, 62)
+    idx, last = [2, 0], [65, 84]
+    u = es.uniforms((B, gamma), seed=63)
+    lg, dr, q = _run(model, state, B, h, idx, last, gamma, u, 1.0, 4, 0)
+    orc = Drafter(cfg, w)
+    for b in range(B):
+        ref = orc.trunk_logits(h[b, idx[b]].astype(np.float64), last[b], gamma)
+        err = logit_err(lg[b], ref)
+        assert err < LOGIT_ATOL, (b, err)
+        d_ref, q_ref = orc.draft(lg[b], last[b], u[b], 1.0, 4)
+        assert np.array_equal(dr[b], d_ref), b
+        assert np.array_equal(q[b], q_ref), b
+    lg2, dr2, _ = _run(model, state, B, h, idx, last, gamma, None, 1.0, 0, 1)
+    assert np.array_equal(lg2, lg)
+    for b in range(B):
+        d_ref, _ = orc.draft(lg2[b], last[b], greedy=True)
+        assert np.array_equal(dr2[b], d_ref), b
+    assert state.error() == 0
+
+
+def test_drafter_exact_causal_prefix_on_gpu():
+    """A shorter draft is an exact prefix of a longer one: logits rows and
+    drafts of gamma = 5 equal the first 5 of gamma = 12 bit for bit."""
+    B = 2
+    cfg, w, model, state = _drafter(seed=64)
+    h = _hidden(B, 1, cfg.inject_dim, 65)
+    u = es.uniforms((B, 12), seed=66)
+    lg12, d12, q12 = _run(model, state, B, h, None, [71, 67], 12, u, 0.8, 0, 0)
+    lg5, d5, q5 = _run(model, state, B, h, None, [71, 67], 5, u[:, :5].copy(), 0.8, 0, 0)
+    assert np.array_equal(lg12[:, :5], lg5)
+    assert np.array_equal(d12[:, :5], d5)
+    assert np.array_equal(q12[:, :5], q5)
+
+
+def test_hidden_index_out_of_range_is_clamped_and_flagged():
+    B = 2
+    cfg, w, model, state = _drafter(seed=67)
+    h = _hidden(B, 3, cfg.inject_dim, 68)
+    a = _run(model, state, B, h, [5, -1], [65, 65], 4, None, 1.0, 0, 1)
+    assert state.error(clear=True) == evs.EVS_ERR_INDEX
+    b = _run(model, state, B, h, [2, 0], [65, 65], 4, None, 1.0, 0, 1)
+    assert state.error() == 0
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
