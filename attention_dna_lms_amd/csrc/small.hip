@@ -266,13 +266,82 @@ __device__ __forceinline__ bool ord_gt(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
+// Wave-wide reductions with every lane of the wave active: DPP steps inside
+// each row of 16 lanes (lane ^ 1, lane ^ 2, then the mirrors within 8 and
+// within 16 lanes, after which every lane of a row holds the row's result),
+// then the four rows' results read as scalars and combined in every lane.
+// The operations are exact and order-independent (a maximum in a total
+// order), so the result is the same as any other reduction order.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+
+template <int CTRL> __device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, x)));
+}
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+template <int CTRL> __device__ __forceinline__ void argmax_dpp(float& v, int& i) {
+  const float v2 = dpp_f<CTRL>(v);
+  const int i2 = dpp_i<CTRL>(i);
+  if (ord_gt(v2, i2, v, i)) { v = v2; i = i2; }
+}
+
+// (value, index) maximum in the total order of ord_gt, in every lane
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_dpp<DPP_XOR1>(v, i);
+  argmax_dpp<DPP_XOR2>(v, i);
+  argmax_dpp<DPP_HALF_MIRROR>(v, i);
+  argmax_dpp<DPP_MIRROR>(v, i);
+  float bv = lane_f(v, 0);
+  int bi = __builtin_amdgcn_readlane(i, 0);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float v2 = __shfl_xor(v, off);
-    const int i2 = __shfl_xor(i, off);
-    if (ord_gt(v2, i2, v, i)) { v = v2; i = i2; }
+  for (int r = 1; r < 4; ++r) {
+    const float v2 = lane_f(v, 16 * r);
+    const int i2 = __builtin_amdgcn_readlane(i, 16 * r);
+    if (ord_gt(v2, i2, bv, bi)) { bv = v2; bi = i2; }
   }
+  v = bv;
+  i = bi;
+}
+
+// maximum of non-NaN values, in every lane
+__device__ __forceinline__ float wave_fmax(float m) {
+  m = fmaxf(m, dpp_f<DPP_XOR1>(m));
+  m = fmaxf(m, dpp_f<DPP_XOR2>(m));
+  m = fmaxf(m, dpp_f<DPP_HALF_MIRROR>(m));
+  m = fmaxf(m, dpp_f<DPP_MIRROR>(m));
+  return fmaxf(fmaxf(lane_f(m, 0), lane_f(m, 16)), fmaxf(lane_f(m, 32), lane_f(m, 48)));
+}
+
+// integer maximum / minimum, in every lane
+__device__ __forceinline__ int wave_imax(int x) {
+  x = max(x, dpp_i<DPP_XOR1>(x));
+  x = max(x, dpp_i<DPP_XOR2>(x));
+  x = max(x, dpp_i<DPP_HALF_MIRROR>(x));
+  x = max(x, dpp_i<DPP_MIRROR>(x));
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+__device__ __forceinline__ int wave_imin(int x) {
+  x = min(x, dpp_i<DPP_XOR1>(x));
+  x = min(x, dpp_i<DPP_XOR2>(x));
+  x = min(x, dpp_i<DPP_HALF_MIRROR>(x));
+  x = min(x, dpp_i<DPP_MIRROR>(x));
+  return min(min(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+// LDS visibility between the lanes of one wave: a wave's LDS operations are
+// performed in order, so only the compiler has to keep them in program order
+// (no wait for outstanding global stores, unlike a workgroup barrier)
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // One wave over one row of V values (NaN logits already read as -inf): returns
@@ -317,7 +386,7 @@ __device__ int wave_target_row(float* pr, int V, float temperature, int top_k, b
     const float z = pr[y];
     if ((all || !ord_gt(tv, ti, z, y)) && isfinite(z)) m = fmaxf(m, z);
   }
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  m = wave_fmax(m);
   for (int y = lane; y < V; y += 64) {
     const float z = pr[y];
     const bool keep = (all || !ord_gt(tv, ti, z, y)) && isfinite(z);
@@ -434,8 +503,7 @@ __device__ int draw_row(float* row, int V, int Vr, float u, bool scale_u, int fa
     int last = -1;
     for (int y = tid; y < V; y += 64)
       if (row[y] > 0.f) last = y;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) last = max(last, __shfl_xor(last, off));
+    last = wave_imax(last);
     if (tid == 0) {
       sh.last = last;
       sh.sum = prefix_in_place(row, Vr);
@@ -448,8 +516,7 @@ __device__ int draw_row(float* row, int V, int Vr, float u, bool scale_u, int fa
     int first = V;
     for (int y = tid; y < V; y += 64)
       if (row[y] > t) { first = y; break; }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) first = min(first, __shfl_xor(first, off));
+    first = wave_imin(first);
     if (tid == 0) sh.first = first;
   }
   __syncthreads();
@@ -702,10 +769,17 @@ template hipError_t launch_slots<float>(const float*, const float*, const float*
 
 // Markov head and draws: one wave per sequence, the slots one after another
 // (each adds the Markov row of the previous draft). Per slot: l' = fp32(l) +
-// markov[prev] (NaN read as -inf), its argmax and top-k softmax numerators
-// (wave_target_row), the normaliser summed by one lane in token order, q = e /
-// S, then the draw: the argmax in greedy mode, else the inverse CDF of q with
-// the slot's uniform (running sums by one lane, searched by the wave).
+// markov[prev] (NaN read as -inf) and its argmax; then q = the softmax of the
+// top_k largest of z = l' / T and the draw (the argmax in greedy mode, else the
+// inverse CDF of q at the slot's uniform), with the verifier's arithmetic.
+// With 0 < top_k <= DRAFT_TOPK_MAX (< V) the kept entries are found by top_k
+// wave passes and everything after runs on them alone, in token order: the
+// other entries of q are zero, and adding a zero leaves every sequential sum
+// and running sum unchanged, so the normaliser, q and the draw equal the
+// full-row evaluation exactly. Otherwise the full row goes through
+// wave_target_row, one lane's normaliser and draw_row.
+constexpr int DRAFT_TOPK_MAX = 16;
+
 template <typename T>
 __global__ void __launch_bounds__(64) draft_kernel(DraftArgs a) {
   extern __shared__ float4 dsm4[];
@@ -713,6 +787,7 @@ __global__ void __launch_bounds__(64) draft_kernel(DraftArgs a) {
   __shared__ DrawShared draw_s;
   __shared__ float ssum_s;
   const int b = blockIdx.x, lane = threadIdx.x, V = a.V, Vr = (V + 3) & ~3;
+  const bool sparse = a.top_k > 0 && a.top_k <= DRAFT_TOPK_MAX && a.top_k < V;
   const T* lg = reinterpret_cast<const T*>(a.logits);
   int prev = a.last[b];
   if (prev < 0 || prev >= V) {
@@ -727,33 +802,321 @@ __global__ void __launch_bounds__(64) draft_kernel(DraftArgs a) {
       row[y] = isnan(v) ? -INFINITY : v;
     }
     for (int y = V + lane; y < Vr; y += 64) row[y] = 0.f;   // the previous draw left running sums there
-    __syncthreads();
-    const int amax = wave_target_row(row, V, a.temperature, a.top_k, true);
-    __syncthreads();
-    if (lane == 0) ssum_s = row_sum(row, Vr);
-    __syncthreads();
-    const float S = ssum_s;
-    for (int y = lane; y < V; y += 64) {
-      const float p = (S > 0.f) ? row[y] / S : 0.f;
-      row[y] = p;
-      if (a.q) a.q[ro + y] = p;
-    }
-    __syncthreads();
-    int d = amax;
-    if (!a.greedy) {
-      float tot;
-      d = draw_row(row, V, Vr, a.u[(size_t)b * a.gamma + i], false, amax, tot, draw_s);
+    wave_sync();
+    const float u = a.greedy ? 0.f : a.u[(size_t)b * a.gamma + i];
+    int d;
+    if (sparse) {
+      float bv = -INFINITY;
+      int amax = 0;
+      for (int y = lane; y < V; y += 64) {
+        const float z = row[y];
+        if (ord_gt(z, y, bv, amax)) { bv = z; amax = y; }
+      }
+      wave_argmax(bv, amax);
+      for (int y = lane; y < V; y += 64) row[y] = row[y] / a.temperature;
+      wave_sync();
+      // the kept entries in value order (all lanes hold the same values)
+      float kv[DRAFT_TOPK_MAX];
+      int ki[DRAFT_TOPK_MAX];
+      float pvv = INFINITY;
+      int pii = -1;
+#pragma unroll
+      for (int r = 0; r < DRAFT_TOPK_MAX; ++r) {
+        kv[r] = -INFINITY;
+        ki[r] = V;
+        if (r < a.top_k) {
+          float cv = -INFINITY;
+          int ci = V;
+          for (int y = lane; y < V; y += 64) {
+            const float z = row[y];
+            if (ord_gt(pvv, pii, z, y) && ord_gt(z, y, cv, ci)) { cv = z; ci = y; }
+          }
+          wave_argmax(cv, ci);
+          kv[r] = cv;
+          ki[r] = ci;
+          pvv = cv;
+          pii = ci;
+        }
+      }
+      // softmax numerators of the finite kept entries, then token order
+      float m = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < DRAFT_TOPK_MAX; ++r)
+        if (r < a.top_k && isfinite(kv[r])) m = fmaxf(m, kv[r]);
+      float e[DRAFT_TOPK_MAX];
+#pragma unroll
+      for (int r = 0; r < DRAFT_TOPK_MAX; ++r)
+        e[r] = (r < a.top_k && isfinite(kv[r])) ? (float)exp((double)(kv[r] - m)) : 0.f;
+#pragma unroll
+      for (int r = 1; r < DRAFT_TOPK_MAX; ++r)
+#pragma unroll
+        for (int t = DRAFT_TOPK_MAX - 1; t >= r; --t)
+          if (ki[t] < ki[t - 1]) {
+            const int xi = ki[t]; ki[t] = ki[t - 1]; ki[t - 1] = xi;
+            const float xe = e[t]; e[t] = e[t - 1]; e[t - 1] = xe;
+          }
+      float S = 0.f;
+#pragma unroll
+      for (int r = 0; r < DRAFT_TOPK_MAX; ++r) S = S + e[r];
+      float p[DRAFT_TOPK_MAX];
+#pragma unroll
+      for (int r = 0; r < DRAFT_TOPK_MAX; ++r) p[r] = (S > 0.f) ? e[r] / S : 0.f;
+      if (a.q) {
+        for (int y = lane; y < V; y += 64) {
+          float v = 0.f;
+#pragma unroll
+          for (int r = 0; r < DRAFT_TOPK_MAX; ++r) v = (ki[r] == y) ? p[r] : v;
+          a.q[ro + y] = v;
+        }
+      }
+      d = amax;
+      if (!a.greedy) {
+        // first kept entry (token order) whose running sum exceeds u; with a
+        // negative u that is token 0 (the running sum starts at 0)
+        int hit = -1, last = -1;
+        float c = 0.f;
+#pragma unroll
+        for (int r = 0; r < DRAFT_TOPK_MAX; ++r) {
+          if (ki[r] < V) {
+            c = c + p[r];
+            if (p[r] > 0.f) last = ki[r];
+            if (hit < 0 && c > u) hit = ki[r];
+          }
+        }
+        d = u < 0.f ? 0 : (hit >= 0 ? hit : (last >= 0 ? last : amax));
+      }
+    } else {
+      const int amax = wave_target_row(row, V, a.temperature, a.top_k, true);
+      wave_sync();
+      if (lane == 0) ssum_s = row_sum(row, Vr);
+      wave_sync();
+      const float S = ssum_s;
+      for (int y = lane; y < V; y += 64) {
+        const float pv = (S > 0.f) ? row[y] / S : 0.f;
+        row[y] = pv;
+        if (a.q) a.q[ro + y] = pv;
+      }
+      wave_sync();
+      d = amax;
+      if (!a.greedy) {
+        float tot;
+        d = draw_row(row, V, Vr, u, false, amax, tot, draw_s);
+      }
     }
     if (lane == 0) a.drafts[(size_t)b * a.gamma + i] = d;
     prev = d;
-    __syncthreads();
+    wave_sync();
+  }
+}
+
+// The same computation for V <= 64 * NPL with each lane's NPL entries (tokens
+// lane + 64 k) held in registers: both rows are loaded NPL-wide at once, and
+// the argmax, the top-k passes, the exps and q need no LDS round trips. The
+// sequential sums of the full-row path still go through LDS (one lane walks
+// the row in token order); the kept-set path needs none.
+template <typename T, int NPL>
+__global__ void __launch_bounds__(64) draft_reg_kernel(DraftArgs a) {
+  extern __shared__ float4 dsm4[];
+  float* row = reinterpret_cast<float*>(dsm4);   // [Vr] (full-row path)
+  __shared__ DrawShared draw_s;
+  __shared__ float ssum_s;
+  const int b = blockIdx.x, lane = threadIdx.x, V = a.V, Vr = (V + 3) & ~3;
+  const bool sparse = a.top_k > 0 && a.top_k <= DRAFT_TOPK_MAX && a.top_k < V;
+  const bool all = a.top_k <= 0 || a.top_k >= V;
+  const T* lg = reinterpret_cast<const T*>(a.logits);
+  int prev = a.last[b];
+  if (prev < 0 || prev >= V) {
+    if (lane == 0) atomicOr(a.err, 1);
+    prev = 0;
+  }
+  for (int i = 0; i < a.gamma; ++i) {
+    const size_t ro = ((size_t)b * a.gamma + i) * V;
+    const float* mk = a.markov + (size_t)prev * V;
+    float lv[NPL], mv[NPL];
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      const int y = min(lane + 64 * k, V - 1);
+      lv[k] = to_f(lg[ro + y]);
+      mv[k] = mk[y];
+    }
+    // l' (NaN read as -inf) and its argmax; entries past V never win
+    float l[NPL];
+    float bv = -INFINITY;
+    int amax = 0;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      const int y = lane + 64 * k;
+      const float v = lv[k] + mv[k];
+      l[k] = isnan(v) ? -INFINITY : v;
+      if (y < V && ord_gt(l[k], y, bv, amax)) { bv = l[k]; amax = y; }
+    }
+    wave_argmax(bv, amax);
+    float z[NPL];
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) z[k] = l[k] / a.temperature;
+    // the top-k cut: top_k passes in the total order (kept entries in value order)
+    float kv[DRAFT_TOPK_MAX];
+    int ki[DRAFT_TOPK_MAX];
+    float tv = -INFINITY;
+    int ti = V;
+    {
+      float pvv = INFINITY;
+      int pii = -1;
+      const int passes = all ? 0 : a.top_k;
+      for (int r = 0; r < passes; ++r) {
+        float cv = -INFINITY;
+        int ci = V;
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) {
+          const int y = lane + 64 * k;
+          if (y < V && ord_gt(pvv, pii, z[k], y) && ord_gt(z[k], y, cv, ci)) { cv = z[k]; ci = y; }
+        }
+        wave_argmax(cv, ci);
+        // the same in every lane: keep it in scalar registers, so the work on
+        // the kept entries below branches uniformly
+        pvv = lane_f(cv, 0);
+        pii = __builtin_amdgcn_readfirstlane(ci);
+        if (sparse) {
+#pragma unroll
+          for (int rr = 0; rr < DRAFT_TOPK_MAX; ++rr)
+            if (rr == r) { kv[rr] = pvv; ki[rr] = pii; }
+        }
+      }
+      tv = pvv;
+      ti = pii;
+    }
+    const float u = a.greedy ? 0.f : a.u[(size_t)b * a.gamma + i];
+    int d = amax;
+    if (sparse) {
+      // the first top_k entries only (uniform guards: the rest is skipped)
+      const int K = a.top_k;
+      float m = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < DRAFT_TOPK_MAX; ++r)
+        if (r < K && isfinite(kv[r])) m = fmaxf(m, kv[r]);
+      // in groups of four independent exps (one uniform guard per group)
+      float e[DRAFT_TOPK_MAX];
+#pragma unroll
+      for (int g = 0; g < DRAFT_TOPK_MAX; g += 4) {
+#pragma unroll
+        for (int r = g; r < g + 4; ++r) e[r] = 0.f;
+        if (g < K) {
+#pragma unroll
+          for (int r = g; r < g + 4; ++r) {
+            const bool ok = r < K && isfinite(kv[r]);
+            const float x = (float)exp((double)(ok ? kv[r] - m : 0.f));
+            e[r] = ok ? x : 0.f;
+          }
+        }
+      }
+      // token order (insertion by index among the first K)
+#pragma unroll
+      for (int r = 1; r < DRAFT_TOPK_MAX; ++r) {
+        if (r < K) {
+#pragma unroll
+          for (int t = r; t > 0; --t)
+            if (ki[t] < ki[t - 1]) {
+              const int xi = ki[t]; ki[t] = ki[t - 1]; ki[t - 1] = xi;
+              const float xe = e[t]; e[t] = e[t - 1]; e[t - 1] = xe;
+            }
+        }
+      }
+      float S = 0.f;
+#pragma unroll
+      for (int r = 0; r < DRAFT_TOPK_MAX; ++r)
+        if (r < K) S = S + e[r];
+      float p[DRAFT_TOPK_MAX];
+      const float Sd = S > 0.f ? S : 1.f;
+#pragma unroll
+      for (int g = 0; g < DRAFT_TOPK_MAX; g += 4) {
+#pragma unroll
+        for (int r = g; r < g + 4; ++r) p[r] = 0.f;
+        if (g < K) {
+#pragma unroll
+          for (int r = g; r < g + 4; ++r) {
+            const float x = e[r] / Sd;
+            p[r] = (r < K && S > 0.f) ? x : 0.f;
+          }
+        }
+      }
+      if (a.q) {
+        float v[NPL];
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) v[k] = 0.f;
+#pragma unroll
+        for (int r = 0; r < DRAFT_TOPK_MAX; ++r) {
+          if (r < K) {
+            // kept entry r lives in lane ki % 64, register ki / 64
+#pragma unroll
+            for (int k = 0; k < NPL; ++k)
+              if (ki[r] == lane + 64 * k) v[k] = p[r];
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < NPL; ++k)
+          if (lane + 64 * k < V) a.q[ro + lane + 64 * k] = v[k];
+      }
+      if (!a.greedy) {
+        int hit = -1, last = -1;
+        float c = 0.f;
+#pragma unroll
+        for (int r = 0; r < DRAFT_TOPK_MAX; ++r) {
+          if (r < K) {
+            c = c + p[r];
+            if (p[r] > 0.f) last = ki[r];
+            if (hit < 0 && c > u) hit = ki[r];
+          }
+        }
+        d = u < 0.f ? 0 : (hit >= 0 ? hit : (last >= 0 ? last : amax));
+      }
+    } else {
+      // kept entries' exp(z - max) in registers, then the row through LDS for
+      // the sequential normaliser and the draw
+      float m = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < NPL; ++k) {
+        const int y = lane + 64 * k;
+        if (y < V && (all || !ord_gt(tv, ti, z[k], y)) && isfinite(z[k])) m = fmaxf(m, z[k]);
+      }
+      m = wave_fmax(m);
+#pragma unroll
+      for (int k = 0; k < NPL; ++k) {
+        const int y = lane + 64 * k;
+        const bool keep = y < V && (all || !ord_gt(tv, ti, z[k], y)) && isfinite(z[k]);
+        if (y < Vr) row[y] = keep ? (float)exp((double)(z[k] - m)) : 0.f;
+      }
+      wave_sync();
+      if (lane == 0) ssum_s = row_sum(row, Vr);
+      wave_sync();
+      const float S = ssum_s;
+#pragma unroll
+      for (int k = 0; k < NPL; ++k) {
+        const int y = lane + 64 * k;
+        if (y < V) {
+          const float pv = (S > 0.f) ? row[y] / S : 0.f;
+          row[y] = pv;
+          if (a.q) a.q[ro + y] = pv;
+        }
+      }
+      wave_sync();
+      if (!a.greedy) {
+        float tot;
+        d = draw_row(row, V, Vr, u, false, amax, tot, draw_s);
+      }
+    }
+    if (lane == 0) a.drafts[(size_t)b * a.gamma + i] = d;
+    prev = d;
+    wave_sync();
   }
 }
 
 template <typename T>
 hipError_t launch_draft(const DraftArgs& a, int B, hipStream_t st) {
   const size_t lds = (size_t)((a.V + 3) & ~3) * sizeof(float);
-  draft_kernel<T><<<B, 64, lds, st>>>(a);
+  if (a.V <= 512)
+    draft_reg_kernel<T, 8><<<B, 64, lds, st>>>(a);
+  else
+    draft_kernel<T><<<B, 64, lds, st>>>(a);
   return hipGetLastError();
 }
 template hipError_t launch_draft<bf16>(const DraftArgs&, int, hipStream_t);

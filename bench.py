@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--batch-sweep", metavar="B1,B2,...",
                     help="speculative rounds against plain batched decoding at these batch sizes "
                          "(imported synthetic state; eager and HIP-graph replay), one JSON line each")
+    ap.add_argument("--drafter", action="store_true",
+                    help="speculative rounds with the gamma-parallel drafter (random-init, layer-27 prefix) "
+                         "and the drafter's own call time; one JSON line")
     ap.add_argument("--weights", choices=("bf16", "fp8"), default="bf16",
                     help="fp8: the block projections held as FP8 E4M3 with per-row scales (bf16 activations); "
                          "the headline is bf16")
@@ -312,6 +315,116 @@ def batch_sweep(args):
         torch.cuda.empty_cache()
 
 
+def drafter_bench(args):
+    """The gamma-parallel drafter in the loop (random-init shapes: the trained
+    drafter weights are not available, so acceptance here says nothing about
+    the method's; the times are what is measured). Each round: evs_draft from
+    the target's layer-27 residual row of the previous round's last consumed
+    position, the block verify of [next, drafts] with that layer's rows
+    exported, rejection-sampling verification with the drafter's q (or greedy
+    verification of greedy drafts), and the rollback. The hidden row and the
+    last token are picked on the device from the previous round's n_accepted
+    and next token, so the loop has no host sync."""
+    import numpy as np
+    import torch
+    import evs_synth as es
+    from attention_dna_lms_amd import evs
+
+    dev = "cuda"
+    gamma, P, ctx = args.gamma, args.gamma + 1, args.context
+    cfg = es.stack_7b()
+    dcfg = es.drafter_1024(vocab=cfg.vocab, inject_dim=cfg.d_model, max_slots=16)
+    export_block = 2 * 27 + 1               # layer 27's MLP ends the layer
+    rounds = args.warmup + args.steps
+    log("generating and packing the target and the drafter")
+    model = evs.Model(cfg, es.make_weights(cfg, seed=args.seed, device=dev), device=dev)
+    dmodel = evs.Model(dcfg, es.make_weights(dcfg, seed=args.seed + 1, device=dev), device=dev)
+    state = evs.State(model, 1, ctx + 2 * rounds * P + 64, 16, device=dev)
+    dstate = evs.State(dmodel, 1, 16, 16, device=dev)
+    log(f"prefill {ctx - 1} tokens")
+    prompt = torch.from_numpy(es.prompt_tokens(cfg, ctx, seed=args.seed)[0]).to(dev)
+    evs.evs_prefill(model, state, prompt[:-1], [0, ctx - 1])
+    hid = torch.zeros(1, 16, cfg.d_model, dtype=torch.float32, device=dev)
+    evs.evs_state_export(state, export_block, hid)
+    lg = torch.empty(1, P, cfg.vocab, dtype=torch.bfloat16, device=dev)
+    dlg = torch.empty(1, gamma, cfg.vocab, dtype=torch.bfloat16, device=dev)
+    drafts = torch.zeros(1, gamma, dtype=torch.int32, device=dev)
+    q = torch.zeros(1, gamma, cfg.vocab, dtype=torch.float32, device=dev)
+    n_acc = torch.zeros(1, dtype=torch.int32, device=dev)
+    nxt = torch.zeros(1, dtype=torch.int32, device=dev)
+    keep = torch.zeros(1, dtype=torch.int32, device=dev)
+    T, top_k = 1.0, 4                        # the pages' generate defaults
+    u_d = torch.from_numpy(es.uniforms((rounds, 1, gamma), seed=args.seed, tag="u-draft")).to(dev)
+    u_v = torch.from_numpy(es.uniforms((rounds, 1, P), seed=args.seed, tag="u-verify")).to(dev)
+    # the first token after the prompt, with its layer-27 row
+    evs.evs_block_verify(model, state, prompt[-1:].view(1, 1), 0, lg[:, :1])
+    evs.evs_verify_sample(1, 0, cfg.vocab, lg[:, :1], evs.EVS_TARGET_LOGITS_BF16, None, None, u_v[0], T, top_k, 0,
+                          n_acc, nxt, keep)
+    evs.evs_rollback(state, keep)
+    torch.cuda.synchronize()
+    snap = state.buf.clone()
+    hid0, nxt0 = hid.clone(), nxt.clone()
+    acc_hist = torch.zeros(rounds, dtype=torch.int32, device=dev)
+
+    def run_round(r, greedy):
+        evs.evs_draft(dmodel, dstate, 1, hid, 16, n_acc, nxt, gamma, u_d[r], T, top_k, greedy, dlg, drafts, q)
+        cand = torch.cat([nxt.view(1, 1), drafts], dim=1)
+        evs.evs_block_verify(model, state, cand, gamma, lg)
+        evs.evs_verify_sample(1, gamma, cfg.vocab, lg, evs.EVS_TARGET_LOGITS_BF16, q, drafts, u_v[r], T, top_k,
+                              greedy, n_acc, nxt, keep)
+        evs.evs_rollback(state, keep)
+        acc_hist[r:r + 1].copy_(n_acc)
+
+    out = {"mode": "drafter", "context": ctx, "gamma": gamma,
+           "drafter": "width 1024, one attention (8x128) + gated-MLP (d_ff 2752) layer, 4096-wide layer-27 "
+                      "prefix, full 512x512 Markov head; random-init",
+           "drafter_weight_bytes": int(dcfg.weight_bytes() + 2 * dcfg.d_model * (dcfg.inject_dim + dcfg.max_slots)
+                                       + 4 * dcfg.vocab ** 2)}
+    for greedy in (0, 1):
+        state.buf.copy_(snap)
+        hid.copy_(hid0)
+        nxt.copy_(nxt0)
+        n_acc.zero_()
+        for r in range(args.warmup):
+            run_round(r, greedy)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(args.warmup, rounds):
+            run_round(r, greedy)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        acc = float(acc_hist[args.warmup:].sum()) / args.steps
+        out["greedy" if greedy else "sampling_T1_top4"] = {
+            "ms_per_round": round(ms, 4), "mean_accepted_drafts_per_round": round(acc, 3),
+            "emitted_tokens_per_s": round((acc + 1) / (ms / 1e3), 2)}
+    assert state.error() == 0 and dstate.error() == 0, "device error word set"
+    # the drafter alone, on the last round's inputs
+    for _ in range(3):
+        evs.evs_draft(dmodel, dstate, 1, hid, 16, n_acc, nxt, gamma, u_d[0], T, top_k, 0, dlg, drafts, q)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 50
+    e0.record()
+    for _ in range(n):
+        evs.evs_draft(dmodel, dstate, 1, hid, 16, n_acc, nxt, gamma, u_d[0], T, top_k, 0, dlg, drafts, q)
+    e1.record()
+    torch.cuda.synchronize()
+    dms = e0.elapsed_time(e1) / n
+    dstate.timing(True, gamma)
+    for _ in range(n):
+        evs.evs_draft(dmodel, dstate, 1, hid, 16, n_acc, nxt, gamma, u_d[0], T, top_k, 0, dlg, drafts, q)
+    g_ms, g_n, g_by = dstate.timing_read(evs.EVS_KC_GEMM)
+    a_ms, a_n, _ = dstate.timing_read(evs.EVS_KC_ATTN)
+    dstate.timing(False)
+    out["drafter_call_ms"] = round(dms, 4)
+    out["drafter_gemm_us_per_call"] = round(g_ms * 1e3 / n, 2)
+    out["drafter_gemm_gbps"] = round(g_by / (g_ms / 1e3) / 1e9, 1) if g_ms > 0 else 0.0
+    out["drafter_attention_us_per_call"] = round(a_ms * 1e3 / n, 2)
+    print(json.dumps(out), flush=True)
+
+
 def soak(args):
     """Generation at depth: from the 8192-token prefill, N tokens of native
     greedy decoding, then the same N tokens generated by speculative rounds
@@ -498,6 +611,9 @@ def main():
         return
     if args.batch_sweep:
         batch_sweep(args)
+        return
+    if args.drafter:
+        drafter_bench(args)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.steps, args.warmup)

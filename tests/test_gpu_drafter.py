@@ -113,6 +113,56 @@ def test_drafter_matches_oracle_and_draws_bitexact():
     assert state.error() == 0
 
 
+@pytest.mark.parametrize("T,top_k", [(1.0, 1), (0.7, 16), (1.3, 17), (1.0, 0), (0.5, 5)])
+def test_drafter_draws_bitexact_over_top_k(T, top_k):
+    """Drafts and q bit for bit against the oracle's Markov head and draws on
+    the GPU's logits across the kept-set paths: top-k up to 16 (the kept
+    entries alone), beyond 16 and no cut (the full row)."""
+    B, gamma = 3, 12
+    cfg, w, model, state = _drafter(seed=69, B=B)
+    h = _hidden(B, 2, cfg.inject_dim, 70)
+    idx, last = [1, 0, 1], [65, 67, 71]
+    u = es.uniforms((B, gamma), seed=71 + top_k)
+    u[2, 3] = 0.0
+    lg, dr, q = _run(model, state, B, h, idx, last, gamma, u, T, top_k, 0)
+    orc = Drafter(cfg, w)
+    for b in range(B):
+        d_ref, q_ref = orc.draft(lg[b], last[b], u[b], T, top_k)
+        assert np.array_equal(dr[b], d_ref), (b, dr[b], d_ref)
+        assert np.array_equal(q[b], q_ref), b
+    _, dg, qg = _run(model, state, B, h, idx, last, gamma, None, T, top_k, 1)
+    for b in range(B):
+        d_ref, q_ref = orc.draft(lg[b], last[b], None, T, top_k, greedy=True)
+        assert np.array_equal(dg[b], d_ref), b
+        assert np.array_equal(qg[b], q_ref), b
+    assert state.error() == 0
+
+
+@pytest.mark.parametrize("top_k", [4, 0])
+def test_drafter_large_vocab_row_path(top_k):
+    """A vocabulary past 512 takes the kernel that keeps the row in LDS: a
+    small drafter (d = 128, V = 600) against the oracle drafter, draws bit
+    for bit on the GPU's logits."""
+    from evs_synth.configs import Block, ModelConfig
+    cfg = ModelConfig("drafter_v600", 128, 600, [Block("attn", n_heads=4, head_dim=32), Block("mlp", d_ff=352)],
+                      dtype="bf16", inject_dim=96, max_slots=8)
+    w = es.make_weights(cfg, seed=72)
+    B, gamma = 2, 8
+    model = evs.Model(cfg, w, device=DEV)
+    state = evs.State(model, B, 8, 8, device=DEV)
+    h = _hidden(B, 1, cfg.inject_dim, 73)
+    u = es.uniforms((B, gamma), seed=74)
+    lg, dr, q = _run(model, state, B, h, None, [65, 599], gamma, u, 0.9, top_k, 0)
+    orc = Drafter(cfg, w)
+    for b, last in enumerate([65, 599]):
+        ref = orc.trunk_logits(h[b, 0].astype(np.float64), last, gamma)
+        assert logit_err(lg[b], ref) < LOGIT_ATOL
+        d_ref, q_ref = orc.draft(lg[b], last, u[b], 0.9, top_k)
+        assert np.array_equal(dr[b], d_ref), b
+        assert np.array_equal(q[b], q_ref), b
+    assert state.error() == 0
+
+
 def test_drafter_exact_causal_prefix_on_gpu():
     """A shorter draft is an exact prefix of a longer one: logits rows and
     drafts of gamma = 5 equal the first 5 of gamma = 12 bit for bit."""
