@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="print the per-round kernel table of a rocprofv3 kernel trace of this bench "
                          "(pass the same --steps/--warmup as the profiled run) and exit")
+    ap.add_argument("--summarize-drafter-trace", metavar="KERNEL_TRACE_CSV",
+                    help="print the per-call kernel table of the evs_draft calls in a rocprofv3 kernel trace "
+                         "of --drafter and exit")
     ap.add_argument("--summarize-counters", nargs=4,
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="print the per-launch HBM traffic (JSON) from rocprofv3 FETCH_SIZE / WRITE_SIZE "
@@ -71,7 +74,8 @@ def parse():
 GEMM_SOURCES = ("attention_dna_lms_amd/csrc/gemm_impl.h", "attention_dna_lms_amd/csrc/gemm_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_kernel_c3_traffic.json")
 KERNEL_FAMILIES = ("attn_merge_kernel", "gemm_kernel", "attn32_kernel", "attn_kernel", "verify_kernel",
-                   "commit_kernel", "embed_kernel")
+                   "commit_kernel", "embed_kernel", "draft_reg_kernel", "draft_kernel", "inject_prep_kernel",
+                   "slots_kernel", "export_rows_kernel")
 
 
 def gemm_sources_hash():
@@ -123,6 +127,37 @@ def summarize_trace(path, steps, warmup):
         for k, v in sorted(g.items(), key=lambda kv: -sum(kv[1])):
             print(f"| {k} | {len(v) / steps:.0f} | {sum(v) / len(v):.2f} | {sum(v) / steps:.1f} |")
         print()
+
+
+def summarize_drafter_trace(path, calls=50):
+    """Per-kernel table of the last `calls` evs_draft calls in a kernel trace of
+    `bench.py --drafter` (each call runs from its injection-prep kernel to its
+    draw kernel; the bench ends with 3 + 50 back-to-back calls)."""
+    import collections
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    starts = [i for i, r in enumerate(rows) if "inject_prep_kernel" in r["Kernel_Name"]][-calls:]
+    g = collections.defaultdict(list)
+    spans = []
+    for i0 in starts:
+        j = i0
+        while True:
+            r = rows[j]
+            name = r["Kernel_Name"]
+            wg = int(r["Grid_Size_X"]) // max(int(r["Workgroup_Size_X"]), 1)
+            key = f"{family(r, False)} (workgroups {wg}x{r['Grid_Size_Y']}x{r['Grid_Size_Z']})"
+            g[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            if "draft_reg_kernel" in name or "draft_kernel" in name:
+                break
+            j += 1
+        spans.append((int(rows[j]["End_Timestamp"]) - int(rows[i0]["Start_Timestamp"])) / 1e3)
+    busy = sum(sum(v) for v in g.values()) / len(starts)
+    print(f"{len(starts)} calls; first dispatch to last end: {sum(spans) / len(spans):.1f} us per call; "
+          f"kernel busy time {busy:.1f} us per call\n")
+    print("| kernel | launches/call | avg us | us/call |\n|---|---|---|---|")
+    for k, v in sorted(g.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| {k} | {len(v) / len(starts):.0f} | {sum(v) / len(v):.2f} | {sum(v) / len(starts):.1f} |")
 
 
 def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, steps, warmup):
@@ -412,16 +447,9 @@ def drafter_bench(args):
     e1.record()
     torch.cuda.synchronize()
     dms = e0.elapsed_time(e1) / n
-    dstate.timing(True, gamma)
-    for _ in range(n):
-        evs.evs_draft(dmodel, dstate, 1, hid, 16, n_acc, nxt, gamma, u_d[0], T, top_k, 0, dlg, drafts, q)
-    g_ms, g_n, g_by = dstate.timing_read(evs.EVS_KC_GEMM)
-    a_ms, a_n, _ = dstate.timing_read(evs.EVS_KC_ATTN)
-    dstate.timing(False)
     out["drafter_call_ms"] = round(dms, 4)
-    out["drafter_gemm_us_per_call"] = round(g_ms * 1e3 / n, 2)
-    out["drafter_gemm_gbps"] = round(g_by / (g_ms / 1e3) / 1e9, 1) if g_ms > 0 else 0.0
-    out["drafter_attention_us_per_call"] = round(a_ms * 1e3 / n, 2)
+    out["drafter_call_note"] = ("evs_draft at batch 1, gamma 12, top-4 sampling: injection GEMM, slot rows, the "
+                                "drafter layer and head, Markov draws; per-kernel split from a kernel trace")
     print(json.dumps(out), flush=True)
 
 
@@ -617,6 +645,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.steps, args.warmup)
+        return
+    if args.summarize_drafter_trace:
+        summarize_drafter_trace(args.summarize_drafter_trace)
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, args.steps, args.warmup)
