@@ -71,6 +71,7 @@ struct evs_state {
   size_t w_x = 0, w_nrm = 0, w_o = 0, w_q = 0, w_h = 0, w_logit = 0, w_apart = 0, ws_total = 0;
   size_t apart_floats = 0;
   size_t w_inj_x = 0, w_inj_nrm = 0, w_z = 0;   // drafter: injected rows, their norm partials, the prefix z
+  size_t w_u = 0;                               // bf16 models: normed rows for multi-tile launches
   int inj_ld = 0;
   int export_block = -1;                        // hidden-state export after this block (evs_block_verify)
   float* export_dst = nullptr;
@@ -263,6 +264,7 @@ void layout_state(evs_state* s) {
   s->qtn_max = (s->max_block + 15) / 16;
   s->apart_floats = (size_t)B * s->qtn_max * H * s->S * 16 * (DHm + 2);
   s->w_apart = take(s->apart_floats * 4);
+  if (es == 2) s->w_u = take(M16 * d * 2);
   if (m->desc.inject_dim > 0) {
     const size_t B16 = align_up((size_t)B, 16);
     s->inj_ld = (int)B16;
@@ -385,6 +387,24 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
   float* nrm = wp<float>(s, s->w_nrm);
   int* t = sp<int>(s, s->off_t);
   int* err = sp<int>(s, s->off_err);
+  // Launches of more than one 16-row tile (bf16 models) read the normed rows
+  // from a norm kernel (the same bf16 operands the fused prologue would form,
+  // so results are unchanged): one bf16 load per step instead of two fp32
+  // loads per tile and step, and half the registers for the operands.
+  const bool pre_norm = sizeof(T) == 2 && m->desc.dtype == EVS_BF16 && slicing(nseq, P).MT >= 2;
+  auto normed = [&](int& amode, const void*& A) -> evs_status {
+    amode = A_NORM;
+    A = x;
+    if constexpr (sizeof(T) == 2) {
+      if (pre_norm) {
+        bf16* u = wp<bf16>(s, s->w_u);
+        HIP_TRY(launch_norm_rows(x, nrm, d / 16, s->M_max, (float)d, m->desc.norm_eps, M, d, u, st));
+        amode = A_ACT;
+        A = u;
+      }
+    }
+    return EVS_OK;
+  };
   if (tokens)
     HIP_TRY(launch_embed<T>(tokens, reinterpret_cast<const T*>(m->base + m->embed), x, nrm, s->M_max, M, d,
                             m->desc.vocab, P, seq0, t, s->max_ctx, err, st));
@@ -395,7 +415,10 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
     if (p.d.kind == EVS_MLP) {
       a.out = wp<void>(s, s->w_h);
       a.ldo = p.d.d_ff;
-      EVS_TRY(gemm_call<T>(m, s, p.w_gu, A_NORM, E_GELU, x, d, nseq, P, a, st));
+      int am;
+      const void* A;
+      EVS_TRY(normed(am, A));
+      EVS_TRY(gemm_call<T>(m, s, p.w_gu, am, E_GELU, A, d, nseq, P, a, st));
       GemmArgs b{};
       b.x = x; b.ldx = d; b.nrm_out = nrm;
       EVS_TRY(gemm_call<T>(m, s, p.w_down, A_ACT, E_RESID, wp<void>(s, s->w_h), p.d.d_ff, nseq, P, b, st));
@@ -427,7 +450,10 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
       a.out = wp<void>(s, s->w_q);
     }
     a.ldo = d;
-    EVS_TRY(gemm_call<T>(m, s, p.w_in, A_NORM, E_MIXER, x, d, nseq, P, a, st, scratch));
+    int am;
+    const void* A;
+    EVS_TRY(normed(am, A));
+    EVS_TRY(gemm_call<T>(m, s, p.w_in, am, E_MIXER, A, d, nseq, P, a, st, scratch));
     if (p.d.kind == EVS_ATTN) {
       AttnArgs at{};
       at.q = wp<void>(s, s->w_q); at.out = wp<void>(s, s->w_o);

@@ -162,6 +162,8 @@ hipError_t launch_pack(const T* W, uint4* out, int rows_valid, int K, int n_grou
                        int map_kind, int map_stride, hipStream_t st);
 hipError_t launch_copy_row(const void* src, void* dst, size_t bytes, hipStream_t st);
 hipError_t launch_verify(const VerifyArgs& a, int B, hipStream_t st);
+hipError_t launch_norm_rows(const float* x, const float* nrm, int n_part, int nrm_ld, float fd, float eps, int M,
+                            int K, bf16* u, hipStream_t st);
 
 struct DraftArgs {
   const void* logits;    // [B, gamma, V] storage type: the drafter head's logits

@@ -354,7 +354,11 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   // k-steps per pipeline chunk: one chunk of NT weight fragments and MT
   // activation fragments (8 registers each for fp32 rows feeding bf16, else 4)
   // per step stays within ~64 registers, the two chunks in flight within ~128
-  constexpr int AREG = (AMODE == A_NORM && sizeof(T) == 2) ? 2 : 1;
+  // (pre-normed bf16 rows feeding the in-projection or gate/up of a
+  // multi-tile launch keep the chunk depth of the fused-norm path: the
+  // registers their smaller operands free go to the row tiles)
+  constexpr bool PRENORMED = AMODE == A_ACT && MT >= 2 && (EPI == E_MIXER || EPI == E_GELU);
+  constexpr int AREG = ((AMODE == A_NORM || PRENORMED) && sizeof(T) == 2) ? 2 : 1;
   // (measured at the 7B shapes: 4 steps for single-tile projections, 2 for
   // the gate/up pairs, the register bound for the in-projection triples)
   constexpr int PER = 16 / (NT + KPW * AREG * MT);
@@ -633,7 +637,16 @@ static hipError_t launch_gemm_mt(int NT, int amode, int epi, const GemmArgs& a, 
     gemm_kernel<T, MT, 2, A_NORM, E_GELU><<<grid, block, lds, st>>>(a);
   else if (NT == 1 && amode == A_NORM && epi == E_STORE)
     gemm_kernel<T, MT, 1, A_NORM, E_STORE><<<grid, block, lds, st>>>(a);
-  else
+  else if constexpr (sizeof(T) == 2 && MT >= 2) {
+    // multi-tile bf16 launches of the normed projections may take rows the
+    // norm kernel already formed (bf16(x * rinv), the same operands)
+    if (NT == 3 && amode == A_ACT && epi == E_MIXER)
+      gemm_kernel<T, MT, 3, A_ACT, E_MIXER><<<grid, block, lds, st>>>(a);
+    else if (NT == 2 && amode == A_ACT && epi == E_GELU)
+      gemm_kernel<T, MT, 2, A_ACT, E_GELU><<<grid, block, lds, st>>>(a);
+    else
+      return hipErrorInvalidValue;
+  } else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }

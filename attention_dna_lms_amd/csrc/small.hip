@@ -51,6 +51,55 @@ template hipError_t launch_embed<bf16>(const int*, const bf16*, float*, float*, 
 template hipError_t launch_embed<float>(const int*, const float*, float*, float*, int, int, int, int, int, int,
                                         const int*, int, int*, hipStream_t);
 
+// ---------------------------------------------------------------- norm rows
+// RMSNorm of fp32 residual rows into bf16 rows in the operand-order layout
+// (bf16 models): u = bf16(x * rinv), with rinv formed from the
+// per-16-column sums of squares exactly as the normed GEMM prologue forms it
+// (32 lanes per row, each adding its partials j + 32q, q < 8, in a fixed tree
+// per 256 partials, then a butterfly over the 32; 1 / sqrt(sum / K + eps)), so
+// u holds, bit for bit, the operands that prologue builds in registers.
+// One workgroup per row; each thread converts runs of 8 columns.
+__global__ void __launch_bounds__(256) norm_rows_kernel(const float* __restrict__ x, const float* __restrict__ nrm,
+                                                        int n_part, int nrm_ld, float fd, float eps, int K,
+                                                        bf16* __restrict__ u) {
+  __shared__ float rinv_s;
+  const int m = blockIdx.x, tid = threadIdx.x;
+  if (tid < 32) {
+    const int j = tid;
+    float sum = 0.f;
+    for (int i0 = 0; i0 < n_part; i0 += 256) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = i0 + j + 32 * q;
+        v[q] = i < n_part ? nrm[(size_t)i * nrm_ld + m] : 0.f;
+      }
+      sum += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    }
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 32);
+    if (j == 0) rinv_s = 1.0f / sqrtf(sum / fd + eps);
+  }
+  __syncthreads();
+  const float r = rinv_s;
+  for (int c = tid * 8; c < K; c += 256 * 8) {
+    const size_t o = act_off<8>(m, c, K);
+    const float4 lo = *reinterpret_cast<const float4*>(x + o);
+    const float4 hi = *reinterpret_cast<const float4*>(x + o + 4);
+    bf16x8 b;
+    b[0] = (bf16)(lo.x * r); b[1] = (bf16)(lo.y * r); b[2] = (bf16)(lo.z * r); b[3] = (bf16)(lo.w * r);
+    b[4] = (bf16)(hi.x * r); b[5] = (bf16)(hi.y * r); b[6] = (bf16)(hi.z * r); b[7] = (bf16)(hi.w * r);
+    *reinterpret_cast<uint4*>(u + o) = __builtin_bit_cast(uint4, b);
+  }
+}
+
+hipError_t launch_norm_rows(const float* x, const float* nrm, int n_part, int nrm_ld, float fd, float eps, int M,
+                            int K, bf16* u, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  norm_rows_kernel<<<M, 256, 0, st>>>(x, nrm, n_part, nrm_ld, fd, eps, K, u);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- commit
 // Slice each sequence's state to its accepted boundary: the committed length
 // advances by n_keep and, if anything was kept, the IIR state pointer moves to
