@@ -19,6 +19,7 @@ namespace {
 
 constexpr size_t ALIGN = 256;
 constexpr int MAX_ROWS_PER_WG = 144;   // 9 MFMA row tiles
+constexpr int SPLIT_MT = 7;            // row tiles from which bf16 launches split K across workgroups
 constexpr int GEMM_WAVES = 8;          // waves per GEMM workgroup (gemm_kernel default)
 constexpr int ATTN_CUS = 256;          // compute units the attention split count is sized for
 
@@ -72,6 +73,7 @@ struct evs_state {
   size_t apart_floats = 0;
   size_t w_inj_x = 0, w_inj_nrm = 0, w_z = 0;   // drafter: injected rows, their norm partials, the prefix z
   size_t w_u = 0;                               // bf16 models: normed rows for multi-tile launches
+  size_t w_part = 0, part_bytes = 0;            // bf16 models: split-K partials of multi-tile launches
   int inj_ld = 0;
   int export_block = -1;                        // hidden-state export after this block (evs_block_verify)
   float* export_dst = nullptr;
@@ -264,7 +266,23 @@ void layout_state(evs_state* s) {
   s->qtn_max = (s->max_block + 15) / 16;
   s->apart_floats = (size_t)B * s->qtn_max * H * s->S * 16 * (DHm + 2);
   s->w_apart = take(s->apart_floats * 4);
-  if (es == 2) s->w_u = take(M16 * d * 2);
+  if (es == 2) {
+    s->w_u = take(M16 * d * 2);
+    // split-K partials: 8 ranges x the padded rows of the widest slicing that
+    // splits x the widest projection
+    size_t rows = 0;
+    for (int P = 1; P <= s->max_block; ++P) {
+      const Slicing sl = slicing(B, P);
+      if (sl.MT >= SPLIT_MT) rows = std::max(rows, (size_t)sl.slices * sl.MT * 16);
+    }
+    size_t nmax = (size_t)((m->desc.vocab + 15) / 16) * 16;
+    for (const auto& p : m->plan) {
+      if (p.d.kind == EVS_MLP) nmax = std::max({nmax, (size_t)2 * p.d.d_ff, (size_t)d});
+      else nmax = std::max(nmax, (size_t)3 * d);
+    }
+    s->part_bytes = 8 * rows * nmax * 4;
+    if (s->part_bytes) s->w_part = take(s->part_bytes);
+  }
   if (m->desc.inject_dim > 0) {
     const size_t B16 = align_up((size_t)B, 16);
     s->inj_ld = (int)B16;
@@ -366,6 +384,14 @@ evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int 
                        (double)a.M * mat.rows_valid * (epi == E_RESID ? 8 : m->es);
   const size_t lds = gemm_lds(sl.MT, mat.NT, scratch_floats);
   if (lds > 65536) return EVS_E_UNSUPPORTED;
+  // multi-tile bf16 launches over normed rows: k-range partials, then the
+  // reduction and epilogue (the same results as one kernel)
+  if (m->desc.dtype == EVS_BF16 && !mat.w8 && amode == A_ACT && sl.MT >= SPLIT_MT &&
+      (size_t)8 * sl.slices * sl.MT * 16 * mat.n_groups * mat.NT * 16 * 4 <= s->part_bytes) {
+    a.part = wp<float>(s, s->w_part);
+    return hip_ok(timed(s, EVS_KC_GEMM, bytes, st,
+                        [&] { return launch_gemm_split(sl.MT, mat.NT, epi, a, sl.slices, lds, st); }));
+  }
   return hip_ok(timed(s, EVS_KC_GEMM, bytes, st,
                       [&] {
                         if constexpr (sizeof(T) == 2)
@@ -476,7 +502,10 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
   if (logits) {
     GemmArgs a{};
     a.N = m->desc.vocab; a.out = logits; a.ldo = m->desc.vocab;
-    EVS_TRY(gemm_call<T>(m, s, m->lm, A_NORM, E_STORE, x, d, nseq, P, a, st));
+    int am;
+    const void* A;
+    EVS_TRY(normed(am, A));
+    EVS_TRY(gemm_call<T>(m, s, m->lm, am, E_STORE, A, d, nseq, P, a, st));
   }
   return EVS_OK;
 }

@@ -112,6 +112,7 @@ struct GemmArgs {
   float* x; int ldx;     // E_RESID residual stream
   float* nrm_out;        // E_RESID per-16-column sum of squares [n_tiles][nrm_ld]
   MixArgs mix;
+  float* part;           // split-K launches: the k-range partials [slice][8][group][MT][NT][64 lanes][4]
 };
 
 struct AttnArgs {
@@ -162,6 +163,9 @@ hipError_t launch_pack(const T* W, uint4* out, int rows_valid, int K, int n_grou
                        int map_kind, int map_stride, hipStream_t st);
 hipError_t launch_copy_row(const void* src, void* dst, size_t bytes, hipStream_t st);
 hipError_t launch_verify(const VerifyArgs& a, int B, hipStream_t st);
+// multi-tile bf16 launches with pre-normed rows: k-range partials, then the
+// reduction and epilogue (results equal launch_gemm's)
+hipError_t launch_gemm_split(int MT, int NT, int epi, const GemmArgs& a, int slices, size_t lds, hipStream_t st);
 hipError_t launch_norm_rows(const float* x, const float* nrm, int n_part, int nrm_ld, float fd, float eps, int M,
                             int K, bf16* u, hipStream_t st);
 

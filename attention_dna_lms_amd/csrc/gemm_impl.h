@@ -343,7 +343,8 @@ __device__ __forceinline__ void fp8_to_bf16(uint4 w, uint4& lo, uint4& hi) {
                   fp8x2_to_bf16x2<true>(w.w));
 }
 
-template <typename T, int MT, int NT, int AMODE, int EPI, int WV = 8, int CHO = 0, int MINB = 1, bool W8 = false>
+template <typename T, int MT, int NT, int AMODE, int EPI, int WV = 8, int CHO = 0, int MINB = 1, bool W8 = false,
+          bool PART = false>
 __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   static_assert(EPI != E_MIXER || WV == 8, "the mixer epilogue assumes 512 threads");
   static_assert(!W8 || sizeof(T) == 2, "FP8 weights feed the bf16 MFMA");
@@ -397,6 +398,17 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) arow[mt] = (size_t)(row0 + min(mt * 16 + rl, rows - 1));
 
+  f32x4 acc[NT][MT];
+  if constexpr (PART) {
+    // the eight k-range partials gemm_part_kernel formed (wave w takes range
+    // w's chains, exactly what this kernel's wave w would have computed)
+    const f32x4* pp = reinterpret_cast<const f32x4*>(a.part) +
+                      ((((size_t)blockIdx.y * 8 + wave) * a.n_groups + g) * MT) * NT * 64 + lane;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = pp[(mt * NT + nt) * 64];
+  } else {
   // two chunk buffers
   uint4 w0[CH][NT], w1[CH][NT];
   AFrag<T, AMODE> x0[CH][MT][KPW], x1[CH][MT][KPW];
@@ -418,7 +430,6 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
         for (int h = 0; h < KPW; ++h)
           x[u][mt][h].load(a, arow[mt], (max(min(k0 + u, wk1 - 1), 0) * KPW + h) * KSTEP + aoff);
   };
-  f32x4 acc[NT][MT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -542,6 +553,8 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
     }
   }
 
+  }   // streaming
+
   // Reduction of the 8 waves' partial tiles in the fixed tree
   // ((w0 + w4) + (w2 + w6)) + ((w1 + w5) + (w3 + w7)). Small tiles: every wave
   // stores its partial once and each thread sums its elements straight into
@@ -625,6 +638,158 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   gemm_epilogue<T, MT, NT, EPI>(a, pf, ep, ep + NT * MT * 256, g, row0, rows);
 }
 
+// ------------------------------------------------------------ split K
+// Multi-tile launches (bf16 rows already normed, read as is) in two kernels.
+// gemm_part_kernel: one workgroup per (eight column groups, one of the eight
+// k-ranges gemm_kernel gives its waves, row slice); wave w takes group 8c + w
+// and forms, for every row tile, exactly the MFMA chain gemm_kernel's wave r
+// forms for that group (range r, ascending k, from zero), writing it to the
+// partial buffer. The row tiles' activation fragments of each chunk of k-steps
+// are staged once in LDS and shared by the eight waves (one stream of
+// activations per eight groups instead of one per group), and a wave keeps no
+// activation fragments in flight in registers. gemm_kernel<..., PART> then
+// loads wave w's partials from range w, reduces them in its fixed tree and
+// runs its epilogue, so every output equals the one-kernel result bit for bit.
+constexpr int PK = 2;   // k-steps per staged activation chunk
+
+template <typename T, int MT, int NT>
+__global__ void __launch_bounds__(512) gemm_part_kernel(GemmArgs a) {
+  static_assert(sizeof(T) == 2, "bf16 rows only");
+  constexpr int E = St<T>::E, KSTEP = St<T>::KSTEP;
+  constexpr int XF = PK * MT * 64;                   // 16-byte units per staged chunk
+  constexpr int XPT = (XF + 511) / 512;              // staging loads per thread
+  constexpr int XB = XPT * 512;                      // buffer stride: every thread writes every round
+  extern __shared__ float lds[];
+  uint4* xs = reinterpret_cast<uint4*>(lds);         // [2][XB]: [PK][MT][64] and padding
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = blockIdx.x * 8 + wave;
+  const bool gv = g < a.n_groups;
+  const int r = blockIdx.y;
+  const int row0 = blockIdx.z * a.rows_per_slice;
+  const int rows = min(a.rows_per_slice, a.M - row0);
+  const int ks = a.ksteps, pw = (ks + 7) / 8;
+  const int kb = min(r * pw, ks), ke = min(kb + pw, ks);
+  const int nchk = (ke - kb + PK - 1) / PK;
+  const u32x4* wp = reinterpret_cast<const u32x4*>(a.W) + lane + (gv ? (size_t)g * a.gstride : 0);
+  const T* A = reinterpret_cast<const T*>(a.A);
+
+  // staging: unit idx = (u * MT + mt) * 64 + l holds lane l's 16 bytes of row
+  // tile mt at k-step u of the chunk (rows past the slice re-read its last row)
+  auto x_addr = [&](int idx, int c) __attribute__((always_inline)) -> const uint4* {
+    const int l = idx & 63, mt = (idx >> 6) % MT, u = (idx >> 6) / MT;
+    const int k = min(kb + c * PK + u, ke - 1);
+    const int row = row0 + min(mt * 16 + (l & 15), rows - 1);
+    return reinterpret_cast<const uint4*>(A + act_off<E>(row, k * KSTEP + (l >> 4) * E, a.lda));
+  };
+  auto issue_w = [&](uint4 (&w)[PK][NT], int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < PK; ++u)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int k = min(kb + c * PK + u, ke - 1);
+        w[u][nt] = ld_stream(wp + (size_t)max(k, 0) * a.tstride + nt * 64);
+      }
+  };
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint4 w0[PK][NT], w1[PK][NT];
+  if (nchk > 0) {
+    // chunk 0's activations straight into LDS buffer 0
+#pragma unroll
+    for (int q = 0; q < XPT; ++q) xs[tid + q * 512] = *x_addr(min(tid + q * 512, XF - 1), 0);
+    issue_w(w0, 0);
+    if (nchk > 1) issue_w(w1, 1);
+  }
+  // chunk c: its activations are in LDS buffer c & 1 and its weights in w0
+  // (even c) or w1 (odd c). Chunk c + 1's activations are loaded while chunk c
+  // computes and stored to the other buffer afterwards; chunk c + 2's weights
+  // replace chunk c's.
+  auto step = [&](int c, uint4 (&w)[PK][NT]) __attribute__((always_inline)) {
+    __syncthreads();                      // chunk c staged; chunk c - 1's buffer free
+    // (after the last chunk this re-stages the last chunk into the free buffer:
+    // harmless, and it keeps the staging free of branches)
+    // (three named registers rather than an array: at most 3 rounds for 9 row
+    // tiles of PK k-steps)
+    static_assert(XPT <= 3, "staging rounds");
+    const int cn = min(c + 1, nchk - 1);
+    uint4 xn0, xn1, xn2;
+    xn0 = *x_addr(min(tid, XF - 1), cn);
+    if constexpr (XPT > 1) xn1 = *x_addr(min(tid + 512, XF - 1), cn);
+    if constexpr (XPT > 2) xn2 = *x_addr(min(tid + 1024, XF - 1), cn);
+    const uint4* xb = xs + (c & 1) * XB;
+#pragma unroll
+    for (int u = 0; u < PK; ++u) {
+      if (kb + c * PK + u < ke) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const uint4 x = xb[(u * MT + mt) * 64 + lane];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mma_frag(w[u][nt], x, acc[mt][nt], T());
+        }
+      }
+    }
+    if (c + 2 < nchk) issue_w(w, c + 2);
+    uint4* dst = xs + ((c + 1) & 1) * XB;
+    dst[tid] = xn0;
+    if constexpr (XPT > 1) dst[tid + 512] = xn1;
+    if constexpr (XPT > 2) dst[tid + 1024] = xn2;
+  };
+  for (int c = 0; c < nchk; c += 2) {
+    step(c, w0);
+    if (c + 1 < nchk) step(c + 1, w1);
+  }
+  if (gv) {
+    f32x4* pp = reinterpret_cast<f32x4*>(a.part) +
+                ((((size_t)blockIdx.z * 8 + r) * a.n_groups + g) * MT) * NT * 64 + lane;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) pp[(mt * NT + nt) * 64] = acc[mt][nt];
+  }
+}
+
+template <typename T, int MT>
+static hipError_t launch_gemm_split_mt(int NT, int epi, const GemmArgs& a, int slices, size_t lds, hipStream_t st) {
+  if constexpr (sizeof(T) != 2 || MT < 2) {
+    return hipErrorInvalidValue;
+  } else {
+    const size_t xlds = (size_t)2 * ((PK * MT * 64 + 511) / 512) * 512 * 16;
+    dim3 pgrid((a.n_groups + 7) / 8, 8, slices), grid(a.n_groups, slices), block(512);
+    if (NT == 3) gemm_part_kernel<T, MT, 3><<<pgrid, block, xlds, st>>>(a);
+    else if (NT == 2) gemm_part_kernel<T, MT, 2><<<pgrid, block, xlds, st>>>(a);
+    else if (NT == 1) gemm_part_kernel<T, MT, 1><<<pgrid, block, xlds, st>>>(a);
+    else return hipErrorInvalidValue;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (NT == 3 && epi == E_MIXER) gemm_kernel<T, MT, 3, A_ACT, E_MIXER, 8, 0, 1, false, true><<<grid, block, lds, st>>>(a);
+    else if (NT == 2 && epi == E_GELU) gemm_kernel<T, MT, 2, A_ACT, E_GELU, 8, 0, 1, false, true><<<grid, block, lds, st>>>(a);
+    else if (NT == 1 && epi == E_RESID) gemm_kernel<T, MT, 1, A_ACT, E_RESID, 8, 0, 1, false, true><<<grid, block, lds, st>>>(a);
+    else if (NT == 1 && epi == E_STORE) gemm_kernel<T, MT, 1, A_ACT, E_STORE, 8, 0, 1, false, true><<<grid, block, lds, st>>>(a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+}
+
+template <typename T>
+hipError_t launch_gemm_split_impl(int MT, int NT, int epi, const GemmArgs& a, int slices, size_t lds, hipStream_t st) {
+  switch (MT) {
+    case 2: return launch_gemm_split_mt<T, 2>(NT, epi, a, slices, lds, st);
+    case 3: return launch_gemm_split_mt<T, 3>(NT, epi, a, slices, lds, st);
+    case 4: return launch_gemm_split_mt<T, 4>(NT, epi, a, slices, lds, st);
+    case 5: return launch_gemm_split_mt<T, 5>(NT, epi, a, slices, lds, st);
+    case 6: return launch_gemm_split_mt<T, 6>(NT, epi, a, slices, lds, st);
+    case 7: return launch_gemm_split_mt<T, 7>(NT, epi, a, slices, lds, st);
+    case 8: return launch_gemm_split_mt<T, 8>(NT, epi, a, slices, lds, st);
+    case 9: return launch_gemm_split_mt<T, 9>(NT, epi, a, slices, lds, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T, int MT>
 static hipError_t launch_gemm_mt(int NT, int amode, int epi, const GemmArgs& a, int slices,
                                  size_t lds, hipStream_t st) {
@@ -644,6 +809,8 @@ static hipError_t launch_gemm_mt(int NT, int amode, int epi, const GemmArgs& a, 
       gemm_kernel<T, MT, 3, A_ACT, E_MIXER><<<grid, block, lds, st>>>(a);
     else if (NT == 2 && amode == A_ACT && epi == E_GELU)
       gemm_kernel<T, MT, 2, A_ACT, E_GELU><<<grid, block, lds, st>>>(a);
+    else if (NT == 1 && amode == A_ACT && epi == E_STORE)
+      gemm_kernel<T, MT, 1, A_ACT, E_STORE><<<grid, block, lds, st>>>(a);
     else
       return hipErrorInvalidValue;
   } else

@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--batch-sweep", metavar="B1,B2,...",
                     help="speculative rounds against plain batched decoding at these batch sizes "
                          "(imported synthetic state; eager and HIP-graph replay), one JSON line each")
+    ap.add_argument("--c5", action="store_true",
+                    help="the ragged batch (8 sequences, contexts 1k-32k, imported state) at gamma 1..16; "
+                         "one JSON line per gamma")
     ap.add_argument("--drafter", action="store_true",
                     help="speculative rounds with the gamma-parallel drafter (random-init, layer-27 prefix) "
                          "and the drafter's own call time; one JSON line")
@@ -453,6 +456,77 @@ def drafter_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def c5_bench(args):
+    """The ragged batch: 8 sequences with contexts drawn from U{1024..32768}
+    (imported synthetic states, the same draw as the ragged parity case),
+    rounds at gamma 1, 4, 8, 12, 16: block verify of [next, drafts] with
+    drafts uniform over ACGT, rejection-sampling verification on the model's
+    logits (T = 1, top-4) with q uniform over ACGT, and the ragged rollback.
+    One JSON line per gamma."""
+    import numpy as np
+    import torch
+    import evs_synth as es
+    from attention_dna_lms_amd import evs
+
+    dev = "cuda"
+    cfg = es.stack_7b()
+    B, V = 8, cfg.vocab
+    ctx = es.gen.rng_for(23, "c5-contexts").integers(1024, 32769, B)
+    W, K = args.warmup, args.steps
+    rounds = W + K
+    gmax = 16
+    log(f"generating and packing weights; contexts {list(map(int, ctx))}")
+    model = evs.Model(cfg, es.make_weights(cfg, seed=args.seed, device=dev), device=dev)
+    state = evs.State(model, B, int(ctx.max()) + rounds * (gmax + 1) + 64, gmax + 1, device=dev)
+    for b in range(B):
+        import_synthetic_state(evs, es, cfg, state, int(ctx[b]), args.seed + b, dev, b)
+    snap = state.buf.clone()
+    acgt = torch.tensor(es.ACGT_IDS(V), dtype=torch.int32, device=dev)
+    for gamma in (1, 4, 8, 12, 16):
+        P = gamma + 1
+        rng = np.random.default_rng([args.seed, 5, gamma])
+        drafts = acgt[torch.from_numpy(rng.integers(0, 4, (rounds, B, gamma))).to(dev)]
+        q = torch.zeros(B, gamma, V, device=dev)
+        q[:, :, acgt.long()] = 0.25
+        u = torch.from_numpy(es.uniforms((rounds, B, P), seed=args.seed, tag=f"c5-u{gamma}")).to(dev)
+        lg = torch.empty(B, P, V, dtype=torch.bfloat16, device=dev)
+        acc = torch.zeros(rounds, B, dtype=torch.int32, device=dev)
+        nxt = torch.zeros(B, dtype=torch.int32, device=dev)
+        keep = torch.zeros(rounds, B, dtype=torch.int32, device=dev)
+        state.buf.copy_(snap)
+        nxt.copy_(acgt[torch.arange(B, device=dev) % 4])
+
+        def run(r):
+            cand = torch.cat([nxt.view(B, 1), drafts[r]], dim=1)
+            evs.evs_block_verify(model, state, cand, gamma, lg)
+            evs.evs_verify_sample(B, gamma, V, lg, evs.EVS_TARGET_LOGITS_BF16, q, drafts[r], u[r], 1.0, 4, 0,
+                                  acc[r], nxt, keep[r])
+            evs.evs_rollback(state, keep[r])
+        for r in range(W):
+            run(r)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(W, rounds):
+            run(r)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / K
+        emitted = int(keep[W:].sum())
+        assert state.error() == 0, "device error word set"
+        by = batch_round_bytes(cfg, ctx, gamma)
+        print(json.dumps({
+            "workload": "ragged batch: 8 sequences, contexts U{1024..32768}, 7B-shaped hybrid stack",
+            "batch": B, "gamma": gamma, "contexts": [int(c) for c in ctx], "steps": K, "warmup": W,
+            "ms_per_round": round(ms, 4), "positions_per_s": round(B * P / (ms / 1e3), 1),
+            "emitted_tokens_per_s": round(emitted / (ms * K / 1e3), 1),
+            "mean_accepted_drafts_per_sequence": round(float(acc[W:].float().mean()), 3),
+            "algorithmic_bytes_per_round": by, "achieved_hbm_gbps": round(by / (ms / 1e3) / 1e9, 1),
+            "hbm_frac_of_8tbps": round(by / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "note": "random-init weights, drafts uniform over ACGT: acceptance is not the method's; "
+                    "bytes at the starting contexts"}), flush=True)
+
+
 def soak(args):
     """Generation at depth: from the 8192-token prefill, N tokens of native
     greedy decoding, then the same N tokens generated by speculative rounds
@@ -597,6 +671,19 @@ def round_bytes(cfg, ctx, gamma, fp8=False):
     return n
 
 
+def batch_round_bytes(cfg, ctxs, gamma):
+    """round_bytes for a batch of sequences at contexts `ctxs`: the weights,
+    taps, poles and residues once, everything per sequence for each."""
+    d = cfg.d_model
+    shared = matrix_bytes(cfg) + cfg.vocab * d * 2
+    for b in cfg.blocks:
+        if b.kind == "fir":
+            shared += b.fir_len * d * 4
+        elif b.kind == "iir":
+            shared += 2 * d * b.iir_states * 4
+    return shared + sum(round_bytes(cfg, int(c), gamma) - shared for c in ctxs)
+
+
 def cpu_baseline(cfg_full, weights_gpu, ctx, gamma, seed, n_layers):
     """The oracle, as it stands, on one block-verify round over the first
     n_layers layers of the stack from a synthetic committed state at `ctx`;
@@ -642,6 +729,9 @@ def main():
         return
     if args.drafter:
         drafter_bench(args)
+        return
+    if args.c5:
+        c5_bench(args)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.steps, args.warmup)
@@ -790,6 +880,19 @@ def main():
     assert state.error() == 0, "device error word set"
     all_accepted = bool((accepted == gamma).all())
 
+    # ---- per-round latency: an event pair around each round of a third pass
+    state.buf.copy_(snap)
+    for r in range(args.warmup):
+        run_round(r)
+    evs_r = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    for k, r in enumerate(range(args.warmup, rounds)):
+        evs_r[k][0].record()
+        run_round(r)
+        evs_r[k][1].record()
+    torch.cuda.synchronize()
+    per_round = np.array([a.elapsed_time(b) for a, b in evs_r])
+
     # ---- per-launch timing pass over the same rounds
     state.buf.copy_(snap)
     for r in range(args.warmup):
@@ -835,6 +938,8 @@ def main():
         "verification_tax": round(ms / native_step_ms, 4),
         "all_drafts_accepted": all_accepted,
         "wall_ms_per_step": round(wall_ms / args.steps, 4),
+        "round_ms_median": round(float(np.median(per_round)), 4),
+        "round_ms_p90": round(float(np.percentile(per_round, 90)), 4),
         "roofline": {"bound": "hbm", "kernel": "gemm_kernel (skinny bf16 MFMA weight streamer)",
                      "achieved": round(gemm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gemm_gbps / HBM_PEAK_GBPS, 4), "traffic": None if fp8 else gemm_traffic(),

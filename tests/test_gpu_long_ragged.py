@@ -95,14 +95,15 @@ def test_c4_attention_block_at_262k_context():
 # ------------------------------------------------------------------- C5
 def committed_equal(cfg, sa, ba, sb, bb):
     """Committed state of sequence ba of sa equals that of sequence bb of sb:
-    length, FIR windows, the committed IIR modes, all K/V rows."""
+    length, FIR windows (their rows at positions >= 0), the committed IIR modes, all K/V rows."""
     t = int(sa.tensor(evs.EVS_ST_T)[ba])
     if t != int(sb.tensor(evs.EVS_ST_T)[bb]):
         return False
     for i, blk in enumerate(cfg.blocks):
         if blk.kind == "fir":
             ra, rb = sa.tensor(evs.EVS_ST_FIR_RING, i)[ba], sb.tensor(evs.EVS_ST_FIR_RING, i)[bb]
-            rows = torch.as_tensor(np.arange(t - blk.fir_len + 1, t) % ra.shape[0], device=DEV)
+            # positions before 0 are never written (the window reads them as 0)
+            rows = torch.as_tensor(np.arange(max(0, t - blk.fir_len + 1), t) % ra.shape[0], device=DEV)
             if not torch.equal(ra[rows], rb[rows]):
                 return False
         elif blk.kind == "iir":
