@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--summarize-drafter-trace", metavar="KERNEL_TRACE_CSV",
                     help="print the per-call kernel table of the evs_draft calls in a rocprofv3 kernel trace "
                          "of --drafter and exit")
+    ap.add_argument("--summarize-c5-trace", metavar="KERNEL_TRACE_CSV",
+                    help="print the per-round kernel table at each gamma of a rocprofv3 kernel trace of --c5 "
+                         "(pass the same --steps/--warmup as the profiled run) and exit")
     ap.add_argument("--summarize-counters", nargs=4,
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="print the per-launch HBM traffic (JSON) from rocprofv3 FETCH_SIZE / WRITE_SIZE "
@@ -76,9 +79,10 @@ def parse():
 
 GEMM_SOURCES = ("attention_dna_lms_amd/csrc/gemm_impl.h", "attention_dna_lms_amd/csrc/gemm_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_kernel_c3_traffic.json")
-KERNEL_FAMILIES = ("attn_merge_kernel", "gemm_kernel", "attn32_kernel", "attn_kernel", "verify_kernel",
-                   "commit_kernel", "embed_kernel", "draft_reg_kernel", "draft_kernel", "inject_prep_kernel",
-                   "slots_kernel", "export_rows_kernel")
+KERNEL_FAMILIES = ("attn_merge_kernel", "gemm_part_kernel", "gemm_kernel", "attn32_kernel", "attn_kernel",
+                   "verify_kernel", "commit_kernel", "embed_kernel", "norm_rows_kernel", "draft_reg_kernel",
+                   "draft_kernel", "inject_prep_kernel", "slots_kernel", "export_rows_kernel")
+C5_GAMMAS = (1, 4, 8, 12, 16)
 
 
 def gemm_sources_hash():
@@ -161,6 +165,38 @@ def summarize_drafter_trace(path, calls=50):
     print("| kernel | launches/call | avg us | us/call |\n|---|---|---|---|")
     for k, v in sorted(g.items(), key=lambda kv: -sum(kv[1])):
         print(f"| {k} | {len(v) / len(starts):.0f} | {sum(v) / len(v):.2f} | {sum(v) / len(starts):.1f} |")
+
+
+def summarize_c5_trace(path, steps, warmup):
+    """Per-round kernel table at each gamma of a kernel trace of `bench.py --c5`:
+    each gamma runs warmup + steps rounds, every round closed by one commit
+    kernel; the table covers the timed rounds (a round runs from the kernel
+    after the previous commit to its own commit)."""
+    import collections
+    import csv
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    commits = [i for i, r in enumerate(rows) if "commit_kernel" in r["Kernel_Name"]]
+    n = warmup + steps
+    if warmup < 1 or len(commits) < n * len(C5_GAMMAS):
+        raise SystemExit("trace does not hold the --c5 rounds of these --steps/--warmup")
+    commits = commits[-n * len(C5_GAMMAS):]
+    for gi, gamma in enumerate(C5_GAMMAS):
+        g = collections.defaultdict(list)
+        spans = []
+        for r in range(gi * n + warmup, (gi + 1) * n):
+            sel = rows[commits[r - 1] + 1: commits[r] + 1]
+            for x in sel:
+                wg = int(x["Grid_Size_X"]) // max(int(x["Workgroup_Size_X"]), 1)
+                key = f"{family(x, False)} (workgroups {wg}x{x['Grid_Size_Y']}x{x['Grid_Size_Z']})"
+                g[key].append((int(x["End_Timestamp"]) - int(x["Start_Timestamp"])) / 1e3)
+            spans.append((int(sel[-1]["End_Timestamp"]) - int(sel[0]["Start_Timestamp"])) / 1e3)
+        busy = sum(sum(v) for v in g.values()) / steps
+        print(f"### gamma {gamma}\n\n{steps} rounds; first dispatch to last end: {sum(spans) / steps:.1f} us "
+              f"per round; kernel busy time {busy:.1f} us per round\n")
+        print("| kernel | launches/round | avg us | us/round |\n|---|---|---|---|")
+        for k, v in sorted(g.items(), key=lambda kv: -sum(kv[1])):
+            print(f"| {k} | {len(v) / steps:.0f} | {sum(v) / len(v):.2f} | {sum(v) / steps:.1f} |")
+        print()
 
 
 def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, steps, warmup):
@@ -482,7 +518,7 @@ def c5_bench(args):
         import_synthetic_state(evs, es, cfg, state, int(ctx[b]), args.seed + b, dev, b)
     snap = state.buf.clone()
     acgt = torch.tensor(es.ACGT_IDS(V), dtype=torch.int32, device=dev)
-    for gamma in (1, 4, 8, 12, 16):
+    for gamma in C5_GAMMAS:
         P = gamma + 1
         rng = np.random.default_rng([args.seed, 5, gamma])
         drafts = acgt[torch.from_numpy(rng.integers(0, 4, (rounds, B, gamma))).to(dev)]
@@ -735,6 +771,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.steps, args.warmup)
+        return
+    if args.summarize_c5_trace:
+        summarize_c5_trace(args.summarize_c5_trace, args.steps, args.warmup)
         return
     if args.summarize_drafter_trace:
         summarize_drafter_trace(args.summarize_drafter_trace)
