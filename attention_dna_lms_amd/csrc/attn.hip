@@ -193,7 +193,11 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
 // group g) holding the probabilities of keys 8g .. 8g+7: exactly its P^T
 // operand of O^T += V^T P^T, whose V^T operand (head dimension e, keys 8g ..
 // 8g+7) is 16 contiguous bytes of a 16-key value block.
-template <int DH>
+// QG query tiles share one pass over the keys (a block of 17-32 positions
+// reads the cache once); every query's arithmetic is the same whatever tiles
+// share the pass. Tiles past the block's last (an odd tile count) repeat the
+// last query and are not stored.
+template <int DH, int QG>
 __global__ void __launch_bounds__(256, 2) attn32_kernel(AttnArgs a) {
   using T = bf16;
   constexpr int E = 8, KSTEP = 32, NKS = DH / KSTEP, NDT = DH / 16;
@@ -202,34 +206,44 @@ __global__ void __launch_bounds__(256, 2) attn32_kernel(AttnArgs a) {
   __shared__ float wo[4][16][DH];
 
   const int j = blockIdx.x, h = blockIdx.y;
-  const int bl = blockIdx.z / a.QTN, qt = blockIdx.z % a.QTN;
+  const int NG = (a.QTN + QG - 1) / QG;          // tile groups per sequence
+  const int bl = blockIdx.z / NG, qt0 = (blockIdx.z % NG) * QG;
   const int b = a.seq0 + bl;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qc = lane & 15, g = lane >> 4;
   const int t = a.t[b], P = a.P;
   const int kv_len = min(t + P, a.cap);
-  const int pe = min(qt * 16 + qc, P - 1);   // padding queries repeat the last real one
-  const int qpos = t + pe;
   const int k0 = j * a.LS, k1 = min(k0 + a.LS, kv_len);   // this workgroup's keys
 
   const T* qm = reinterpret_cast<const T*>(a.q);
-  uint4 qf[NKS];
+  uint4 qf[QG][NKS];
+  int qpos[QG];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks)
-    qf[ks] = *reinterpret_cast<const uint4*>(qm + act_off<E>(bl * P + pe, h * DH + ks * KSTEP + g * E, a.d));
+  for (int u = 0; u < QG; ++u) {
+    const int pe = min((qt0 + u) * 16 + qc, P - 1);   // padding queries repeat the last real one
+    qpos[u] = t + pe;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qf[u][ks] = *reinterpret_cast<const uint4*>(qm + act_off<E>(bl * P + pe, h * DH + ks * KSTEP + g * E, a.d));
+  }
 
   const T* K = reinterpret_cast<const T*>(a.kc) + (size_t)b * a.kv_bs + (size_t)h * a.cap * DH;
   const T* Vb = reinterpret_cast<const T*>(a.vt) + (size_t)b * a.kv_bs + (size_t)h * DH * a.cap;
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[NDT];
+  float m_run[QG], l_run[QG];
+  f32x4 o[QG][NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < QG; ++u) {
+    m_run[u] = -INFINITY;
+    l_run[u] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // this wave's tiles: key0 = k0 + 32 * (wave + 4 * i). One tile buffer,
   // refilled as soon as it is consumed: the next tile's K loads go out right
-  // after this tile's S^T product, its V loads right after the P V product.
+  // after this tile's S^T products, its V loads right after the P V products.
   // Tiles past the last re-read the last one (inside the cache: the capacity
   // is a multiple of 32) and are never used.
   const int nt_all = (k1 > k0) ? (k1 - k0 + 31) / 32 : 0;
@@ -255,41 +269,52 @@ __global__ void __launch_bounds__(256, 2) attn32_kernel(AttnArgs a) {
   issue_v(0);
   for (int i = 0; i < ntile; ++i) {
     const int key0 = tile_key(i);
-    f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 sc[QG][2];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      sc[0] = mma_frag(kf[0][ks], qf[ks], sc[0], T());
-      sc[1] = mma_frag(kf[1][ks], qf[ks], sc[1], T());
+    for (int u = 0; u < QG; ++u) {
+      sc[u][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        sc[u][0] = mma_frag(kf[0][ks], qf[u][ks], sc[u][0], T());
+        sc[u][1] = mma_frag(kf[1][ks], qf[u][ks], sc[u][1], T());
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     issue_k(i + 1);
     __builtin_amdgcn_sched_barrier(0);
     // lane holds the scores of keys key0 + 8g + 4 * half + r (r < 4) for query qc
     const int kb = key0 + 8 * g;
-    float sv[8];
-    float mt = -INFINITY;
+    uint4 pu[QG];
+    float alpha[QG];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int key = kb + q;
-      sv[q] = (key <= qpos && key < k1) ? sc[q >> 2][q & 3] * a.scale : -INFINITY;
-      mt = fmaxf(mt, sv[q]);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = (m_new == -INFINITY) ? 1.f : expf(m_run - m_new);
-    float ls = 0.f;
-    bf16x8 pb;
+    for (int u = 0; u < QG; ++u) {
+      float sv[8];
+      float mt = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float pv = (sv[q] == -INFINITY) ? 0.f : expf(sv[q] - m_new);
-      ls += pv;
-      pb[q] = (bf16)pv;
+      for (int q = 0; q < 8; ++q) {
+        const int key = kb + q;
+        sv[q] = (key <= qpos[u] && key < k1) ? sc[u][q >> 2][q & 3] * a.scale : -INFINITY;
+        mt = fmaxf(mt, sv[q]);
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float m_new = fmaxf(m_run[u], mt);
+      alpha[u] = (m_new == -INFINITY) ? 1.f : expf(m_run[u] - m_new);
+      float ls = 0.f;
+      bf16x8 pb;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float pv = (sv[q] == -INFINITY) ? 0.f : expf(sv[q] - m_new);
+        ls += pv;
+        pb[q] = (bf16)pv;
+      }
+      ls += __shfl_xor(ls, 16);
+      ls += __shfl_xor(ls, 32);
+      l_run[u] = l_run[u] * alpha[u] + ls;
+      m_run[u] = m_new;
+      pu[u] = __builtin_bit_cast(uint4, pb);
     }
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
     // values of keys past this workgroup's range are zeroed (the cache rows
     // there may hold anything, and 0 * NaN is NaN)
     if (kb + 8 > k1) {
@@ -306,42 +331,50 @@ __global__ void __launch_bounds__(256, 2) attn32_kernel(AttnArgs a) {
       }
     }
     // O^T += V^T P^T: A rows = head dims, B columns = queries, k = the tile's keys
-    const uint4 pu = __builtin_bit_cast(uint4, pb);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      o[dt] = o[dt] * alpha;
-      o[dt] = mma_frag(vf[dt], pu, o[dt], T());
-    }
+    for (int u = 0; u < QG; ++u)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        o[u][dt] = o[u][dt] * alpha[u];
+        o[u][dt] = mma_frag(vf[dt], pu[u], o[u][dt], T());
+      }
     __builtin_amdgcn_sched_barrier(0);
     issue_v(i + 1);
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // merge the 4 waves (fixed order) into this workgroup's partial
-  if (g == 0) { wm[wave][qc] = m_run; wl[wave][qc] = l_run; }
+  // merge the 4 waves (fixed order) into this workgroup's partial, one query
+  // tile at a time
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+  for (int u = 0; u < QG; ++u) {
+    const int qt = qt0 + u;
+    if (qt >= a.QTN) break;   // uniform: an odd tile count's padding tile
+    if (u > 0) __syncthreads();   // the previous tile's merge has read the buffers
+    if (g == 0) { wm[wave][qc] = m_run[u]; wl[wave][qc] = l_run[u]; }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) wo[wave][qc][dt * 16 + 4 * g + q] = o[dt][q];
-  __syncthreads();
-  const size_t head = (size_t)blockIdx.z * a.H + h;
-  float* part = a.part + head * a.S * 16 * ROW;
-  for (int idx = tid; idx < 16 * ROW; idx += 256) {
-    const int q = idx / ROW, e = idx % ROW;
-    float M = -INFINITY;
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][q]);
-    float v = 0.f;
-    if (e == DH) {
-      v = M;
-    } else {
+      for (int q = 0; q < 4; ++q) wo[wave][qc][dt * 16 + 4 * g + q] = o[u][dt][q];
+    __syncthreads();
+    const size_t head = ((size_t)bl * a.QTN + qt) * a.H + h;
+    float* part = a.part + head * a.S * 16 * ROW;
+    for (int idx = tid; idx < 16 * ROW; idx += 256) {
+      const int q = idx / ROW, e = idx % ROW;
+      float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float f = (wm[w][q] == -INFINITY) ? 0.f : expf(wm[w][q] - M);
-        v += (e < DH ? wo[w][q][e] : wl[w][q]) * f;
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][q]);
+      float v = 0.f;
+      if (e == DH) {
+        v = M;
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float f = (wm[w][q] == -INFINITY) ? 0.f : expf(wm[w][q] - M);
+          v += (e < DH ? wo[w][q][e] : wl[w][q]) * f;
+        }
       }
+      part[((size_t)j * 16 + q) * ROW + e] = v;
     }
-    part[((size_t)j * 16 + q) * ROW + e] = v;
   }
 }
 
@@ -395,18 +428,33 @@ hipError_t launch_attn(const AttnArgs& a, int n_seq, hipStream_t st) {
   // multiple of 256, so a range's last tile stays inside the cache)
   if (a.S > 64 || a.S < 1 || a.LS < 16 || a.LS % 16 || a.cap % 256) return hipErrorInvalidValue;
   dim3 grid(a.S, a.H, n_seq * a.QTN), block(256), mgrid(a.Dh / 16, a.H, n_seq * a.QTN);
+  // bf16: query tiles in pairs (grid z = sequence x tile pair)
+  dim3 grid2(a.S, a.H, n_seq * ((a.QTN + 1) / 2));
   constexpr bool B16 = sizeof(T) == 2;
+  const bool pair = a.QTN >= 2;
   switch (a.Dh) {
     case 32:
-      if constexpr (B16) attn32_kernel<32><<<grid, block, 0, st>>>(a); else attn_kernel<T, 32><<<grid, block, 0, st>>>(a);
+      if constexpr (B16) {
+        if (pair) attn32_kernel<32, 2><<<grid2, block, 0, st>>>(a); else attn32_kernel<32, 1><<<grid, block, 0, st>>>(a);
+      } else {
+        attn_kernel<T, 32><<<grid, block, 0, st>>>(a);
+      }
       attn_merge_kernel<T, 32><<<mgrid, block, 0, st>>>(a);
       break;
     case 64:
-      if constexpr (B16) attn32_kernel<64><<<grid, block, 0, st>>>(a); else attn_kernel<T, 64><<<grid, block, 0, st>>>(a);
+      if constexpr (B16) {
+        if (pair) attn32_kernel<64, 2><<<grid2, block, 0, st>>>(a); else attn32_kernel<64, 1><<<grid, block, 0, st>>>(a);
+      } else {
+        attn_kernel<T, 64><<<grid, block, 0, st>>>(a);
+      }
       attn_merge_kernel<T, 64><<<mgrid, block, 0, st>>>(a);
       break;
     case 128:
-      if constexpr (B16) attn32_kernel<128><<<grid, block, 0, st>>>(a); else attn_kernel<T, 128><<<grid, block, 0, st>>>(a);
+      if constexpr (B16) {
+        if (pair) attn32_kernel<128, 2><<<grid2, block, 0, st>>>(a); else attn32_kernel<128, 1><<<grid, block, 0, st>>>(a);
+      } else {
+        attn_kernel<T, 128><<<grid, block, 0, st>>>(a);
+      }
       attn_merge_kernel<T, 128><<<mgrid, block, 0, st>>>(a);
       break;
     default: return hipErrorInvalidValue;
