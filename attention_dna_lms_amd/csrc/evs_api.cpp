@@ -22,6 +22,7 @@ constexpr int MAX_ROWS_PER_WG = 144;   // 9 MFMA row tiles
 constexpr int SPLIT_MT = 7;            // row tiles from which bf16 launches split K across workgroups
 constexpr int GEMM_WAVES = 8;          // waves per GEMM workgroup (gemm_kernel default)
 constexpr int ATTN_CUS = 256;          // compute units the attention split count is sized for
+constexpr size_t LDS_MAX = 163840;     // LDS one workgroup may use on gfx950 (160 KB)
 
 size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
 int next_pow2(int x) { int p = 1; while (p < x) p <<= 1; return p; }
@@ -383,7 +384,7 @@ evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int 
   const double bytes = (double)(mat.bytes(m->es) + mat.scale_bytes()) + (double)a.M * mat.K * (amode == A_NORM ? 4 : m->es) +
                        (double)a.M * mat.rows_valid * (epi == E_RESID ? 8 : m->es);
   const size_t lds = gemm_lds(sl.MT, mat.NT, scratch_floats);
-  if (lds > 65536) return EVS_E_UNSUPPORTED;
+  if (lds > LDS_MAX) return EVS_E_UNSUPPORTED;
   // multi-tile bf16 launches over normed rows: k-range partials, then the
   // reduction and epilogue (the same results as one kernel)
   if (m->desc.dtype == EVS_BF16 && !mat.w8 && amode == A_ACT && sl.MT >= SPLIT_MT &&
@@ -458,7 +459,13 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
       mx.kind = MIX_FIR;
       mx.ring = sp<float>(s, s->ring[i]); mx.R = s->R[i]; mx.ring_bs = (long long)s->R[i] * d;
       mx.taps = reinterpret_cast<const float*>(m->base + p.taps); mx.L = p.d.fir_len;
-      scratch = (p.d.fir_len - 1 + P) * 16 + 16 * (p.d.fir_len | 1);   // window + taps (odd row stride)
+      // taps (odd row stride) + the windows and inputs of fb sequences: the
+      // most of a slice's sequences (up to FIR_FB) that fit the workgroup's LDS
+      const Slicing sl = slicing(nseq, P);
+      const int per_seq = (p.d.fir_len - 1 + P) * 16, taps_f = 16 * (p.d.fir_len | 1);
+      mx.fb = std::min(FIR_FB, sl.rows_per_slice / P);
+      while (mx.fb > 1 && gemm_lds(sl.MT, p.w_in.NT, taps_f + mx.fb * per_seq) > LDS_MAX) --mx.fb;
+      scratch = taps_f + mx.fb * per_seq;
       a.out = wp<void>(s, s->w_o);
     } else if (p.d.kind == EVS_IIR) {
       mx.kind = MIX_IIR;
@@ -467,10 +474,11 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
       mx.iir_bs = 2 * mx.iir_buf_s;
       mx.lam = reinterpret_cast<const float*>(m->base + p.lam);
       mx.res = reinterpret_cast<const float*>(m->base + p.res);
-      scratch = IIR_CH * 256 + 256;   // one chunk of modes + the residues
+      scratch = 0;   // the epilogue works in registers and DPP rows
       a.out = wp<void>(s, s->w_o);
     } else {
       mx.kind = MIX_ATTN;
+      scratch = MAX_ROWS_PER_WG;   // the slice's committed lengths
       mx.kc = sp<void>(s, s->kc[i]); mx.vt = sp<void>(s, s->vt[i]);
       mx.kv_bs = (long long)p.d.n_heads * s->cap * p.d.head_dim; mx.cap = s->cap; mx.Dh = p.d.head_dim;
       a.out = wp<void>(s, s->w_q);

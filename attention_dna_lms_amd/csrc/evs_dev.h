@@ -87,6 +87,7 @@ struct MixArgs {
   int* err;              // sticky error word
   // FIR
   float* ring; int R; long long ring_bs; const float* taps; int L;
+  int fb;                // sequences whose windows the epilogue stages together (1 .. FIR_FB)
   // IIR
   float* iirst; long long iir_bs; long long iir_buf_s; int N; const float* lam; const float* res;
   // ATTN
@@ -130,6 +131,8 @@ struct AttnArgs {
 
 constexpr int ATTN_CHUNK = 256;   // the KV capacity is a multiple of this many keys
 constexpr int IIR_CH = 16;        // positions per chunk of the IIR mixer epilogue
+constexpr int IIR_FB = 8;         // sequences whose committed IIR modes are loaded together
+constexpr int FIR_FB = 8;         // most sequences whose FIR windows are staged together
 
 struct VerifyArgs {
   int gamma, V, kind, top_k, greedy;

@@ -73,6 +73,13 @@ template <> struct AFrag<float, A_NORM> {                 // fp32 rows, RMSNorm 
   }
 };
 
+// each 16-lane row rotated by K lanes (DPP row_ror): a lane receives the value
+// of the lane K away in its own row
+template <int K>
+__device__ __forceinline__ float dpp_row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + K, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float gelu_f(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
 }
@@ -118,17 +125,22 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, EpiPre& pf, int 
         const int tc = idx / x.L, tj = idx % x.L;
         pf.tap[q] = idx < 16 * x.L ? x.taps[(size_t)(ch0 + tc) * x.L + tj] : 0.f;
       }
-    } else if (x.kind == MIX_IIR && tid < 256) {
-      const int c = tid >> 4, n = tid & 15, ch = ch0 + c;
+    } else if (x.kind == MIX_IIR) {
+      // every thread: its channel's pole and residue of mode n; the first 256
+      // (the first sequence's threads): that sequence's committed mode
+      const int c = (tid >> 4) & 15, n = tid & 15, ch = ch0 + c;
       const bool vn = n < x.N;
-      const int b = x.seq0 + row0 / x.P;
-      const int buf = x.iir_buf[b], slot = x.iir_slot[b];
-      const float* base = x.iirst + (size_t)b * x.iir_bs;
-      const size_t so = (size_t)buf * x.iir_buf_s + ((size_t)(slot < 0 ? 0 : slot) * x.d + ch) * x.N + (vn ? n : 0);
-      const float sv = base[so];
-      pf.s0 = (vn && slot >= 0) ? sv : 0.f;
       pf.lam = vn ? x.lam[(size_t)ch * x.N + n] : 0.f;
       pf.res = vn ? x.res[(size_t)ch * x.N + n] : 0.f;
+      pf.s0 = 0.f;
+      if (tid < 256) {
+        const int b = x.seq0 + row0 / x.P;
+        const int buf = x.iir_buf[b], slot = x.iir_slot[b];
+        const float* base = x.iirst + (size_t)b * x.iir_bs;
+        const size_t so = (size_t)buf * x.iir_buf_s + ((size_t)(slot < 0 ? 0 : slot) * x.d + ch) * x.N + (vn ? n : 0);
+        const float sv = base[so];
+        pf.s0 = (vn && slot >= 0) ? sv : 0.f;
+      }
     }
   }
 }
@@ -186,13 +198,19 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
     const int P = x.P;
     const int nseq = rows / P;
     const int sbase = x.seq0 + row0 / P;
+    // (every per-sequence value is loaded before the first store: on this
+    // GPU stores and loads share one in-order counter, so a load issued after
+    // a store waits for the store too)
     if (x.kind == MIX_ATTN) {
       T* kc = reinterpret_cast<T*>(x.kc);
       T* vt = reinterpret_cast<T*>(x.vt);
+      int* tl = reinterpret_cast<int*>(scratch);   // [nseq] committed lengths
+      for (int j = tid; j < nseq; j += nth) tl[j] = x.t[sbase + j];
+      __syncthreads();
       for (int idx = tid; idx < rows * 16; idx += nth) {
         const int m = idx / 16, c = idx & 15;
         const int b = sbase + m / P, p = m % P;
-        const int pos = x.t[b] + p;
+        const int pos = tl[m / P] + p;
         const int ch = ch0 + c, h = ch / x.Dh, dh = ch % x.Dh;
         out[act_off<St<T>::E>(row0 + m, ch, a.ldo)] = from_f<T>(eq[idx]);
         if (pos < x.cap) {
@@ -204,11 +222,15 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
         }
       }
     } else if (x.kind == MIX_FIR) {
-      const int L = x.L, W = L - 1 + P;
+      // Sequences in batches of x.fb: the windows of a batch are loaded
+      // together (one memory round trip per batch), its inputs h = k v written
+      // to LDS and to each ring, then every (sequence, position, channel)
+      // output of the batch is formed in one pass.
+      const int L = x.L, LW = L - 1, WR = LW + P;   // window rows; rows per sequence buffer
       const int LP = L | 1;            // odd row stride: the 16 channels' taps sit in 16 distinct banks
       const bool pre = L <= FIR_PRE * 32;
       float* tp = scratch;             // [16][LP] taps
-      float* hw = scratch + 16 * LP;   // [W][16]: filter inputs at positions t-L+1 .. t+P-1
+      float* hb = scratch + 16 * LP;   // [fb][WR][16]: a sequence's inputs at positions t-L+1 .. t+P-1
       if (pre) {
 #pragma unroll
         for (int q = 0; q < FIR_PRE; ++q) {
@@ -218,34 +240,81 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
       } else {
         for (int idx = tid; idx < 16 * L; idx += nth) tp[(idx / L) * LP + idx % L] = x.taps[(size_t)(ch0 + idx / L) * L + idx % L];
       }
-      for (int j = 0; j < nseq; ++j) {
-        const int b = sbase + j;
-        const int tb = x.t[b];
-        float* ring = x.ring + (size_t)b * x.ring_bs;
-        if (j == 0 && pre) {
+      const int fb = max(1, min(x.fb, FIR_FB));
+      for (int j0 = 0; j0 < nseq; j0 += fb) {
+        const int nb = min(fb, nseq - j0);
+        // committed lengths and windows of the batch: every load unconditional
+        // (indices clamped to the batch), so all are in flight together; a
+        // single-sequence launch keeps the window loaded with the prologue
+        int tbv[FIR_FB];
 #pragma unroll
-          for (int q = 0; q < FIR_PRE; ++q) {
-            const int idx = tid + q * 512;
-            if (idx < (L - 1) * 16) hw[idx] = pf.win[q];
+        for (int u = 0; u < FIR_FB; ++u) tbv[u] = x.t[sbase + j0 + min(u, nb - 1)];
+        if (pre) {
+          float wv[FIR_FB][FIR_PRE];
+          if (nseq == 1) {
+#pragma unroll
+            for (int q = 0; q < FIR_PRE; ++q) wv[0][q] = pf.win[q];
+          } else {
+            // the loads as one group between scheduling barriers, then the
+            // masking (pos < 0 reads as 0; ring rows are always in range)
+#pragma unroll
+            for (int u = 0; u < FIR_FB; ++u) {
+              const float* ring = x.ring + (size_t)(sbase + j0 + min(u, nb - 1)) * x.ring_bs;
+#pragma unroll
+              for (int q = 0; q < FIR_PRE; ++q) {
+                const int idx = tid + q * 512;
+                wv[u][q] = ring[(size_t)((tbv[u] - LW + (idx >> 4)) & (x.R - 1)) * x.d + ch0 + (idx & 15)];
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < FIR_FB; ++u)
+#pragma unroll
+              for (int q = 0; q < FIR_PRE; ++q) {
+                const int idx = tid + q * 512, jw = idx >> 4;
+                const int pos = tbv[u] - LW + jw;
+                const unsigned keep = (jw < LW && pos >= 0) ? 0xffffffffu : 0u;
+                wv[u][q] = __uint_as_float(__float_as_uint(wv[u][q]) & keep);
+              }
+          }
+#pragma unroll
+          for (int u = 0; u < FIR_FB; ++u) {
+            if (u < nb) {
+#pragma unroll
+              for (int q = 0; q < FIR_PRE; ++q) {
+                const int idx = tid + q * 512;
+                if (idx < LW * 16) hb[u * WR * 16 + idx] = wv[u][q];
+              }
+            }
           }
         } else {
-          for (int idx = tid; idx < (L - 1) * 16; idx += nth) {
-            const int pos = tb - (L - 1) + (idx >> 4);
-            const float v = ring[(size_t)(pos & (x.R - 1)) * x.d + ch0 + (idx & 15)];
-            hw[idx] = pos >= 0 ? v : 0.f;
+          for (int idx = tid; idx < nb * LW * 16; idx += nth) {
+            const int u = idx / (LW * 16), r = idx % (LW * 16);
+            const int b = sbase + j0 + u;
+            int tb = 0;
+#pragma unroll
+            for (int v = 0; v < FIR_FB; ++v) tb = v == u ? tbv[v] : tb;
+            const int pos = tb - LW + (r >> 4);
+            const float v = x.ring[(size_t)b * x.ring_bs + (size_t)(pos & (x.R - 1)) * x.d + ch0 + (r & 15)];
+            hb[u * WR * 16 + r] = pos >= 0 ? v : 0.f;
           }
         }
-        for (int idx = tid; idx < P * 16; idx += nth) {
-          const int p = idx >> 4, c = idx & 15, m = j * P + p;
+        for (int idx = tid; idx < nb * P * 16; idx += nth) {
+          const int u = idx / (P * 16), r = idx % (P * 16), p = r >> 4, c = r & 15;
+          const int b = sbase + j0 + u, m = (j0 + u) * P + p;
           const float h = rnd<T>(ek[m * 16 + c]) * rnd<T>(ev[m * 16 + c]);
-          hw[(L - 1) * 16 + idx] = h;
-          ring[(size_t)((tb + p) & (x.R - 1)) * x.d + ch0 + c] = h;
+          int tb = 0;
+#pragma unroll
+          for (int v = 0; v < FIR_FB; ++v) tb = v == u ? tbv[v] : tb;
+          hb[(u * WR + LW) * 16 + r] = h;
+          x.ring[(size_t)b * x.ring_bs + (size_t)((tb + p) & (x.R - 1)) * x.d + ch0 + c] = h;
         }
         __syncthreads();
-        for (int idx = tid; idx < P * 16; idx += nth) {
-          const int p = idx >> 4, c = idx & 15, m = j * P + p;
+        for (int idx = tid; idx < nb * P * 16; idx += nth) {
+          const int u = idx / (P * 16), r = idx % (P * 16), p = r >> 4, c = r & 15;
+          const int m = (j0 + u) * P + p;
           const float* tc = tp + c * LP;
-          const float* hc = hw + (L - 1 + p) * 16 + c;   // input at lag jj: hc[-16 * jj]
+          const float* hc = hb + (u * WR + LW + p) * 16 + c;   // input at lag jj: hc[-16 * jj]
           // taps in order 0 .. L-1 (one fma chain); the LDS reads of 16 taps go
           // out together ahead of their fmas
           float y = 0.f;
@@ -262,66 +331,90 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
         }
         __syncthreads();
       }
-      (void)W;
     } else {  // MIX_IIR
-      // Per chunk of up to IIR_CH positions: (1) lanes (c, n), the 16 modes of
-      // one channel in 16 adjacent lanes, run the recurrence in position order
-      // (one fma per step), writing every position's modes to the state and to
-      // LDS; (2) threads (position, channel) sum the 16 mode contributions in
-      // the fixed order ((r0+r8)+(r4+r12)) + ((r2+r10)+(r6+r14)) +
-      // (((r1+r9)+(r5+r13)) + ((r3+r11)+(r7+r15))).
-      float* sb = scratch;                    // [IIR_CH][16 channels][16 modes]
-      float* rb = scratch + IIR_CH * 256;     // [16 channels][16 modes] residues
-      const int c = (tid >> 4) & 15, n = tid & 15, ch = ch0 + c;
+      // Thread (half h, channel c, mode n): the 16 modes of a channel sit in
+      // one 16-lane DPP row; the two halves of the workgroup take two
+      // sequences at a time. Per position: the recurrence step s = lam s + h
+      // (serial in position order, one fma), the mode to the state, r = res s,
+      // and the row's 16 r summed by rotate-and-add over 8, 4, 2, 1 lanes:
+      // every addition pairs the same two partial sums in either rotation
+      // direction, so the row's first lane holds exactly
+      // ((r0+r8)+(r4+r12)) + ((r2+r10)+(r6+r14)) +
+      // (((r1+r9)+(r5+r13)) + ((r3+r11)+(r7+r15))). No barrier: the inputs
+      // are the epilogue tile in LDS, the outputs go to memory.
+      const int half = tid >> 8, c = (tid >> 4) & 15, n = tid & 15, ch = ch0 + c;
       const bool vn = n < x.N;
-      for (int j = 0; j < nseq; ++j) {
-        const int b = sbase + j;
-        const int buf = x.iir_buf[b], slot = x.iir_slot[b];
-        float* base = x.iirst + (size_t)b * x.iir_bs;
-        float s = 0.f, lam = 0.f;
-        if (tid < 256) {
-          float res;
-          if (j == 0) {
-            s = pf.s0; lam = pf.lam; res = pf.res;
-          } else {
-            s = (vn && slot >= 0) ? base[(size_t)buf * x.iir_buf_s + ((size_t)slot * x.d + ch) * x.N + n] : 0.f;
-            lam = vn ? x.lam[(size_t)ch * x.N + n] : 0.f;
-            res = vn ? x.res[(size_t)ch * x.N + n] : 0.f;
-          }
-          rb[tid] = res;
+      const int nr = (nseq + 1) / 2;   // rounds of two sequences
+      for (int r0 = 0; r0 < nr; r0 += IIR_FB / 2) {
+        constexpr int RB = IIR_FB / 2;
+        const int nb = min(RB, nr - r0);
+        // this half's sequences of the batch (clamped: a missing odd sequence
+        // repeats the last and is skipped below)
+        int dbv[RB], slv[RB];
+        float sv[RB];
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+          const int j = min(2 * (r0 + min(u, nb - 1)) + half, nseq - 1);
+          dbv[u] = x.iir_buf[sbase + j];
+          slv[u] = x.iir_slot[sbase + j];
         }
-        float* dst = base + (size_t)(buf ^ 1) * x.iir_buf_s;
-        for (int p0 = 0; p0 < P; p0 += IIR_CH) {
-          const int np = min(IIR_CH, P - p0);
-          if (tid < 256) {
-            float hv[IIR_CH];
+        if (nseq == 1) {
 #pragma unroll
-            for (int q = 0; q < IIR_CH; ++q) {
-              const int m = j * P + p0 + min(q, np - 1);
-              hv[q] = rnd<T>(ek[m * 16 + c]) * rnd<T>(ev[m * 16 + c]);
-            }
+          for (int u = 0; u < RB; ++u) sv[u] = pf.s0;
+        } else {
+          // addresses, then the loads as one group (scheduling barriers keep
+          // the compiler from issuing them one round trip at a time), then v,
+          // or +0 for padding modes and an empty state (a mask, not a select,
+          // which would become a branch around each load)
+          const float* ap[RB];
 #pragma unroll
-            for (int q = 0; q < IIR_CH; ++q) {
-              if (q < np) {
-                s = fmaf(lam, s, hv[q]);
-                if (vn) dst[((size_t)(p0 + q) * x.d + ch) * x.N + n] = s;
-                sb[q * 256 + tid] = s;
+          for (int u = 0; u < RB; ++u) {
+            const int j = min(2 * (r0 + min(u, nb - 1)) + half, nseq - 1);
+            ap[u] = x.iirst + (size_t)(sbase + j) * x.iir_bs + (size_t)dbv[u] * x.iir_buf_s +
+                    ((size_t)(slv[u] < 0 ? 0 : slv[u]) * x.d + ch) * x.N + (vn ? n : 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          float v[RB];
+#pragma unroll
+          for (int u = 0; u < RB; ++u) v[u] = *ap[u];
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < RB; ++u) {
+            const unsigned keep = (vn && slv[u] >= 0) ? 0xffffffffu : 0u;
+            sv[u] = __uint_as_float(__float_as_uint(v[u]) & keep);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+          const int j = 2 * (r0 + u) + half;
+          if (u < nb && j < nseq) {   // uniform per wave
+            float s = sv[u];
+            const float lam = pf.lam, res = pf.res;
+            float* dst = x.iirst + (size_t)(sbase + j) * x.iir_bs + (size_t)(dbv[u] ^ 1) * x.iir_buf_s;
+            for (int p0 = 0; p0 < P; p0 += IIR_CH) {
+              const int np = min(IIR_CH, P - p0);
+              float hv[IIR_CH];
+#pragma unroll
+              for (int q = 0; q < IIR_CH; ++q) {
+                const int m = j * P + p0 + min(q, np - 1);
+                hv[q] = rnd<T>(ek[m * 16 + c]) * rnd<T>(ev[m * 16 + c]);
+              }
+#pragma unroll
+              for (int q = 0; q < IIR_CH; ++q) {
+                if (q < np) {
+                  const int m = j * P + p0 + q;
+                  s = fmaf(lam, s, hv[q]);
+                  if (vn) dst[((size_t)(p0 + q) * x.d + ch) * x.N + n] = s;
+                  float rs = vn ? res * s : 0.f;
+                  rs += dpp_row_ror<8>(rs);
+                  rs += dpp_row_ror<4>(rs);
+                  rs += dpp_row_ror<2>(rs);
+                  rs += dpp_row_ror<1>(rs);
+                  if (n == 0) out[act_off<St<T>::E>(row0 + m, ch, a.ldo)] = from_f<T>(rnd<T>(eq[m * 16 + c]) * rs);
+                }
               }
             }
           }
-          __syncthreads();
-          for (int idx = tid; idx < np * 16; idx += nth) {
-            const int q = idx >> 4, cc = idx & 15, m = j * P + p0 + q;
-            const float* sp = sb + q * 256 + cc * 16;
-            const float* rp = rb + cc * 16;
-            float r[16];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) r[k] = k < x.N ? rp[k] * sp[k] : 0.f;
-            const float tot = (((r[0] + r[8]) + (r[4] + r[12])) + ((r[2] + r[10]) + (r[6] + r[14]))) +
-                              (((r[1] + r[9]) + (r[5] + r[13])) + ((r[3] + r[11]) + (r[7] + r[15])));
-            out[act_off<St<T>::E>(row0 + m, ch0 + cc, a.ldo)] = from_f<T>(rnd<T>(eq[m * 16 + cc]) * tot);
-          }
-          __syncthreads();
         }
       }
     }
