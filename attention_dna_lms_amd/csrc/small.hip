@@ -58,12 +58,19 @@ template hipError_t launch_embed<float>(const int*, const float*, float*, float*
 // (32 lanes per row, each adding its partials j + 32q, q < 8, in a fixed tree
 // per 256 partials, then a butterfly over the 32; 1 / sqrt(sum / K + eps)), so
 // u holds, bit for bit, the operands that prologue builds in registers.
-// One workgroup per row; each thread converts runs of 8 columns.
+// Workgroup (row, 2048-column chunk); each thread converts one run of 8
+// columns. The run is loaded first, so its latency overlaps the scale's (each
+// workgroup of a row forms the same scale from the same partials).
 __global__ void __launch_bounds__(256) norm_rows_kernel(const float* __restrict__ x, const float* __restrict__ nrm,
                                                         int n_part, int nrm_ld, float fd, float eps, int K,
                                                         bf16* __restrict__ u) {
   __shared__ float rinv_s;
   const int m = blockIdx.x, tid = threadIdx.x;
+  const int c = (blockIdx.y * 256 + tid) * 8;
+  const bool live = c < K;
+  const size_t o = act_off<8>(m, live ? c : 0, K);
+  const float4 lo = *reinterpret_cast<const float4*>(x + o);
+  const float4 hi = *reinterpret_cast<const float4*>(x + o + 4);
   if (tid < 32) {
     const int j = tid;
     float sum = 0.f;
@@ -82,10 +89,7 @@ __global__ void __launch_bounds__(256) norm_rows_kernel(const float* __restrict_
   }
   __syncthreads();
   const float r = rinv_s;
-  for (int c = tid * 8; c < K; c += 256 * 8) {
-    const size_t o = act_off<8>(m, c, K);
-    const float4 lo = *reinterpret_cast<const float4*>(x + o);
-    const float4 hi = *reinterpret_cast<const float4*>(x + o + 4);
+  if (live) {
     bf16x8 b;
     b[0] = (bf16)(lo.x * r); b[1] = (bf16)(lo.y * r); b[2] = (bf16)(lo.z * r); b[3] = (bf16)(lo.w * r);
     b[4] = (bf16)(hi.x * r); b[5] = (bf16)(hi.y * r); b[6] = (bf16)(hi.z * r); b[7] = (bf16)(hi.w * r);
@@ -96,7 +100,7 @@ __global__ void __launch_bounds__(256) norm_rows_kernel(const float* __restrict_
 hipError_t launch_norm_rows(const float* x, const float* nrm, int n_part, int nrm_ld, float fd, float eps, int M,
                             int K, bf16* u, hipStream_t st) {
   if (M <= 0) return hipSuccess;
-  norm_rows_kernel<<<M, 256, 0, st>>>(x, nrm, n_part, nrm_ld, fd, eps, K, u);
+  norm_rows_kernel<<<dim3(M, (K + 2047) / 2048), 256, 0, st>>>(x, nrm, n_part, nrm_ld, fd, eps, K, u);
   return hipGetLastError();
 }
 
