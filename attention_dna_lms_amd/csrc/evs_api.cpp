@@ -674,6 +674,10 @@ static evs_status state_setup(const evs_model* m, int32_t batch, int32_t max_ctx
     int s0 = ATTN_CUS / heads;
     s0 = std::min(std::min(64, s0), s->cap / 64);
     s0 = std::max(1, s0);
+    // mid-size capacities (batches of mixed contexts): ranges of ~2048 keys,
+    // so sequences far shorter than the capacity still spread over many
+    // workgroups and the longest do not leave a tail
+    if (s->cap >= 16384 && s->cap <= 65536) s0 = std::max(s0, std::min(64, s->cap / 2048));
     s->LS = (int)align_up((size_t)((s->cap + s0 - 1) / s0), 64);
     s->S = (s->cap + s->LS - 1) / s->LS;
   }
