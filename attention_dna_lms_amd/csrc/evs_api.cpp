@@ -414,16 +414,19 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
   float* nrm = wp<float>(s, s->w_nrm);
   int* t = sp<int>(s, s->off_t);
   int* err = sp<int>(s, s->off_err);
-  // Launches of more than one 16-row tile (bf16 models) read the normed rows
-  // from a norm kernel (the same bf16 operands the fused prologue would form,
-  // so results are unchanged): one bf16 load per step instead of two fp32
-  // loads per tile and step, and half the registers for the operands.
-  const bool pre_norm = sizeof(T) == 2 && m->desc.dtype == EVS_BF16 && slicing(nseq, P).MT >= 2;
-  auto normed = [&](int& amode, const void*& A) -> evs_status {
+  // bf16 models: the gate/up projection, and every normed projection of a
+  // launch of more than one 16-row tile, read the normed rows from a norm
+  // kernel (the same bf16 operands the fused prologue would form, so results
+  // are unchanged): one bf16 load per step instead of two fp32 loads per tile
+  // and step, and half the registers for the operands. A single-tile
+  // in-projection or LM head saves less than the extra launch costs.
+  const bool bf16_model = sizeof(T) == 2 && m->desc.dtype == EVS_BF16;
+  const bool multi_tile = slicing(nseq, P).MT >= 2;
+  auto normed = [&](int& amode, const void*& A, bool gate_up = false) -> evs_status {
     amode = A_NORM;
     A = x;
     if constexpr (sizeof(T) == 2) {
-      if (pre_norm) {
+      if (bf16_model && (multi_tile || gate_up)) {
         bf16* u = wp<bf16>(s, s->w_u);
         HIP_TRY(launch_norm_rows(x, nrm, d / 16, s->M_max, (float)d, m->desc.norm_eps, M, d, u, st));
         amode = A_ACT;
@@ -444,7 +447,7 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
       a.ldo = p.d.d_ff;
       int am;
       const void* A;
-      EVS_TRY(normed(am, A));
+      EVS_TRY(normed(am, A, true));
       EVS_TRY(gemm_call<T>(m, s, p.w_gu, am, E_GELU, A, d, nseq, P, a, st));
       GemmArgs b{};
       b.x = x; b.ldx = d; b.nrm_out = nrm;

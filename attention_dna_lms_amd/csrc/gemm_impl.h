@@ -456,7 +456,9 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   // (measured at the 7B shapes: 4 steps for single-tile projections, 2 for
   // the gate/up pairs, the register bound for the in-projection triples)
   constexpr int PER = 16 / (NT + KPW * AREG * MT);
-  constexpr int CAP = NT == 1 ? 4 : NT == 2 ? 2 : 8;
+  // (a single-tile gate/up over bf16 rows keeps 4 steps: one 16-byte
+  // activation load per step leaves the registers for them)
+  constexpr int CAP = NT == 1 ? 4 : NT == 2 ? (AMODE == A_ACT && MT == 1 ? 4 : 2) : 8;
   constexpr int CH = CHO ? CHO : PER < 1 ? 1 : PER < CAP ? PER : CAP;
   extern __shared__ float lds[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -887,17 +889,20 @@ template <typename T, int MT>
 static hipError_t launch_gemm_mt(int NT, int amode, int epi, const GemmArgs& a, int slices,
                                  size_t lds, hipStream_t st) {
   dim3 grid(a.n_groups, slices), block(512);
-  if (NT == 3 && amode == A_NORM && epi == E_MIXER)
-    gemm_kernel<T, MT, 3, A_NORM, E_MIXER><<<grid, block, lds, st>>>(a);
-  else if (NT == 1 && amode == A_ACT && epi == E_RESID)
+  if (NT == 3 && amode == A_NORM && epi == E_MIXER) {
+    // single tile: 2-step chunks (a wave's 16 steps at the 7B shapes in whole
+    // chunk pairs; measured 17.9 us against 20.7 us for 3-step chunks)
+    if constexpr (MT == 1) gemm_kernel<T, 1, 3, A_NORM, E_MIXER, 8, 2><<<grid, block, lds, st>>>(a);
+    else gemm_kernel<T, MT, 3, A_NORM, E_MIXER><<<grid, block, lds, st>>>(a);
+  } else if (NT == 1 && amode == A_ACT && epi == E_RESID)
     gemm_kernel<T, MT, 1, A_ACT, E_RESID><<<grid, block, lds, st>>>(a);
   else if (NT == 2 && amode == A_NORM && epi == E_GELU)
     gemm_kernel<T, MT, 2, A_NORM, E_GELU><<<grid, block, lds, st>>>(a);
   else if (NT == 1 && amode == A_NORM && epi == E_STORE)
     gemm_kernel<T, MT, 1, A_NORM, E_STORE><<<grid, block, lds, st>>>(a);
-  else if constexpr (sizeof(T) == 2 && MT >= 2) {
-    // multi-tile bf16 launches of the normed projections may take rows the
-    // norm kernel already formed (bf16(x * rinv), the same operands)
+  else if constexpr (sizeof(T) == 2) {
+    // bf16 launches of the normed projections may take rows the norm kernel
+    // already formed (bf16(x * rinv), the same operands)
     if (NT == 3 && amode == A_ACT && epi == E_MIXER)
       gemm_kernel<T, MT, 3, A_ACT, E_MIXER><<<grid, block, lds, st>>>(a);
     else if (NT == 2 && amode == A_ACT && epi == E_GELU)
