@@ -419,14 +419,16 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
   // kernel (the same bf16 operands the fused prologue would form, so results
   // are unchanged): one bf16 load per step instead of two fp32 loads per tile
   // and step, and half the registers for the operands. A single-tile
-  // in-projection or LM head saves less than the extra launch costs.
-  const bool bf16_model = sizeof(T) == 2 && m->desc.dtype == EVS_BF16;
+  // in-projection or LM head saves less than the extra launch costs. FP8
+  // weights: the single-tile gate/up only.
   const bool multi_tile = slicing(nseq, P).MT >= 2;
+  const bool bf16_w = sizeof(T) == 2 && m->desc.dtype == EVS_BF16;
+  const bool fp8_w = sizeof(T) == 2 && m->desc.dtype == EVS_BF16_FP8W;
   auto normed = [&](int& amode, const void*& A, bool gate_up = false) -> evs_status {
     amode = A_NORM;
     A = x;
     if constexpr (sizeof(T) == 2) {
-      if (bf16_model && (multi_tile || gate_up)) {
+      if ((bf16_w && (multi_tile || gate_up)) || (fp8_w && gate_up && !multi_tile)) {
         bf16* u = wp<bf16>(s, s->w_u);
         HIP_TRY(launch_norm_rows(x, nrm, d / 16, s->M_max, (float)d, m->desc.norm_eps, M, d, u, st));
         amode = A_ACT;

@@ -928,8 +928,11 @@ static hipError_t launch_gemm_w8_mt(int NT, int amode, int epi, const GemmArgs& 
     // one row tile: one-step chunks within 128 VGPRs, so two workgroups share a CU
     if constexpr (MT == 1) gemm_kernel<bf16, MT, 2, A_NORM, E_GELU, 8, 1, 4, true><<<grid, block, lds, st>>>(a);
     else gemm_kernel<bf16, MT, 2, A_NORM, E_GELU, 8, 0, 1, true><<<grid, block, lds, st>>>(a);
-  }
-  else
+  } else if (NT == 2 && amode == A_ACT && epi == E_GELU) {
+    // one row tile over pre-normed bf16 rows (the same operands)
+    if constexpr (MT == 1) gemm_kernel<bf16, 1, 2, A_ACT, E_GELU, 8, 1, 4, true><<<grid, block, lds, st>>>(a);
+    else return hipErrorInvalidValue;
+  } else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
