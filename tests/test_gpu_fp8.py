@@ -80,3 +80,29 @@ def test_fp8_full_width_layers_match_oracle_and_steps():
         assert np.array_equal(one[0, 0], blk[0, k]), k
         rollback(sB, [1])
     assert list(lengths(sB)) == [40 + P]
+
+
+def test_fp8_batch_equals_single_sequences():
+    """Four sequences in one FP8 launch (52 rows: the gate/up and in-projection
+    norm fused into the GEMM prologue) against each run alone (13 rows: the
+    single-tile gate/up over the norm kernel's bf16 rows): logits and, after a
+    ragged rollback, lengths bit for bit. The two operand paths form the same
+    bf16(x * rinv)."""
+    cfg = ModelConfig("fir_mlp_d4096", 4096, 512, [Block("fir", fir_len=7), Block("mlp", d_ff=11008)], dtype="bf16")
+    w = es.make_weights(cfg, seed=37)
+    B, P = 4, 13
+    prompts = [es.prompt_tokens(cfg, 20 + 7 * b, seed=38 + b)[0] for b in range(B)]
+    cand = es.prompt_tokens(cfg, P, seed=43, batch=B).astype(np.int32)
+    mA, sA = engine(cfg, w, True, batch=B)
+    prefill(mA, sA, prompts)
+    blk, _ = block_verify(mA, sA, cand)
+    keep = np.array([0, 5, 13, 9], np.int32)
+    rollback(sA, keep)
+    for b in range(B):
+        mB, sB = engine(cfg, w, True)
+        prefill(mB, sB, [prompts[b]])
+        one, _ = block_verify(mB, sB, cand[b:b + 1])
+        assert np.array_equal(one[0], blk[b]), b
+        rollback(sB, keep[b:b + 1])
+        assert lengths(sB)[0] == lengths(sA)[b], b
+    assert sA.error() == 0
