@@ -92,6 +92,33 @@ def test_c4_attention_block_at_262k_context():
     assert np.array_equal(vd.double().cpu().numpy(), pend.v_new[0][:5])
 
 
+def test_attention_mid_capacity_ranges_match_oracle():
+    """A state of ~20k keys of capacity takes ~2048-key ranges (9 per head,
+    not the 8 of 8k and 262k states): one 32 x 128 attention layer at
+    d = 4096, two sequences at 20,000 and 7,000 imported keys (dyadic weights:
+    q, k, v exact on both sides), block logits of each against the fp64
+    oracle, and each sequence against itself run alone bit for bit."""
+    cfg = ModelConfig("single_attn", 4096, 512, [Block("attn", n_heads=32, head_dim=128)], dtype="bf16")
+    w = es.dyadic_weights(cfg, seed=24)
+    ctx = [20000, 7000]
+    model, state = make_engine(cfg, w, batch=2, max_ctx=20064, max_block=13)
+    synths = [es.synthetic_state(cfg, t, seed=25 + b, device=DEV) for b, t in enumerate(ctx)]
+    for b, t in enumerate(ctx):
+        import_state(state, cfg, synths[b], t, b)
+    cand = es.prompt_tokens(cfg, 13, seed=27, batch=2).astype(np.int32)
+    lg, _ = block_verify(model, state, cand)
+    orc = HybridLM(cfg, w)
+    for b, t in enumerate(ctx):
+        m1, s1 = make_engine(cfg, w, batch=1, max_ctx=20064, max_block=13)
+        import_state(s1, cfg, synths[b], t, 0)
+        one, _ = block_verify(m1, s1, cand[b:b + 1])
+        assert np.array_equal(one[0], lg[b]), b
+        pend = orc.block(orc.import_state(t, synths[b]), cand[b])
+        err = logit_err(lg[b], pend.logits)
+        assert err < LOGIT_ATOL, (b, err)
+    assert state.error() == 0
+
+
 # ------------------------------------------------------------------- C5
 def committed_equal(cfg, sa, ba, sb, bb):
     """Committed state of sequence ba of sa equals that of sequence bb of sb:
