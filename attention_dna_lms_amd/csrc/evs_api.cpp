@@ -20,6 +20,7 @@ namespace {
 constexpr size_t ALIGN = 256;
 constexpr int MAX_ROWS_PER_WG = 144;   // 9 MFMA row tiles
 constexpr int SPLIT_MT = 7;            // row tiles from which bf16 launches split K across workgroups
+constexpr int SPLIT_PAIR_MT = 9;       // row tiles from which split launches store range-pair partials (4, not 8)
 constexpr int GEMM_WAVES = 8;          // waves per GEMM workgroup (gemm_kernel default)
 constexpr int ATTN_CUS = 256;          // compute units the attention split count is sized for
 constexpr size_t LDS_MAX = 163840;     // LDS one workgroup may use on gfx950 (160 KB)
@@ -390,6 +391,9 @@ evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int 
   if (m->desc.dtype == EVS_BF16 && !mat.w8 && amode == A_ACT && sl.MT >= SPLIT_MT &&
       (size_t)8 * sl.slices * sl.MT * 16 * mat.n_groups * mat.NT * 16 * 4 <= s->part_bytes) {
     a.part = wp<float>(s, s->w_part);
+    // 9 row tiles: range-pair partials (half the partial bytes for twice the
+    // activation staging: measured faster there, slower at 7 tiles)
+    a.nparts = sl.MT >= SPLIT_PAIR_MT ? 4 : 8;
     return hip_ok(timed(s, EVS_KC_GEMM, bytes, st,
                         [&] { return launch_gemm_split(sl.MT, mat.NT, epi, a, sl.slices, lds, st); }));
   }

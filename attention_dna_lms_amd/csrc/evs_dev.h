@@ -113,7 +113,8 @@ struct GemmArgs {
   float* x; int ldx;     // E_RESID residual stream
   float* nrm_out;        // E_RESID per-16-column sum of squares [n_tiles][nrm_ld]
   MixArgs mix;
-  float* part;           // split-K launches: the k-range partials [slice][8][group][MT][NT][64 lanes][4]
+  float* part;           // split-K launches: the k-range partials [slice][nparts][group][MT][NT][64 lanes][4]
+  int nparts;            // 8 (one per k-range) or 4 (range pairs r + (r + 4)); 0 reads as 8
 };
 
 struct AttnArgs {

@@ -19,6 +19,8 @@
 // of attention), which keeps each channel tile's q, k, v in one workgroup.
 #pragma once
 
+#include <algorithm>
+
 #include "evs_dev.h"
 
 namespace evs {
@@ -496,13 +498,23 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   f32x4 acc[NT][MT];
   if constexpr (PART) {
     // the eight k-range partials gemm_part_kernel formed (wave w takes range
-    // w's chains, exactly what this kernel's wave w would have computed)
+    // w's chains, exactly what this kernel's wave w would have computed), or
+    // the four pair sums gemm_pair_kernel formed (wave w < 4 takes ranges
+    // w + (w + 4), the tree's first level; waves 4..7 hold -0, the exact
+    // additive identity, so the tree's remaining levels are unchanged)
+    const int np = a.nparts == 4 ? 4 : 8;
     const f32x4* pp = reinterpret_cast<const f32x4*>(a.part) +
-                      ((((size_t)blockIdx.y * 8 + wave) * a.n_groups + g) * MT) * NT * 64 + lane;
+                      ((((size_t)blockIdx.y * np + min(wave, np - 1)) * a.n_groups + g) * MT) * NT * 64 + lane;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = pp[(mt * NT + nt) * 64];
+    if (wave >= np) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{-0.f, -0.f, -0.f, -0.f};
+    }
   } else {
   // two chunk buffers
   uint4 w0[CH][NT], w1[CH][NT];
@@ -848,17 +860,159 @@ __global__ void __launch_bounds__(512) gemm_part_kernel(GemmArgs a) {
   }
 }
 
+// gemm_pair_kernel: one workgroup per (four column groups, range pair p, row
+// slice); wave w takes group 4c + (w & 3) over k-range p + 4 (w >> 2), forming
+// the same MFMA chain as gemm_kernel's wave of that range. Both ranges'
+// activation chunks are staged in LDS (each shared by four waves); at the end
+// the waves of range p + 4 hand their tiles to those of range p through LDS,
+// which add them (range p + range p + 4: the first level of gemm_kernel's
+// tree) and store one partial per pair: half the partial bytes of
+// gemm_part_kernel for twice its activation staging.
+template <typename T, int MT, int NT>
+__global__ void __launch_bounds__(512) gemm_pair_kernel(GemmArgs a) {
+  static_assert(sizeof(T) == 2, "bf16 rows only");
+  constexpr int E = St<T>::E, KSTEP = St<T>::KSTEP;
+  constexpr int XF = PK * MT * 64;                   // 16-byte units per staged chunk of one range
+  constexpr int XPT = (XF + 511) / 512;              // staging loads per thread and range
+  constexpr int XB = XPT * 512;                      // per-range buffer stride
+  static_assert(XPT <= 3, "staging rounds");
+  extern __shared__ float lds[];
+  uint4* xs = reinterpret_cast<uint4*>(lds);         // [2 buffers][2 ranges][XB]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gi = wave & 3, h = wave >> 2;
+  const int g = blockIdx.x * 4 + gi;
+  const bool gv = g < a.n_groups;
+  const int p = blockIdx.y;                          // range pair: ranges p and p + 4
+  const int row0 = blockIdx.z * a.rows_per_slice;
+  const int rows = min(a.rows_per_slice, a.M - row0);
+  const int ks = a.ksteps, pw = (ks + 7) / 8;
+  // both ranges of the pair (range p is never shorter than range p + 4)
+  const int kb0 = min(p * pw, ks), ke0 = min(kb0 + pw, ks);
+  const int kb1 = min((p + 4) * pw, ks), ke1 = min(kb1 + pw, ks);
+  const int kb = h ? kb1 : kb0, ke = h ? ke1 : ke0;  // this wave's range
+  const int nchk = (ke0 - kb0 + PK - 1) / PK;
+  const u32x4* wp = reinterpret_cast<const u32x4*>(a.W) + lane + (gv ? (size_t)g * a.gstride : 0);
+  const T* A = reinterpret_cast<const T*>(a.A);
+
+  // staging unit idx (< 2 * XF): range idx / XF, then (u * MT + mt) * 64 + l
+  // within it, as in gemm_part_kernel (k-steps past a range's end re-read its
+  // last step; an empty range reads the matrix's last step)
+  auto x_addr = [&](int idx, int c) __attribute__((always_inline)) -> const uint4* {
+    const int hh = idx >= XF ? 1 : 0, j = idx - hh * XF;
+    const int l = j & 63, mt = (j >> 6) % MT, u = (j >> 6) / MT;
+    const int b0 = hh ? kb1 : kb0, e0 = hh ? ke1 : ke0;
+    const int k = max(min(b0 + c * PK + u, e0 - 1), 0);
+    const int row = row0 + min(mt * 16 + (l & 15), rows - 1);
+    return reinterpret_cast<const uint4*>(A + act_off<E>(row, k * KSTEP + (l >> 4) * E, a.lda));
+  };
+  auto x_unit = [&](int q) __attribute__((always_inline)) { return min(q, 2 * XF - 1); };
+  auto x_slot = [&](int q) __attribute__((always_inline)) {   // LDS slot of staging unit q
+    return q >= XF ? XB + (q - XF) : q;
+  };
+  auto issue_w = [&](uint4 (&w)[PK][NT], int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < PK; ++u)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int k = min(kb + c * PK + u, ke - 1);
+        w[u][nt] = ld_stream(wp + (size_t)max(k, 0) * a.tstride + nt * 64);
+      }
+  };
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint4 w0[PK][NT], w1[PK][NT];
+  // each thread stages units tid + 512 q, q < 2 XPT (both ranges)
+  if (nchk > 0) {
+#pragma unroll
+    for (int q = 0; q < 2 * XPT; ++q) {
+      const int uq = tid + q * 512;
+      if (uq < 2 * XF) xs[x_slot(uq)] = *x_addr(x_unit(uq), 0);
+    }
+    issue_w(w0, 0);
+    if (nchk > 1) issue_w(w1, 1);
+  }
+  auto step = [&](int c, uint4 (&w)[PK][NT]) __attribute__((always_inline)) {
+    __syncthreads();                      // chunk c staged; chunk c - 1's buffers free
+    const int cn = min(c + 1, nchk - 1);
+    uint4 xn0, xn1, xn2, xn3, xn4, xn5;
+    xn0 = *x_addr(x_unit(tid), cn);
+    xn1 = *x_addr(x_unit(tid + 512), cn);
+    if constexpr (XPT > 1) { xn2 = *x_addr(x_unit(tid + 1024), cn); xn3 = *x_addr(x_unit(tid + 1536), cn); }
+    if constexpr (XPT > 2) { xn4 = *x_addr(x_unit(tid + 2048), cn); xn5 = *x_addr(x_unit(tid + 2560), cn); }
+    const uint4* xb = xs + (c & 1) * 2 * XB + h * XB;
+#pragma unroll
+    for (int u = 0; u < PK; ++u) {
+      if (kb + c * PK + u < ke) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const uint4 x = xb[(u * MT + mt) * 64 + lane];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mma_frag(w[u][nt], x, acc[mt][nt], T());
+        }
+      }
+    }
+    if (c + 2 < nchk) issue_w(w, c + 2);
+    uint4* dst = xs + ((c + 1) & 1) * 2 * XB;
+    auto put = [&](int uq, const uint4& v) __attribute__((always_inline)) {
+      if (uq < 2 * XF) dst[x_slot(uq)] = v;
+    };
+    put(tid, xn0);
+    put(tid + 512, xn1);
+    if constexpr (XPT > 1) { put(tid + 1024, xn2); put(tid + 1536, xn3); }
+    if constexpr (XPT > 2) { put(tid + 2048, xn4); put(tid + 2560, xn5); }
+  };
+  for (int c = 0; c < nchk; c += 2) {
+    step(c, w0);
+    if (c + 1 < nchk) step(c + 1, w1);
+  }
+  // range p + 4's tiles to range p's waves through LDS (the staging buffers
+  // are free once every wave has passed the barrier)
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(lds) + (size_t)gi * MT * NT * 64 + lane;   // [4][MT][NT][64]
+  if (h == 1) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) red[(mt * NT + nt) * 64] = acc[mt][nt];
+  }
+  __syncthreads();
+  if (h == 0 && gv) {
+    f32x4* pp = reinterpret_cast<f32x4*>(a.part) +
+                ((((size_t)blockIdx.z * 4 + p) * a.n_groups + g) * MT) * NT * 64 + lane;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) pp[(mt * NT + nt) * 64] = acc[mt][nt] + red[(mt * NT + nt) * 64];
+  }
+}
+
 template <typename T, int MT>
 static hipError_t launch_gemm_split_mt(int NT, int epi, const GemmArgs& a, int slices, size_t lds, hipStream_t st) {
   if constexpr (sizeof(T) != 2 || MT < 2) {
     return hipErrorInvalidValue;
   } else {
-    const size_t xlds = (size_t)2 * ((PK * MT * 64 + 511) / 512) * 512 * 16;
-    dim3 pgrid((a.n_groups + 7) / 8, 8, slices), grid(a.n_groups, slices), block(512);
-    if (NT == 3) gemm_part_kernel<T, MT, 3><<<pgrid, block, xlds, st>>>(a);
-    else if (NT == 2) gemm_part_kernel<T, MT, 2><<<pgrid, block, xlds, st>>>(a);
-    else if (NT == 1) gemm_part_kernel<T, MT, 1><<<pgrid, block, xlds, st>>>(a);
-    else return hipErrorInvalidValue;
+    const size_t xb = (size_t)((PK * MT * 64 + 511) / 512) * 512 * 16;   // bytes per staged chunk of one range
+    dim3 grid(a.n_groups, slices), block(512);
+    if (a.nparts == 4) {
+      // two buffers of two ranges, or the pair hand-off ([4][MT][NT][64] f32x4)
+      const size_t plds = std::max((size_t)4 * xb, (size_t)4 * MT * NT * 64 * 16);
+      dim3 pgrid((a.n_groups + 3) / 4, 4, slices);
+      if (NT == 3) gemm_pair_kernel<T, MT, 3><<<pgrid, block, plds, st>>>(a);
+      else if (NT == 2) gemm_pair_kernel<T, MT, 2><<<pgrid, block, plds, st>>>(a);
+      else if (NT == 1) gemm_pair_kernel<T, MT, 1><<<pgrid, block, plds, st>>>(a);
+      else return hipErrorInvalidValue;
+    } else {
+      dim3 pgrid((a.n_groups + 7) / 8, 8, slices);
+      if (NT == 3) gemm_part_kernel<T, MT, 3><<<pgrid, block, 2 * xb, st>>>(a);
+      else if (NT == 2) gemm_part_kernel<T, MT, 2><<<pgrid, block, 2 * xb, st>>>(a);
+      else if (NT == 1) gemm_part_kernel<T, MT, 1><<<pgrid, block, 2 * xb, st>>>(a);
+      else return hipErrorInvalidValue;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (NT == 3 && epi == E_MIXER) gemm_kernel<T, MT, 3, A_ACT, E_MIXER, 8, 0, 1, false, true><<<grid, block, lds, st>>>(a);
