@@ -783,7 +783,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the block-verify path is single-GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
+              "(the block-verify path runs on one GPU)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
