@@ -49,7 +49,7 @@ typedef enum {
   EVS_E_RANGE = -2,       /* a size exceeds what the state was created for */
   EVS_E_STATE = -3,       /* call out of order (e.g. rollback with nothing pending) */
   EVS_E_HIP = -4,         /* a HIP runtime call or kernel launch failed */
-  EVS_E_UNSUPPORTED = -5  /* valid request outside what this build implements */
+  EVS_E_UNSUPPORTED = -5  /* valid request outside what the library implements */
 } evs_status;
 
 /* block kinds */
