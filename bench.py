@@ -67,6 +67,11 @@ def parse():
     ap.add_argument("--summarize-c5-trace", metavar="KERNEL_TRACE_CSV",
                     help="print the per-round kernel table at each gamma of a rocprofv3 kernel trace of --c5 "
                          "(pass the same --steps/--warmup as the profiled run) and exit")
+    ap.add_argument("--summarize-c5-counters", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="print per-gamma HBM bytes per launch of each kernel from rocprofv3 FETCH_SIZE / "
+                         "WRITE_SIZE passes of --c5 and of --copy-calibration (pass the same --steps/--warmup), "
+                         "and exit")
     ap.add_argument("--summarize-counters", nargs=4,
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="print the per-launch HBM traffic (JSON) from rocprofv3 FETCH_SIZE / WRITE_SIZE "
@@ -79,7 +84,7 @@ def parse():
 
 GEMM_SOURCES = ("attention_dna_lms_amd/csrc/gemm_impl.h", "attention_dna_lms_amd/csrc/gemm_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_kernel_c3_traffic.json")
-KERNEL_FAMILIES = ("attn_merge_kernel", "gemm_part_kernel", "gemm_kernel", "attn32_kernel", "attn_kernel",
+KERNEL_FAMILIES = ("attn_merge_kernel", "gemm_part_kernel", "gemm_pair_kernel", "gemm_kernel", "attn32_kernel", "attn_kernel",
                    "verify_kernel", "commit_kernel", "embed_kernel", "norm_rows_kernel", "draft_reg_kernel",
                    "draft_kernel", "inject_prep_kernel", "slots_kernel", "export_rows_kernel")
 C5_GAMMAS = (1, 4, 8, 12, 16)
@@ -196,6 +201,49 @@ def summarize_c5_trace(path, steps, warmup):
         print("| kernel | launches/round | avg us | us/round |\n|---|---|---|---|")
         for k, v in sorted(g.items(), key=lambda kv: -sum(kv[1])):
             print(f"| {k} | {len(v) / steps:.0f} | {sum(v) / len(v):.2f} | {sum(v) / steps:.1f} |")
+        print()
+
+
+def summarize_c5_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, steps, warmup):
+    """Per gamma of a --c5 run: HBM bytes per launch of each kernel (fetched
+    and written, each scaled by what the counter reads for a known-size copy)
+    over the timed rounds, and per round."""
+    import collections
+    import csv
+
+    def copy_scale(path, counter):
+        vals = [float(r["Counter_Value"]) * 1024 for r in csv.DictReader(open(path))
+                if "MulFunctor" in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        if not vals:
+            raise SystemExit(f"no copy dispatch in {path}")
+        return (1 << 30) / (sum(vals) / len(vals))
+
+    n = warmup + steps
+    per = {}
+    for counter, path, cpath in (("FETCH_SIZE", fetch_csv, copy_fetch_csv), ("WRITE_SIZE", write_csv, copy_write_csv)):
+        scale = copy_scale(cpath, counter)
+        rows = sorted((r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter),
+                      key=lambda r: int(r["Dispatch_Id"]))
+        commits = [i for i, r in enumerate(rows) if "commit_kernel" in r["Kernel_Name"]]
+        if warmup < 1 or len(commits) < n * len(C5_GAMMAS):
+            raise SystemExit("counters do not hold the --c5 rounds of these --steps/--warmup")
+        commits = commits[-n * len(C5_GAMMAS):]
+        for gi, gamma in enumerate(C5_GAMMAS):
+            g = collections.defaultdict(list)
+            for r in range(gi * n + warmup, (gi + 1) * n):
+                for x in rows[commits[r - 1] + 1: commits[r] + 1]:
+                    g[family(x, True)].append(float(x["Counter_Value"]) * 1024 * scale)
+            per.setdefault(gamma, {})[counter] = g
+    for gamma in C5_GAMMAS:
+        f, w = per[gamma]["FETCH_SIZE"], per[gamma]["WRITE_SIZE"]
+        tot = sum(sum(v) for v in f.values()) / steps + sum(sum(v) for v in w.values()) / steps
+        print(f"### gamma {gamma}\n\n{tot / 1e9:.2f} GB of HBM traffic per round "
+              f"(fetched + written)\n")
+        print("| kernel | launches/round | MB fetched per launch | MB written per launch | GB/round |\n|---|---|---|---|---|")
+        for k in sorted(f, key=lambda k: -(sum(f[k]) + sum(w.get(k, [0.0])))):
+            fv, wv = f[k], w.get(k, [0.0])
+            print(f"| {k} | {len(fv) / steps:.0f} | {sum(fv) / len(fv) / 1e6:.2f} | {sum(wv) / len(wv) / 1e6:.2f} | "
+                  f"{(sum(fv) + sum(wv)) / steps / 1e9:.3f} |")
         print()
 
 
@@ -771,6 +819,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.steps, args.warmup)
+        return
+    if args.summarize_c5_counters:
+        summarize_c5_counters(*args.summarize_c5_counters, args.steps, args.warmup)
         return
     if args.summarize_c5_trace:
         summarize_c5_trace(args.summarize_c5_trace, args.steps, args.warmup)
