@@ -337,6 +337,42 @@ __device__ __forceinline__ float lane_f(float x, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
+// The same total order as one 64-bit key per entry, so a selection step is
+// one unsigned compare and a select (no short-circuit control flow): the high
+// word is the value's bits made monotone (with -0 read as +0, which the
+// float compare treats as equal), the low word 0xFFFFFFFF - id (a lower id is
+// the larger key on ties). Key 0 is below every real entry.
+typedef unsigned long long okey_t;
+__device__ __forceinline__ okey_t ord_key(float v, int y) {
+  const unsigned u = __float_as_uint(v + 0.f);
+  const unsigned hi = u ^ ((unsigned)((int)u >> 31) | 0x80000000u);
+  return ((okey_t)hi << 32) | (okey_t)(0xFFFFFFFFu - (unsigned)y);
+}
+__device__ __forceinline__ float key_value(okey_t k) {
+  const unsigned hi = (unsigned)(k >> 32);
+  return __uint_as_float(hi ^ (~(unsigned)((int)hi >> 31) | 0x80000000u));
+}
+__device__ __forceinline__ int key_index(okey_t k) { return (int)(0xFFFFFFFFu - (unsigned)k); }
+__device__ __forceinline__ okey_t key_max(okey_t a, okey_t b) { return a > b ? a : b; }
+template <int CTRL> __device__ __forceinline__ okey_t dpp_key(okey_t k) {
+  const unsigned lo = (unsigned)dpp_i<CTRL>((int)(unsigned)k);
+  const unsigned hi = (unsigned)dpp_i<CTRL>((int)(unsigned)(k >> 32));
+  return ((okey_t)hi << 32) | lo;
+}
+__device__ __forceinline__ okey_t lane_key(okey_t k, int l) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)k, l);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(k >> 32), l);
+  return ((okey_t)hi << 32) | lo;
+}
+// largest key of the wave, in every lane (the same row steps as wave_argmax)
+__device__ __forceinline__ okey_t wave_keymax(okey_t k) {
+  k = key_max(k, dpp_key<DPP_XOR1>(k));
+  k = key_max(k, dpp_key<DPP_XOR2>(k));
+  k = key_max(k, dpp_key<DPP_HALF_MIRROR>(k));
+  k = key_max(k, dpp_key<DPP_MIRROR>(k));
+  return key_max(key_max(lane_key(k, 0), lane_key(k, 16)), key_max(lane_key(k, 32), lane_key(k, 48)));
+}
+
 template <int CTRL> __device__ __forceinline__ void argmax_dpp(float& v, int& i) {
   const float v2 = dpp_f<CTRL>(v);
   const int i2 = dpp_i<CTRL>(i);
@@ -994,49 +1030,49 @@ __global__ void __launch_bounds__(64) draft_reg_kernel(DraftArgs a) {
     }
     // l' (NaN read as -inf) and its argmax; entries past V never win
     float l[NPL];
-    float bv = -INFINITY;
-    int amax = 0;
+    okey_t ak = 0;
 #pragma unroll
     for (int k = 0; k < NPL; ++k) {
       const int y = lane + 64 * k;
       const float v = lv[k] + mv[k];
       l[k] = isnan(v) ? -INFINITY : v;
-      if (y < V && ord_gt(l[k], y, bv, amax)) { bv = l[k]; amax = y; }
+      ak = key_max(ak, y < V ? ord_key(l[k], y) : 0);
     }
-    wave_argmax(bv, amax);
+    const int amax = key_index(wave_keymax(ak));
     float z[NPL];
+    okey_t zk[NPL];
 #pragma unroll
-    for (int k = 0; k < NPL; ++k) z[k] = l[k] / a.temperature;
+    for (int k = 0; k < NPL; ++k) {
+      const int y = lane + 64 * k;
+      z[k] = l[k] / a.temperature;
+      zk[k] = y < V ? ord_key(z[k], y) : 0;
+    }
     // the top-k cut: top_k passes in the total order (kept entries in value order)
     float kv[DRAFT_TOPK_MAX];
     int ki[DRAFT_TOPK_MAX];
     float tv = -INFINITY;
     int ti = V;
     {
-      float pvv = INFINITY;
-      int pii = -1;
+      // pass r: the largest key below the previous pass's (all keys first)
+      okey_t pk = ~0ull;
       const int passes = all ? 0 : a.top_k;
       for (int r = 0; r < passes; ++r) {
-        float cv = -INFINITY;
-        int ci = V;
+        okey_t c = 0;
 #pragma unroll
-        for (int k = 0; k < NPL; ++k) {
-          const int y = lane + 64 * k;
-          if (y < V && ord_gt(pvv, pii, z[k], y) && ord_gt(z[k], y, cv, ci)) { cv = z[k]; ci = y; }
-        }
-        wave_argmax(cv, ci);
-        // the same in every lane: keep it in scalar registers, so the work on
-        // the kept entries below branches uniformly
-        pvv = lane_f(cv, 0);
-        pii = __builtin_amdgcn_readfirstlane(ci);
+        for (int k = 0; k < NPL; ++k) c = (zk[k] < pk) & (zk[k] > c) ? zk[k] : c;
+        // the same in every lane (scalar registers), so the work on the kept
+        // entries below branches uniformly
+        pk = wave_keymax(c);
         if (sparse) {
+          const float pvv = key_value(pk);
+          const int pii = key_index(pk);
 #pragma unroll
           for (int rr = 0; rr < DRAFT_TOPK_MAX; ++rr)
             if (rr == r) { kv[rr] = pvv; ki[rr] = pii; }
         }
       }
-      tv = pvv;
-      ti = pii;
+      tv = passes > 0 ? key_value(pk) : INFINITY;
+      ti = passes > 0 ? key_index(pk) : -1;
     }
     const float u = a.greedy ? 0.f : a.u[(size_t)b * a.gamma + i];
     int d = amax;
