@@ -440,13 +440,15 @@ __device__ __forceinline__ void wave_sync() {
 // entries, 0 elsewhere.
 __device__ int wave_target_row(float* pr, int V, float temperature, int top_k, bool soft) {
   const int lane = threadIdx.x & 63;
-  float bv = -INFINITY;
-  int bi = 0;
+  // selections over ord_key keys; a NaN entry (key 0) is never selected, and
+  // every lane starts from (-inf, id 0), so a row with no entry above -inf
+  // gives id 0
+  okey_t bk = ord_key(-INFINITY, 0);
   for (int y = lane; y < V; y += 64) {
     const float z = pr[y];
-    if (ord_gt(z, y, bv, bi)) { bv = z; bi = y; }
+    bk = key_max(bk, isnan(z) ? 0 : ord_key(z, y));
   }
-  wave_argmax(bv, bi);
+  const int bi = key_index(wave_keymax(bk));
   if (!soft) return bi;
   // z / T, then the top-k threshold (the k-th element in the total order)
   for (int y = lane; y < V; y += 64) pr[y] = pr[y] / temperature;
@@ -454,21 +456,21 @@ __device__ int wave_target_row(float* pr, int V, float temperature, int top_k, b
   float tv = -INFINITY;
   int ti = V;
   if (!all) {
-    float pvv = INFINITY;
-    int pii = -1;
+    // pass r: the largest key below the previous pass's; a lane with none
+    // left offers (-inf, id V)
+    okey_t pk = ~0ull;
+    const okey_t none = ord_key(-INFINITY, V);
     for (int r = 0; r < top_k; ++r) {
-      float cv = -INFINITY;
-      int ci = V;
+      okey_t c = none;
       for (int y = lane; y < V; y += 64) {
         const float z = pr[y];
-        if (ord_gt(pvv, pii, z, y) && ord_gt(z, y, cv, ci)) { cv = z; ci = y; }
+        const okey_t k = isnan(z) ? 0 : ord_key(z, y);
+        c = (k < pk) & (k > c) ? k : c;
       }
-      wave_argmax(cv, ci);
-      pvv = cv;
-      pii = ci;
+      pk = wave_keymax(c);
     }
-    tv = pvv;
-    ti = pii;
+    tv = key_value(pk);
+    ti = key_index(pk);
   }
   float m = -INFINITY;
   for (int y = lane; y < V; y += 64) {
