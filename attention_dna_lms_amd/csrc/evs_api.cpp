@@ -841,7 +841,8 @@ evs_status evs_verify_sample(int32_t batch, int32_t gamma, int32_t vocab, const 
     return EVS_E_INVALID;
   if (gamma > 0 && !draft) return EVS_E_INVALID;
   if (!greedy && (!u || (gamma > 0 && !q))) return EVS_E_INVALID;
-  if (!greedy && kind != EVS_TARGET_PROBS_F32 && !(temperature > 0.f)) return EVS_E_INVALID;
+  if (!greedy && kind != EVS_TARGET_PROBS_F32 && !(temperature > 0.f && std::isfinite(temperature)))
+    return EVS_E_INVALID;
   if ((long long)(gamma + 2) * vocab > 15360) return EVS_E_UNSUPPORTED;   // LDS: about 60 KB of fp32 rows
   VerifyArgs a{};
   a.gamma = gamma; a.V = vocab; a.kind = kind; a.top_k = top_k; a.greedy = greedy ? 1 : 0;
@@ -869,7 +870,7 @@ evs_status evs_draft(evs_model* m, evs_state* s, int32_t batch, const float* hid
                      void* stream) {
   if (!m || !s || s->m != m || m->desc.inject_dim <= 0) return EVS_E_INVALID;
   if (!hidden || hidden_rows < 1 || !last || !logits || !drafts || (!greedy && !u)) return EVS_E_INVALID;
-  if (!(temperature > 0.f)) return EVS_E_INVALID;
+  if (!(temperature > 0.f && std::isfinite(temperature))) return EVS_E_INVALID;
   if (batch < 1 || batch > s->B || gamma < 1 || gamma > m->desc.max_slots) return EVS_E_RANGE;
   if (gamma > s->max_block) return EVS_E_RANGE;
   if (m->desc.vocab > 15360) return EVS_E_UNSUPPORTED;   // one fp32 row in LDS

@@ -1047,7 +1047,9 @@ __global__ void __launch_bounds__(64) draft_reg_kernel(DraftArgs a) {
     for (int k = 0; k < NPL; ++k) {
       const int y = lane + 64 * k;
       z[k] = l[k] / a.temperature;
-      zk[k] = y < V ? ord_key(z[k], y) : 0;
+      // (a NaN z, which a finite temperature cannot produce, would never be
+      // kept, as in the verifier's top-k passes)
+      zk[k] = (y < V && !isnan(z[k])) ? ord_key(z[k], y) : 0;
     }
     // the top-k cut: top_k passes in the total order (kept entries in value order)
     float kv[DRAFT_TOPK_MAX];

@@ -57,7 +57,9 @@ enum { EVS_FIR = 1, EVS_IIR = 2, EVS_ATTN = 3, EVS_MLP = 4 };
 /* storage types; EVS_BF16_FP8W is a model dtype only: a bf16 model whose block
  * projection matrices (w_in, w_out, w_gu, w_down) are held as OCP FP8 E4M3 with
  * one power-of-two scale per output row, the smallest s with max|w| <= 448 s
- * (EvSpark preprint "next" item: FP8 weights). evs_pack_weights quantises the
+ * (Evo2 discussion #232, author reply, "Regime overlap": FP8 weights shrink
+ * the weight read further; the E4M3 format and the row scaling are this
+ * library's choice, the page names neither). evs_pack_weights quantises the
  * bf16 canonical tensors (round to nearest, ties to even); activations,
  * states, embedding and LM head stay bf16 and the accumulation stays fp32. */
 enum { EVS_BF16 = 1, EVS_F32 = 2, EVS_I32 = 3, EVS_BF16_FP8W = 4 };
@@ -215,7 +217,11 @@ evs_status evs_rollback(evs_state* s, const int32_t* n_keep_dev, void* stream);
  *   draft_dev   [B, gamma] i32: draft tokens d_1 .. d_gamma
  *   u_dev       [B, gamma+1] f32 in [0,1): u[i] for the accept test of draft
  *               i+1, u[gamma] for the final draw (unused if greedy)
- *   temperature > 0, top_k (0 or >= V keeps all) apply to logits targets.
+ *   temperature (finite, > 0; checked when sampling from logits) and top_k
+ *               (0 or >= V keeps all) apply to logits targets.
+ * NaN entries: a NaN logit reads as -inf; a NaN probability (target or draft,
+ * greedy or sampling) reads as 0. A target row with no positive probability
+ * falls back to its argmax (lowest id on ties).
  * Sampling: accept draft i+1 iff u[i] < p_i[x] / q_i[x] (iff p_i[x] > 0 when
  * q_i[x] = 0); at the first reject draw from max(0, p_i - q_i) normalised
  * (p_i if that is all zero); if all are accepted draw a bonus token from
@@ -263,7 +269,8 @@ evs_status evs_state_export(evs_state* s, int32_t block, float* dst_dev);
  *   with u_dev[b, i] (f32 [B, gamma]; the argmax of l' if q has no positive
  *   entry), or the argmax of l' (lowest id) when greedy != 0 (u unused).
  * Outputs: drafts_dev [B, gamma] i32, q_dev [B, gamma, V] f32 (may be NULL).
- * 1 <= gamma <= max_slots; V <= 15360; errors go to the drafter state's word.
+ * 1 <= gamma <= max_slots; temperature finite and > 0; V <= 15360; errors go
+ * to the drafter state's word.
  * The drafter state's timing covers its GEMM and attention launches. */
 evs_status evs_draft(evs_model* drafter, evs_state* ds, int32_t batch, const float* hidden_dev,
                      int32_t hidden_rows, const int32_t* hidden_index_dev, const int32_t* last_dev,

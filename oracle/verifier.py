@@ -152,11 +152,14 @@ def verify_sample(target, q, drafts, u, temperature=1.0, top_k=0, target_is_prob
     return gamma, icdf(P[gamma], uf[gamma], fallback(gamma))
 
 
-def verify_greedy(target, drafts):
-    """Greedy verification of one sequence: (n_accepted, next_token)."""
+def verify_greedy(target, drafts, target_is_probs=False):
+    """Greedy verification of one sequence: (n_accepted, next_token). With
+    probability targets a NaN entry reads as probability 0 (as in sampling
+    mode); with logits it reads as -inf."""
     gamma = len(drafts)
+    rows = [_clean_probs(target[i]) if target_is_probs else target[i] for i in range(gamma + 1)]
     for i in range(gamma):
-        a = argmax_lowest(target[i])
+        a = argmax_lowest(rows[i])
         if int(drafts[i]) != a:
             return i, a
-    return gamma, argmax_lowest(target[gamma])
+    return gamma, argmax_lowest(rows[gamma])

@@ -7,6 +7,44 @@ from attention_dna_lms_amd import evs
 
 DEV = "cuda"
 
+# bf16 logits: within 2e-2 absolute of the oracle's (bf16-rounded) value, or
+# exactly one bf16 step from it. A step is 2^-5 = 0.03125 at |b| in [4, 8),
+# so at those magnitudes a one-step rounding flip of an honest fp32 result is
+# the only allowance beyond 2e-2; below |b| = 4 a step is already < 2e-2.
+LOGIT_ATOL = 2e-2
+
+
+def _bf16_order(x):
+    """bf16 values as integers in their total order (adjacent values differ by
+    one), and whether each value is exactly representable in bf16."""
+    f = np.asarray(x, np.float64).astype(np.float32)
+    bits = f.view(np.uint32)
+    exact = ((bits & 0xFFFF) == 0) & (f.astype(np.float64) == np.asarray(x, np.float64))
+    hi = (bits >> 16).astype(np.int64)
+    mag = hi & 0x7FFF
+    return np.where(hi & 0x8000, -mag, mag), exact
+
+
+def logit_err(a, b):
+    """Largest |a - b| over the entries where a is not exactly one bf16 step
+    from b (b: the oracle's bf16 logits; a: the GPU's). An entry one step away
+    counts as 0 whatever the step's size; every other entry counts its full
+    difference, so `logit_err(a, b) < LOGIT_ATOL` is the bar stated above."""
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    if a.size == 0:
+        return 0.0
+    oa, ea = _bf16_order(a)
+    ob, eb = _bf16_order(b)
+    one_step = ea & eb & (np.abs(oa - ob) == 1)
+    diff = np.abs(a - b)
+    return float(np.max(np.where(one_step, 0.0, diff)))
+
+
+def near_tie(row, tol=2 * LOGIT_ATOL):
+    """The oracle's two largest logits of a row are within `tol`."""
+    s = np.sort(np.asarray(row, np.float64))[::-1]
+    return s[0] - s[1] <= tol
+
 
 def make_engine(cfg, weights, batch=1, max_ctx=1024, max_block=16):
     model = evs.Model(cfg, weights, device=DEV)

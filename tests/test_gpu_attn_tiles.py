@@ -10,19 +10,11 @@ import pytest
 import evs_synth as es
 from oracle import HybridLM
 
-from gpu_util import DEV, block_verify, lengths, make_engine, prefill, rollback
+from gpu_util import LOGIT_ATOL, logit_err, DEV, block_verify, lengths, make_engine, prefill, rollback
 from attention_dna_lms_amd import evs
 
 pytestmark = pytest.mark.gpu
 
-LOGIT_ATOL = 2e-2
-
-
-def logit_err(a, b):
-    """Largest |a - b| beyond one bf16 quantum of b (logits are stored in bf16)."""
-    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
-    ulp = np.ldexp(1.0, np.frexp(np.abs(b))[1] - 8)
-    return float(np.max(np.abs(a - b) - ulp))
 
 
 @pytest.mark.parametrize("P,head_dim", [(17, 128), (32, 64), (40, 32), (40, 128)])

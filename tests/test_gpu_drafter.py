@@ -10,19 +10,11 @@ import evs_synth as es
 from oracle import HybridLM
 from oracle.drafter import Drafter
 
-from gpu_util import DEV, block_verify, make_engine, prefill, rollback
+from gpu_util import LOGIT_ATOL, logit_err, DEV, block_verify, make_engine, prefill, rollback
 from attention_dna_lms_amd import evs
 
 pytestmark = pytest.mark.gpu
 
-LOGIT_ATOL = 2e-2
-
-
-def logit_err(a, b):
-    """Largest |a - b| beyond one bf16 quantum of b (values are stored in bf16)."""
-    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
-    ulp = np.ldexp(1.0, np.frexp(np.abs(b))[1] - 8)
-    return float(np.max(np.abs(a - b) - ulp))
 
 
 def test_hidden_export_matches_oracle_and_sequential_steps():

@@ -10,19 +10,11 @@ from evs_synth.configs import Block, ModelConfig
 from oracle import HybridLM
 from oracle.fp8 import fp8_weights
 
-from gpu_util import DEV, block_verify, lengths, prefill, rollback, snapshot
+from gpu_util import LOGIT_ATOL, logit_err, DEV, block_verify, lengths, prefill, rollback, snapshot
 from attention_dna_lms_amd import evs
 
 pytestmark = pytest.mark.gpu
 
-LOGIT_ATOL = 2e-2
-
-
-def logit_err(a, b):
-    """Largest |a - b| beyond one bf16 quantum of b (logits are stored in bf16)."""
-    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
-    ulp = np.ldexp(1.0, np.frexp(np.abs(b))[1] - 8)
-    return float(np.max(np.abs(a - b) - ulp))
 
 
 def engine(cfg, w, fp8, batch=1, max_ctx=256, max_block=16):

@@ -20,19 +20,11 @@ from evs_synth.configs import Block, ModelConfig
 from oracle import HybridLM
 from oracle.verifier import verify_sample
 
-from gpu_util import DEV, block_verify, import_state, lengths, make_engine, rollback
+from gpu_util import LOGIT_ATOL, logit_err, DEV, block_verify, import_state, lengths, make_engine, rollback
 from attention_dna_lms_amd import evs
 
 pytestmark = pytest.mark.gpu
 
-LOGIT_ATOL = 2e-2
-
-
-def logit_err(a, b):
-    """Largest |a - b| beyond one bf16 quantum of b (logits are stored in bf16)."""
-    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
-    ulp = np.ldexp(1.0, np.frexp(np.abs(b))[1] - 8)
-    return float(np.max(np.abs(a - b) - ulp))
 
 
 def run_verify(B, gamma, V, target, kind, q, drafts, u, T=1.0, top_k=0):

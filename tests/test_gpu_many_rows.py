@@ -10,13 +10,12 @@ import evs_synth as es
 from evs_synth.configs import Block, ModelConfig
 from oracle import HybridLM
 
-from gpu_util import DEV, block_verify, lengths, prefill, rollback
-from test_gpu_long_ragged import committed_equal, logit_err
+from gpu_util import LOGIT_ATOL, logit_err, DEV, block_verify, lengths, prefill, rollback
+from test_gpu_long_ragged import committed_equal
 from attention_dna_lms_amd import evs
 
 pytestmark = pytest.mark.gpu
 
-LOGIT_ATOL = 2e-2
 
 
 def _engines(cfg, w, B, max_ctx, max_block=16):

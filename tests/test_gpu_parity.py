@@ -11,27 +11,11 @@ from evs_synth.configs import Block, ModelConfig
 from oracle import HybridLM
 from oracle.verifier import argmax_lowest, target_probs, verify_greedy, verify_sample
 
-from gpu_util import (DEV, block_verify, import_state, lengths, make_engine, max_rel, pending_iir, prefill,
-                      rel_close, rollback, snapshot)
+from gpu_util import (DEV, LOGIT_ATOL, block_verify, import_state, lengths, logit_err, make_engine, max_rel,
+                      near_tie, pending_iir, prefill, rel_close, rollback, snapshot)
 from attention_dna_lms_amd import evs
 
 pytestmark = pytest.mark.gpu
-
-LOGIT_ATOL = 2e-2
-
-
-def logit_err(a, b):
-    """Largest |a - b| beyond one bf16 quantum of b: logits are stored in bf16,
-    so values of magnitude >= 4 carry a quantum (0.03125) above the 2e-2 bar and
-    an honest one-quantum rounding flip must not count against it."""
-    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
-    ulp = np.ldexp(1.0, np.frexp(np.abs(b))[1] - 8)
-    return float(np.max(np.abs(a - b) - ulp))
-
-
-def _near_tie(row, tol=2 * LOGIT_ATOL):
-    s = np.sort(row)[::-1]
-    return s[0] - s[1] <= tol
 
 
 # --------------------------------------------------------------- C1 (fp32)
@@ -154,7 +138,7 @@ def test_small_stack_bf16_ragged_batch_matches_oracle():
         err = logit_err(lg[b], pends[b].logits)
         assert err < LOGIT_ATOL, (b, err)
         for i in range(gamma + 1):
-            if not _near_tie(pends[b].logits[i]):
+            if not near_tie(pends[b].logits[i]):
                 assert argmax_lowest(lg[b, i]) == argmax_lowest(pends[b].logits[i])
     rollback(state, [5, 13])
     assert list(lengths(state)) == [305, 190]

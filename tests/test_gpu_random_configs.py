@@ -12,12 +12,11 @@ import evs_synth as es
 from evs_synth.configs import Block, ModelConfig
 from oracle import HybridLM
 
-from gpu_util import DEV, block_verify, lengths, make_engine, prefill, rollback
-from test_gpu_long_ragged import committed_equal, logit_err
+from gpu_util import LOGIT_ATOL, logit_err, DEV, block_verify, lengths, make_engine, prefill, rollback
+from test_gpu_long_ragged import committed_equal
 
 pytestmark = pytest.mark.gpu
 
-LOGIT_ATOL = 2e-2
 
 # (d, blocks, B, P, dtype)
 CASES = [

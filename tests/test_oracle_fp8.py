@@ -56,3 +56,59 @@ def test_row_scales_are_the_smallest_fitting_powers_of_two():
     assert np.array_equal(s, s2)
     assert np.array_equal(q, _torch_e4m3((W / s[:, None]).astype(np.float32)))
     assert np.all(np.abs(q) <= E4M3_MAX)
+
+
+# Hand-worked rows (values checked by hand, not by the quantiser):
+#   row 0 = [0.0103, 0.02, -0.0105, 0]: max 0.02 = 0.64 * 2^-5, so s = 2^-14
+#     (448 * 2^-14 = 0.0273 fits, 224 * 2^-14 = 0.0137 does not); scaled values
+#     168.76, 327.68, -172.03, 0 round in E4M3 steps of 16, 32, 16 to 176, 320,
+#     -176, 0 -> [0.0107421875, 0.01953125, -0.0107421875, 0].
+#   row 1 = [300, -0.5, 0.25, 1.3]: max 300 = 0.586 * 2^9, so s = 1; 300 rounds
+#     in steps of 32 to 288, 1.3 in steps of 1/8 to 1.25 -> [288, -0.5, 0.25, 1.25].
+# A column-wise scale would put column 0's 0.0103 on the subnormal grid of
+# column max 300 (steps of 2^-9) and give 0.009765625 instead.
+HAND_ROWS = np.array([[0.0103, 0.02, -0.0105, 0.0], [300.0, -0.5, 0.25, 1.3]])
+HAND_EFFECTIVE = np.array([[0.0107421875, 0.01953125, -0.0107421875, 0.0], [288.0, -0.5, 0.25, 1.25]])
+
+
+def _two_block_weights():
+    """A [FIR(3), MLP(2)] model at d = 4, vocab 6, as float64 arrays: every
+    matrix starts with the hand-worked rows, the rest random."""
+    from evs_synth.configs import Block, ModelConfig
+    cfg = ModelConfig("fp8_pin", 4, 6, [Block("fir", fir_len=3), Block("mlp", d_ff=2)], dtype="bf16")
+    rng = np.random.default_rng(11)
+    shapes = {"embed": (6, 4), "b0.w_in": (12, 4), "b0.taps": (4, 3), "b0.w_out": (4, 4),
+              "b1.w_gu": (4, 4), "b1.w_down": (4, 2), "lm_head": (6, 4)}
+    w = {}
+    for name, (r, c) in shapes.items():
+        a = rng.standard_normal((r, c)) * np.exp(rng.uniform(-6, 3, (r, 1)))
+        if c == 4 and name != "b0.taps":
+            a[:2] = HAND_ROWS
+        # fp32 values (as bf16 model weights are), so W / s is exact in fp32 and
+        # torch's fp32 -> e4m3 conversion rounds once
+        w[name] = a.astype(np.float32).astype(np.float64)
+    return cfg, w
+
+
+def test_fp8_weights_changes_only_block_projections_row_by_row():
+    from oracle.fp8 import fp8_weights
+    cfg, w = _two_block_weights()
+    out = fp8_weights(cfg, w)
+    assert set(out) == set(w)
+    # the embedding, LM head and FIR taps pass through untouched (their hand
+    # rows are not E4M3 values, so quantising them would show)
+    for name in ("embed", "lm_head", "b0.taps"):
+        assert np.array_equal(np.asarray(out[name]), w[name]), name
+    assert not np.array_equal(round_e4m3(HAND_ROWS), HAND_ROWS)
+    for name in ("b0.w_in", "b0.w_out", "b1.w_gu"):
+        assert np.array_equal(out[name][:2], HAND_EFFECTIVE), name
+    assert not np.array_equal(np.asarray(w['embed'][:2]), HAND_EFFECTIVE)
+    # every row of every projection (w_down has 2 columns: no hand rows):
+    # e4m3(W[n] / s_n) * s_n with s_n from that row alone, e4m3 by torch
+    for name in ("b0.w_in", "b0.w_out", "b1.w_gu", "b1.w_down"):
+        W = w[name]
+        for n in range(W.shape[0]):
+            amax = np.abs(W[n]).max()
+            s = 2.0 ** np.ceil(np.log2(amax / E4M3_MAX))     # smallest power of two with amax <= 448 s
+            expect = _torch_e4m3(W[n] / s) * s
+            assert np.array_equal(out[name][n], expect), (name, n)

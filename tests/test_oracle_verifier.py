@@ -170,6 +170,12 @@ def test_greedy_rules():
     assert verify_greedy(logits, [2, 0]) == (0, 1)       # mismatch at 0 emits argmax
     assert verify_greedy(logits, [1, 3]) == (1, 0)
     assert argmax_lowest(np.array([np.nan, 1.0, np.nan], np.float32)) == 1
+    # NaN reads as -inf in a logits row but as probability 0 in a probability
+    # row: [NaN, 0, 0] has its maximum at id 1 as logits and at id 0 (every
+    # entry 0, lowest id) as probabilities
+    nanrow = np.array([[np.nan, 0.0, 0.0]], np.float32)
+    assert verify_greedy(nanrow, []) == (0, 1)
+    assert verify_greedy(nanrow, [], target_is_probs=True) == (0, 0)
 
 
 def test_degenerate_target_falls_back_to_argmax():
