@@ -81,6 +81,7 @@ class Pending:
     k_new: Dict[int, np.ndarray] = field(default_factory=dict)  # [P, H, Dh]
     v_new: Dict[int, np.ndarray] = field(default_factory=dict)  # [P, H, Dh]
     x_out: Dict[int, np.ndarray] = field(default_factory=dict)  # residual after block i, [P, d]
+    z: Dict[int, np.ndarray] = field(default_factory=dict)      # mixer in-projection [q|k|v], [P, 3d]
 
     @property
     def P(self):
@@ -259,6 +260,7 @@ class HybridLM:
             M = self.st(gelu(G) * Up)
             return X + self.st(M @ self.W[f"b{i}.w_down"].T)
         Z = self.st(U @ self.W[f"b{i}.w_in"].T)
+        pend.z[i] = Z
         Q, K, V = Z[:, :d], Z[:, d:2 * d], Z[:, 2 * d:]
         if b.kind == "fir":
             Hh = K * V                                            # [P, d]

@@ -138,29 +138,42 @@ def committed_equal(cfg, sa, ba, sb, bb):
     return True
 
 
+@pytest.mark.timeout(900)
 def test_c5_ragged_batch_gamma_sweep_full_stack():
     """The 32-layer 7B-shaped stack, B = 8 with contexts ~ U{1024..32768}
     (imported state), gamma swept 1, 4, 8, 12, 16 in consecutive rounds. Each
     round: the ragged block against each sequence run alone (logits bit for
-    bit), the verifier on Dirichlet(0.3) (p, q) pairs against the oracle
-    verifier, a ragged rollback to n_acc + 1, and every sequence's committed
-    state against its solo twin's."""
+    bit), two of the eight sequences (the two shortest contexts) against the
+    fp64 oracle, which follows them through every round on its own state
+    (logits within 2e-2 or one bf16 step), the verifier on Dirichlet(0.3)
+    (p, q) pairs against the oracle verifier, a ragged rollback to n_acc + 1,
+    and every sequence's committed state against its solo twin's."""
     cfg = es.stack_7b()
     B, gmax = 8, 16
     ctx = es.gen.rng_for(23, "c5-contexts").integers(1024, 32769, B)
     print(f"C5: contexts {list(ctx)}", flush=True)
     w = es.make_weights(cfg, seed=22, device=DEV)
     model = evs.Model(cfg, w, device=DEV)
+    wcpu = {k: v.cpu() for k, v in w.items()}
     del w
     max_ctx = int(ctx.max()) + 5 * (gmax + 1) + 16
     batch = evs.State(model, B, max_ctx, gmax + 1, device=DEV)
     solo = [evs.State(model, 1, max_ctx, gmax + 1, device=DEV) for _ in range(B)]
+    watch = [int(b) for b in np.argsort(ctx)[:2]]
+    synth_cpu = {}
     for b in range(B):
         synth = es.synthetic_state(cfg, int(ctx[b]), seed=100 + b, device=DEV)
         import_state(batch, cfg, synth, int(ctx[b]), b)
         import_state(solo[b], cfg, synth, int(ctx[b]), 0)
+        if b in watch:
+            synth_cpu[b] = {i: {k: v.cpu() for k, v in st.items()} for i, st in synth.items()}
         del synth
     torch.cuda.synchronize()
+    print(f"C5: oracle weights (fp64) for sequences {watch}", flush=True)
+    orc = HybridLM(cfg, wcpu)
+    del wcpu
+    ost = {b: orc.import_state(int(ctx[b]), synth_cpu[b]) for b in watch}
+    del synth_cpu
     for r, gamma in enumerate((1, 4, 8, 12, 16)):
         P = gamma + 1
         print(f"C5: round {r}, gamma {gamma}", flush=True)
@@ -173,6 +186,13 @@ def test_c5_ragged_batch_gamma_sweep_full_stack():
         for b in range(B):
             one, _ = block_verify(model, solo[b], cand[b:b + 1])
             assert np.array_equal(one[0], lg[b]), (gamma, b)
+        opend = {}
+        for b in watch:
+            opend[b] = orc.block(ost[b], cand[b])
+            err = logit_err(lg[b], opend[b].logits)
+            print(f"C5: round {r}, sequence {b} (context {int(lengths(batch)[b])}): oracle bar value {err:.4g}",
+                  flush=True)
+            assert err < LOGIT_ATOL, (gamma, b, err)
         u = es.uniforms((B, P), seed=50 + r)
         a, n, keep = run_verify(B, gamma, cfg.vocab, torch.as_tensor(pt).to(DEV), evs.EVS_TARGET_PROBS_F32,
                                 qd, drafts, u)
@@ -183,6 +203,8 @@ def test_c5_ragged_batch_gamma_sweep_full_stack():
         for b in range(B):
             rollback(solo[b], keep[b:b + 1])
         assert np.array_equal(lengths(batch), t_before + keep)
+        for b in watch:
+            ost[b] = orc.rollback(opend[b], int(keep[b]))
         for b in range(B):
             assert committed_equal(cfg, batch, b, solo[b], 0), (gamma, b)
     assert batch.error() == 0 and all(s.error() == 0 for s in solo)
