@@ -11,7 +11,7 @@ The pages name these parts but give none of their formulas; the readings:
   * hidden-state export: h = the target's fp32 residual row after layer 27
     at the last consumed block position (the row whose logits produced the
     token the drafter continues from);
-  * injection: z = st(rmsnorm(h) W_inj^T), W_inj [d, inject_dim]. The RMS
+  * injection: z = st(st(rmsnorm(h)) W_inj^T), W_inj [d, inject_dim]. The RMS
     normalisation makes the prefix independent of the hidden state's scale
     (the pages report residual magnitudes near 1e11 in the last target blocks
     and carry them in fp32 for that reason);
@@ -19,7 +19,7 @@ The pages name these parts but give none of their formulas; the readings:
     drafter's (frozen) token embedding and pos its position embeddings;
   * trunk: the drafter's blocks (one pre-norm causal attention + gated MLP
     layer) over the gamma slots from an empty state, then the final RMSNorm
-    and the untied head: l_i = st(rmsnorm(x_i) W_o^T). Causal attention makes
+    and the untied head: l_i = st(st(rmsnorm(x_i)) W_o^T). Causal attention makes
     slot i independent of the slots after it (the exact causal prefix);
   * Markov head: l'_i = fp32(l_i) + T[d_{i-1}], T a full [V, V] fp32 matrix,
     d_{-1} = x_last, so the drafts are drawn one after another;
@@ -65,9 +65,9 @@ class Drafter:
         self.W = self.lm.W
 
     def prefix(self, hidden_row):
-        """z = st(rmsnorm(h) W_inj^T) for one exported target row h."""
+        """z = st(st(rmsnorm(h)) W_inj^T) for one exported target row h."""
         h = np.asarray(hidden_row, dtype=np.float64)
-        return self.lm.st(rmsnorm(h, self.lm.eps) @ self.W["inject"].T)
+        return self.lm.st(self.lm.st(rmsnorm(h, self.lm.eps)) @ self.W["inject"].T)
 
     def slots(self, hidden_row, last_tok: int, gamma: int):
         """Input rows of the gamma draft slots, [gamma, d]."""

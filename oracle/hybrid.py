@@ -7,7 +7,9 @@ recurrent states that depend on the whole accepted prefix, and append-only
 attention KV caches. The pages give no layer formulas; the readings used here:
 
   * model   = embedding -> pre-norm residual blocks -> RMSNorm -> untied LM head;
-  * norm    = RMSNorm, unit gain, eps from the config;
+  * norm    = RMSNorm, unit gain, eps from the config; its output is rounded
+              to the storage type as the operand of the product it feeds
+              (the mixer, the MLP and the LM head alike);
   * mixer   = z = u W_in^T split [q | k | v]; h = k * v; y = op(h); o = q * y;
               x += o W_out^T, where op is
       FIR   : y_t[c] = sum_{j<L} taps[c, j] * h_{t-j}[c]   (h before position 0 is 0);
@@ -134,15 +136,42 @@ def causal_attention(Kc, Vc, Qh, Kn, Vn):
 
 
 class HybridLM:
-    def __init__(self, cfg, weights):
+    def __init__(self, cfg, weights, accumulate: str = "f64"):
+        """accumulate: "f64" (the reference: every product and sum of a
+        matrix product in float64) or "f32" (the block form's matrix products
+        accumulate in float32, as an implementation with fp32 accumulators
+        does; operands are the same stored values, so only the rounding of
+        the sums differs). The step form always uses float64."""
+        if accumulate not in ("f64", "f32"):
+            raise ValueError(accumulate)
         self.cfg = cfg
         self.d = cfg.d_model
         self.W = {k: _f64(v) for k, v in weights.items()}
         self.dt = cfg.dtype
         self.eps = float(cfg.norm_eps)
+        self.acc = accumulate
 
     def st(self, x):
         return store(x, self.dt)
+
+    def mm(self, A, W):
+        """A @ W^T with the block form's accumulation (see __init__)."""
+        if self.acc == "f32":
+            return (np.asarray(A, np.float32) @ np.asarray(W, np.float32).T).astype(np.float64)
+        return A @ W.T
+
+    def with_accumulation(self, accumulate: str) -> "HybridLM":
+        """The same model (weights shared, not copied) with another accumulation."""
+        if accumulate not in ("f64", "f32"):
+            raise ValueError(accumulate)
+        other = copy.copy(self)
+        other.acc = accumulate
+        return other
+
+    def head(self, X):
+        """Logits of residual rows X [P, d]: final RMSNorm (rounded to the
+        storage type as the head's operand) and the LM head."""
+        return self.st(self.mm(self.st(rmsnorm(X, self.eps)), self.W["lm_head"]))
 
     # ------------------------------------------------------------------ state
     def empty_state(self) -> SeqState:
@@ -179,7 +208,7 @@ class HybridLM:
         for i, b in enumerate(self.cfg.blocks):
             x = self._block_step(i, b, s, x)
         s.t += 1
-        logits = self.st(self.W["lm_head"] @ rmsnorm(x, self.eps))
+        logits = self.st(self.W["lm_head"] @ self.st(rmsnorm(x, self.eps)))
         return logits, s
 
     def _block_step(self, i, b, s: SeqState, x):
@@ -245,7 +274,7 @@ class HybridLM:
             X = self.block_layer(i, b, state, X, pend)
             if keep_x:
                 pend.x_out[i] = X.copy()
-        pend.logits = self.st(rmsnorm(X, self.eps) @ self.W["lm_head"].T)
+        pend.logits = self.head(X)
         return pend
 
     def block_layer(self, i, b, state: SeqState, X, pend: Pending):
@@ -255,11 +284,11 @@ class HybridLM:
         U = self.st(rmsnorm(X, self.eps))
         if b.kind == "mlp":
             wgu = self.W[f"b{i}.w_gu"]
-            G = self.st(U @ wgu[: b.d_ff].T)
-            Up = self.st(U @ wgu[b.d_ff:].T)
+            G = self.st(self.mm(U, wgu[: b.d_ff]))
+            Up = self.st(self.mm(U, wgu[b.d_ff:]))
             M = self.st(gelu(G) * Up)
-            return X + self.st(M @ self.W[f"b{i}.w_down"].T)
-        Z = self.st(U @ self.W[f"b{i}.w_in"].T)
+            return X + self.st(self.mm(M, self.W[f"b{i}.w_down"]))
+        Z = self.st(self.mm(U, self.W[f"b{i}.w_in"]))
         pend.z[i] = Z
         Q, K, V = Z[:, :d], Z[:, d:2 * d], Z[:, 2 * d:]
         if b.kind == "fir":
@@ -279,7 +308,7 @@ class HybridLM:
             O = self.st(Oh.reshape(P, d))
         else:
             raise ValueError(b.kind)
-        return X + self.st(O @ self.W[f"b{i}.w_out"].T)
+        return X + self.st(self.mm(O, self.W[f"b{i}.w_out"]))
 
     def rollback(self, pend: Pending, n_keep: int) -> SeqState:
         """State sliced to the first ``n_keep`` candidate positions (0..P)."""

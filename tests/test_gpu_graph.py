@@ -44,6 +44,7 @@ def test_graph_replay_matches_eager_across_ragged_n_keep():
     prefill(model, se, prompts)
 
     cand = torch.zeros(B, P, dtype=torch.int32, device=DEV)
+    drafts = torch.zeros(B, gamma, dtype=torch.int32, device=DEV)      # cand[:, 1:], contiguous
     u = torch.zeros(B, P, dtype=torch.float32, device=DEV)
     q = torch.zeros(B, gamma, V, dtype=torch.float32, device=DEV)
     lg = torch.zeros(B, P, V, dtype=torch.bfloat16, device=DEV)
@@ -53,7 +54,7 @@ def test_graph_replay_matches_eager_across_ragged_n_keep():
 
     def round_on(state, cand, u, q, lg, acc, nxt, keep):
         evs.evs_block_verify(model, state, cand, gamma, lg)
-        evs.evs_verify_sample(B, gamma, V, lg, evs.EVS_TARGET_LOGITS_BF16, q, cand[:, 1:], u, 1.0, 0, 0,
+        evs.evs_verify_sample(B, gamma, V, lg, evs.EVS_TARGET_LOGITS_BF16, q, drafts, u, 1.0, 0, 0,
                               acc, nxt, keep)
         evs.evs_rollback(state, keep)
 
@@ -71,6 +72,7 @@ def test_graph_replay_matches_eager_across_ragged_n_keep():
         for b in range(B):
             qq[b, np.arange(gamma), c[b, 1:]] = 1.0
         cand.copy_(torch.from_numpy(c))
+        drafts.copy_(torch.from_numpy(np.ascontiguousarray(c[:, 1:])))
         u.copy_(torch.from_numpy(uu))
         q.copy_(torch.from_numpy(qq))
         return c, reject

@@ -144,8 +144,10 @@ def test_c5_ragged_batch_gamma_sweep_full_stack():
     (imported state), gamma swept 1, 4, 8, 12, 16 in consecutive rounds. Each
     round: the ragged block against each sequence run alone (logits bit for
     bit), two of the eight sequences (the two shortest contexts) against the
-    fp64 oracle, which follows them through every round on its own state
-    (logits within 2e-2 or one bf16 step), the verifier on Dirichlet(0.3)
+    oracle, which follows them through every round on its own state (the LM
+    head on the GPU's final residual rows within 2e-2 or one bf16 step; the
+    free-running logits within 1.5x of the drift the oracle's own arithmetic
+    shows with fp32 accumulators), the verifier on Dirichlet(0.3)
     (p, q) pairs against the oracle verifier, a ragged rollback to n_acc + 1,
     and every sequence's committed state against its solo twin's."""
     cfg = es.stack_7b()
@@ -172,8 +174,13 @@ def test_c5_ragged_batch_gamma_sweep_full_stack():
     print(f"C5: oracle weights (fp64) for sequences {watch}", flush=True)
     orc = HybridLM(cfg, wcpu)
     del wcpu
+    o32 = orc.with_accumulation("f32")
     ost = {b: orc.import_state(int(ctx[b]), synth_cpu[b]) for b in watch}
+    ost32 = {b: o32.import_state(int(ctx[b]), synth_cpu[b]) for b in watch}
     del synth_cpu
+    # the residual rows after the last block, for the teacher-forced LM head
+    xlast = torch.zeros(B, gmax + 1, cfg.d_model, dtype=torch.float32, device=DEV)
+    evs.evs_state_export(batch, len(cfg.blocks) - 1, xlast)
     for r, gamma in enumerate((1, 4, 8, 12, 16)):
         P = gamma + 1
         print(f"C5: round {r}, gamma {gamma}", flush=True)
@@ -186,13 +193,23 @@ def test_c5_ragged_batch_gamma_sweep_full_stack():
         for b in range(B):
             one, _ = block_verify(model, solo[b], cand[b:b + 1])
             assert np.array_equal(one[0], lg[b]), (gamma, b)
-        opend = {}
+        opend, opend32 = {}, {}
         for b in watch:
+            # the LM head on the GPU's final residual rows: the 2e-2 bar
+            # (the export is laid out [B, gamma + 1, d] for this call's gamma)
+            xl = xlast.view(-1)[: B * P * cfg.d_model].view(B, P, cfg.d_model)
+            err = logit_err(lg[b], orc.head(xl[b].double().cpu().numpy()))
+            # free running against the drift of fp32 accumulation in the
+            # oracle's own arithmetic (as in the 7B-shaped stack test)
             opend[b] = orc.block(ost[b], cand[b])
-            err = logit_err(lg[b], opend[b].logits)
-            print(f"C5: round {r}, sequence {b} (context {int(lengths(batch)[b])}): oracle bar value {err:.4g}",
-                  flush=True)
+            opend32[b] = o32.block(ost32[b], cand[b])
+            dg, d32 = np.abs(lg[b] - opend[b].logits), np.abs(opend32[b].logits - opend[b].logits)
+            rg, r32 = np.sqrt(np.mean(dg ** 2)), np.sqrt(np.mean(d32 ** 2))
+            print(f"C5: round {r}, sequence {b} (context {int(lengths(batch)[b])}): teacher-forced head bar "
+                  f"value {err:.4g}; free running GPU max {dg.max():.4g} rms {rg:.4g}, fp32-accumulation "
+                  f"oracle max {d32.max():.4g} rms {r32:.4g}", flush=True)
             assert err < LOGIT_ATOL, (gamma, b, err)
+            assert rg <= 1.5 * r32 and dg.max() <= max(LOGIT_ATOL, 1.5 * d32.max()), (gamma, b, rg, r32)
         u = es.uniforms((B, P), seed=50 + r)
         a, n, keep = run_verify(B, gamma, cfg.vocab, torch.as_tensor(pt).to(DEV), evs.EVS_TARGET_PROBS_F32,
                                 qd, drafts, u)
@@ -205,6 +222,7 @@ def test_c5_ragged_batch_gamma_sweep_full_stack():
         assert np.array_equal(lengths(batch), t_before + keep)
         for b in watch:
             ost[b] = orc.rollback(opend[b], int(keep[b]))
+            ost32[b] = o32.rollback(opend32[b], int(keep[b]))
         for b in range(B):
             assert committed_equal(cfg, batch, b, solo[b], 0), (gamma, b)
     assert batch.error() == 0 and all(s.error() == 0 for s in solo)

@@ -292,3 +292,20 @@ def test_bf16_storage_points_are_bf16_values():
     for i in pend.k_new:
         k = pend.k_new[i].astype(np.float32)
         assert np.array_equal(torch.from_numpy(k).to(torch.bfloat16).float().numpy(), k)
+
+
+def test_lm_head_reads_the_normed_row_rounded_to_bf16():
+    """Reading R3: the RMSNorm output is rounded to the storage type as the
+    operand of the product it feeds, the LM head included. Hand-worked: x =
+    [9, 1, 1, 1] has rms sqrt(21) = 4.5826, so u = [1.96396, 0.21822 x 3],
+    which bf16 holds as [1.9609375, 0.2177734375 x 3] (steps 2^-7 and 2^-10).
+    A head row of ones sums them to 2.6142578125 -> bf16 2.609375 (step 2^-6);
+    summing the unrounded u (2.61861) would give 2.625 instead."""
+    from evs_synth.configs import ModelConfig
+    cfg = ModelConfig("lm_head_pin", 4, 2, [], dtype="bf16")
+    w = {"embed": np.array([[9.0, 1, 1, 1], [1, 1, 1, 1]]), "lm_head": np.array([[1.0, 1, 1, 1], [1, 0, 0, 0]])}
+    orc = HybridLM(cfg, w)
+    want = [2.609375, 1.9609375]
+    assert list(orc.block(orc.empty_state(), [0]).logits[0]) == want
+    assert list(orc.step(orc.empty_state(), 0)[0]) == want
+    assert list(HybridLM(cfg, w, accumulate="f32").block(orc.empty_state(), [0]).logits[0]) == want
