@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -562,6 +563,35 @@ evs_status draft_pass(evs_model* m, evs_state* s, int B, const float* hidden, in
 
 }  // namespace
 
+// ------------------------------------------------------ no-allocation scratch
+// The workspace of evs_block_verify_noalloc: one array per GPU, resident for
+// the life of the process. Host code never passes `scratch` itself to a
+// kernel (on the host it names a stand-in, not device memory): each device's
+// address is looked up once with hipGetSymbolAddress, with that device
+// current, and that pointer is what the forward uses.
+static __device__ __align__(256) unsigned char scratch[EVS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_dev[SCRATCH_MAX_DEVICES] = {};
+
+// The current device's scratch address (looked up on the first call on that device).
+evs_status scratch_ptr(char** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return EVS_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return EVS_E_HIP;
+    scratch_dev[dev] = p;
+  }
+  *out = reinterpret_cast<char*>(scratch_dev[dev]);
+  return EVS_OK;
+}
+}  // namespace
+
 // =================================================================== C ABI
 extern "C" {
 
@@ -707,7 +737,9 @@ evs_status evs_state_bytes(const evs_model* m, int32_t batch, int32_t max_ctx, i
 
 evs_status evs_state_create(const evs_model* m, int32_t batch, int32_t max_ctx, int32_t max_block, void* state_dev,
                             void* workspace_dev, void* stream, evs_state** out) {
-  if (!out || !state_dev || !workspace_dev || ((uintptr_t)state_dev % ALIGN) || ((uintptr_t)workspace_dev % ALIGN))
+  // (workspace_dev NULL: a state with no workspace of its own, for
+  // evs_block_verify_noalloc)
+  if (!out || !state_dev || ((uintptr_t)state_dev % ALIGN) || ((uintptr_t)workspace_dev % ALIGN))
     return EVS_E_INVALID;
   evs_state* s = new (std::nothrow) evs_state();
   if (!s) return EVS_E_INVALID;
@@ -784,7 +816,7 @@ evs_status evs_state_error(evs_state* s, int32_t* host_word, int32_t clear, void
 evs_status evs_prefill(evs_model* m, evs_state* s, const int32_t* tokens, const int32_t* offs, void* last_logits,
                        void* stream) {
   if (!m || !s || !tokens || !offs || s->m != m) return EVS_E_INVALID;
-  if (s->pending) return EVS_E_STATE;
+  if (s->pending || !s->wb) return EVS_E_STATE;
   for (int b = 0; b < s->B; ++b)
     if (offs[b + 1] < offs[b] || offs[b] < 0) return EVS_E_INVALID;
   for (int b = 0; b < s->B; ++b)
@@ -814,6 +846,7 @@ evs_status evs_block_verify(evs_model* m, evs_state* s, const int32_t* cand, int
                             void* stream) {
   if (!m || !s || !cand || !logits || s->m != m) return EVS_E_INVALID;
   if (gamma < 0 || gamma + 1 > s->max_block) return EVS_E_RANGE;
+  if (!s->wb) return EVS_E_STATE;
   s->pending = false;   // a pending block is discarded (rollback to 0 changes nothing on device)
   EVS_TRY(forward_any(m, s, 0, s->B, gamma + 1, cand, logits, reinterpret_cast<hipStream_t>(stream),
                       s->export_block >= 0 ? s->export_dst : nullptr));
@@ -829,6 +862,30 @@ evs_status evs_rollback(evs_state* s, const int32_t* n_keep, void* stream) {
   HIP_TRY(launch_commit(sp<int>(s, s->off_t), sp<int>(s, s->off_ib), sp<int>(s, s->off_is), n_keep, s->pending_P,
                         s->B, s->pending_P, sp<int>(s, s->off_err), reinterpret_cast<hipStream_t>(stream)));
   s->pending = false;
+  return EVS_OK;
+}
+
+evs_status evs_block_verify_noalloc(evs_model* m, evs_state* s, const int32_t* cand, int32_t gamma, void* logits,
+                                    void* stream) {
+  if (!m || !s || !cand || !logits || s->m != m) return EVS_E_INVALID;
+  if (gamma < 0 || gamma + 1 > s->max_block) return EVS_E_RANGE;
+  if (s->ws_total > (size_t)EVS_NOALLOC_SCRATCH_BYTES) return EVS_E_RANGE;
+  char* ws = nullptr;
+  EVS_TRY(scratch_ptr(&ws));
+  // the same forward over the device scratch; no timing events (creating
+  // them could allocate)
+  char* own = s->wb;
+  const bool timing = s->timing;
+  s->wb = ws;
+  s->timing = false;
+  s->pending = false;
+  const evs_status r = forward_any(m, s, 0, s->B, gamma + 1, cand, logits, reinterpret_cast<hipStream_t>(stream),
+                                   s->export_block >= 0 ? s->export_dst : nullptr);
+  s->wb = own;
+  s->timing = timing;
+  if (r != EVS_OK) return r;
+  s->pending = true;
+  s->pending_P = gamma + 1;
   return EVS_OK;
 }
 
@@ -870,6 +927,7 @@ evs_status evs_draft(evs_model* m, evs_state* s, int32_t batch, const float* hid
                      void* stream) {
   if (!m || !s || s->m != m || m->desc.inject_dim <= 0) return EVS_E_INVALID;
   if (!hidden || hidden_rows < 1 || !last || !logits || !drafts || (!greedy && !u)) return EVS_E_INVALID;
+  if (!s->wb) return EVS_E_STATE;
   if (!(temperature > 0.f && std::isfinite(temperature))) return EVS_E_INVALID;
   if (batch < 1 || batch > s->B || gamma < 1 || gamma > m->desc.max_slots) return EVS_E_RANGE;
   if (gamma > s->max_block) return EVS_E_RANGE;

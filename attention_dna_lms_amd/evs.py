@@ -32,7 +32,8 @@ EXPORTS = ("evs_status_string", "evs_canonical_count", "evs_canonical_shape", "e
            "evs_model_create", "evs_pack_weights", "evs_model_destroy", "evs_state_bytes", "evs_state_create",
            "evs_state_destroy", "evs_state_tensor", "evs_state_error", "evs_prefill", "evs_block_verify",
            "evs_rollback", "evs_verify_sample", "evs_state_export", "evs_draft", "evs_state_timing",
-           "evs_state_timing_read")
+           "evs_state_timing_read", "evs_block_verify_noalloc")
+EVS_NOALLOC_SCRATCH_BYTES = 32 << 20
 EVS_KC_GEMM, EVS_KC_ATTN = 1, 2
 
 
@@ -83,6 +84,7 @@ def lib():
         "evs_state_error": [c_void_p, POINTER(c_int32), c_int32, c_void_p],
         "evs_prefill": [c_void_p, c_void_p, c_void_p, POINTER(c_int32), c_void_p, c_void_p],
         "evs_block_verify": [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p],
+        "evs_block_verify_noalloc": [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p],
         "evs_rollback": [c_void_p, c_void_p, c_void_p],
         "evs_state_timing": [c_void_p, c_int32, c_int64],
         "evs_state_timing_read": [c_void_p, c_int32, POINTER(ctypes.c_double), POINTER(c_int64),
@@ -203,7 +205,8 @@ class Model:
 class State:
     """Inference state of `batch` sequences plus the call workspace."""
 
-    def __init__(self, model: Model, batch: int, max_ctx: int, max_block: int, device="cuda"):
+    def __init__(self, model: Model, batch: int, max_ctx: int, max_block: int, device="cuda", workspace=True):
+        """workspace=False: no workspace of its own (evs_block_verify_noalloc only)."""
         L = lib()
         self.model = model
         self.B, self.max_ctx, self.max_block = batch, max_ctx, max_block
@@ -212,7 +215,7 @@ class State:
                "evs_state_bytes")
         self.state_bytes, self.workspace_bytes = sb.value, wb.value
         self._sraw, self.buf = _aligned_buffer(sb.value, device)
-        self._wraw, self.ws = _aligned_buffer(wb.value, device)
+        self._wraw, self.ws = _aligned_buffer(wb.value, device) if workspace else (None, None)
         h = c_void_p()
         _check(L.evs_state_create(model.handle, batch, max_ctx, max_block, _ptr(self.buf), _ptr(self.ws), _stream(),
                                   ctypes.byref(h)), "evs_state_create")
@@ -264,6 +267,11 @@ def evs_prefill(model: Model, state: State, tokens: torch.Tensor, seq_offsets, l
 def evs_block_verify(model: Model, state: State, cand: torch.Tensor, gamma: int, logits: torch.Tensor):
     _check(lib().evs_block_verify(model.handle, state.handle, _ptr(cand), int(gamma), _ptr(logits), _stream()),
            "evs_block_verify")
+
+
+def evs_block_verify_noalloc(model: Model, state: State, cand: torch.Tensor, gamma: int, logits: torch.Tensor):
+    _check(lib().evs_block_verify_noalloc(model.handle, state.handle, _ptr(cand), int(gamma), _ptr(logits),
+                                          _stream()), "evs_block_verify_noalloc")
 
 
 def evs_rollback(state: State, n_keep=None):

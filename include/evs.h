@@ -164,7 +164,11 @@ evs_status evs_state_bytes(const evs_model* m, int32_t batch, int32_t max_ctx,
 
 /* Create a state over caller-owned buffers (256-byte aligned) and enqueue their
  * initialisation on `stream`: every sequence empty (t = 0, zero IIR state),
- * error word cleared, workspace counters zeroed. */
+ * error word cleared (the workspace needs no initialisation).
+ * workspace_dev may be NULL: the state then has no workspace of its own, and
+ * evs_prefill, evs_block_verify and evs_draft on it return EVS_E_STATE; use
+ * evs_block_verify_noalloc (and evs_rollback with all positions kept to
+ * consume a prompt chunk). */
 evs_status evs_state_create(const evs_model* m, int32_t batch, int32_t max_ctx,
                             int32_t max_block, void* state_dev, void* workspace_dev,
                             void* stream, evs_state** out);
@@ -203,6 +207,25 @@ evs_status evs_prefill(evs_model* m, evs_state* s, const int32_t* tokens_dev,
  * discards the pending block (rollback to 0). 0 <= gamma < max_block. */
 evs_status evs_block_verify(evs_model* m, evs_state* s, const int32_t* cand_dev,
                             int32_t gamma, void* logits_dev, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * evs_block_verify with the call's workspace taken from a library-owned device
+ * array of EVS_NOALLOC_SCRATCH_BYTES per GPU (resident until the process
+ * ends) instead of the state's own workspace, so the state may have been
+ * created with workspace_dev = NULL. Results are those of evs_block_verify bit
+ * for bit (same kernels, same order). Allocates nothing: no hipMalloc, no
+ * hipFree, no event creation (the state's timing is not recorded for it).
+ * Errors: as evs_block_verify; EVS_E_RANGE if the state's workspace (see
+ * evs_state_bytes) exceeds EVS_NOALLOC_SCRATCH_BYTES; EVS_E_HIP if the scratch
+ * address of the current device cannot be looked up. The scratch is shared by
+ * every call on one GPU and keeps the last call's contents (nothing in it has
+ * to start at zero): calls that overlap on one GPU (other streams, other
+ * threads, other states) race and must be serialised by the caller. The state
+ * and all pointers must live on the current device. */
+#define EVS_NOALLOC_SCRATCH_BYTES (32u << 20)
+evs_status evs_block_verify_noalloc(evs_model* m, evs_state* s, const int32_t* cand_dev,
+                                    int32_t gamma, void* logits_dev, void* stream);
 
 /* Commit the pending block: sequence b keeps the first n_keep_dev[b] positions
  * (0 .. gamma+1; n_accepted + 1 after a verification). Zero bytes of state are
