@@ -74,10 +74,9 @@ struct evs_state {
   // workspace
   size_t w_x = 0, w_nrm = 0, w_o = 0, w_q = 0, w_h = 0, w_logit = 0, w_apart = 0, ws_total = 0;
   size_t apart_floats = 0;
-  size_t w_inj_x = 0, w_inj_nrm = 0, w_z = 0;   // drafter: injected rows, their norm partials, the prefix z
-  size_t w_u = 0;                               // bf16 models: normed rows for multi-tile launches
+  size_t w_inj_x = 0, w_z = 0;                  // drafter: the normalised injected rows, the prefix z
+  size_t w_xb = 0;                              // bf16 models: the residual rows in bf16 (normed operands)
   size_t w_part = 0, part_bytes = 0;            // bf16 models: split-K partials of multi-tile launches
-  int inj_ld = 0;
   int export_block = -1;                        // hidden-state export after this block (evs_block_verify)
   float* export_dst = nullptr;
   bool pending = false;
@@ -270,7 +269,7 @@ void layout_state(evs_state* s) {
   s->apart_floats = (size_t)B * s->qtn_max * H * s->S * 16 * (DHm + 2);
   s->w_apart = take(s->apart_floats * 4);
   if (es == 2) {
-    s->w_u = take(M16 * d * 2);
+    s->w_xb = take(M16 * d * 2);
     // split-K partials: 8 ranges x the padded rows of the widest slicing that
     // splits x the widest projection
     size_t rows = 0;
@@ -288,9 +287,7 @@ void layout_state(evs_state* s) {
   }
   if (m->desc.inject_dim > 0) {
     const size_t B16 = align_up((size_t)B, 16);
-    s->inj_ld = (int)B16;
-    s->w_inj_x = take(B16 * m->desc.inject_dim * 4);
-    s->w_inj_nrm = take((size_t)(m->desc.inject_dim / 16) * B16 * 4);
+    s->w_inj_x = take(B16 * m->desc.inject_dim * es);
     s->w_z = take(B16 * d * es);
   }
   s->ws_total = off;
@@ -348,18 +345,9 @@ hipError_t timed(evs_state* s, int kc, double bytes, hipStream_t st, F&& launch)
 #define HIP_TRY(x) do { if ((x) != hipSuccess) return EVS_E_HIP; } while (0)
 
 // ------------------------------------------------------------------ forward
-// where a normed GEMM finds its input rows' per-16-column sums of squares
-// (default: the forward's residual rows)
-struct NormSrc {
-  const float* part;
-  int n_part, ld;
-  float fd;
-};
-
 template <typename T>
 evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int epi, const void* A, int lda,
-                     int nseq, int P, GemmArgs a, hipStream_t st, int scratch_floats = 0,
-                     const NormSrc* ns = nullptr) {
+                     int nseq, int P, GemmArgs a, hipStream_t st, int scratch_floats = 0) {
   const Slicing sl = slicing(nseq, P);
   a.W = reinterpret_cast<const uint4*>(m->base + mat.off);
   a.ksteps = mat.K / (mat.w8 ? 2 * m->kstep : m->kstep);   // weight steps (FP8: two k-steps each)
@@ -377,19 +365,19 @@ evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int 
   a.lda = lda;
   a.M = nseq * P;
   a.rows_per_slice = sl.rows_per_slice;
-  a.nrm_part = ns ? ns->part : wp<float>(s, s->w_nrm);
-  a.n_part = ns ? ns->n_part : m->desc.d_model / 16;
-  a.nrm_ld = ns ? ns->ld : s->M_max;
-  a.fd = ns ? ns->fd : (float)m->desc.d_model;
+  a.nrm_part = wp<float>(s, s->w_nrm);
+  a.n_part = m->desc.d_model / 16;
+  a.nrm_ld = m->desc.d_model / 16;   // partials per row
+  a.fd = (float)m->desc.d_model;
   a.eps = m->desc.norm_eps;
   // algorithmic bytes: the weights once, the A rows once, the outputs once
-  const double bytes = (double)(mat.bytes(m->es) + mat.scale_bytes()) + (double)a.M * mat.K * (amode == A_NORM ? 4 : m->es) +
+  const double bytes = (double)(mat.bytes(m->es) + mat.scale_bytes()) + (double)a.M * mat.K * m->es +
                        (double)a.M * mat.rows_valid * (epi == E_RESID ? 8 : m->es);
   const size_t lds = gemm_lds(sl.MT, mat.NT, scratch_floats);
   if (lds > LDS_MAX) return EVS_E_UNSUPPORTED;
-  // multi-tile bf16 launches over normed rows: k-range partials, then the
-  // reduction and epilogue (the same results as one kernel)
-  if (m->desc.dtype == EVS_BF16 && !mat.w8 && amode == A_ACT && sl.MT >= SPLIT_MT &&
+  // multi-tile bf16 launches: k-range partials, then the reduction and
+  // epilogue (the same results as one kernel)
+  if (m->desc.dtype == EVS_BF16 && !mat.w8 && sl.MT >= SPLIT_MT &&
       (size_t)8 * sl.slices * sl.MT * 16 * mat.n_groups * mat.NT * 16 * 4 <= s->part_bytes) {
     a.part = wp<float>(s, s->w_part);
     // 9 row tiles: range-pair partials (half the partial bytes for twice the
@@ -416,34 +404,19 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
                    hipStream_t st, float* export_dst = nullptr) {
   const int d = m->desc.d_model, M = nseq * P;
   float* x = wp<float>(s, s->w_x);
+  // the residual rows in the storage type: the operand of every normed
+  // projection, written by the same producer as x and its norm partials
+  bf16* xb = sizeof(T) == 2 ? wp<bf16>(s, s->w_xb) : nullptr;
   float* nrm = wp<float>(s, s->w_nrm);
   int* t = sp<int>(s, s->off_t);
   int* err = sp<int>(s, s->off_err);
-  // bf16 models: the gate/up projection, and every normed projection of a
-  // launch of more than one 16-row tile, read the normed rows from a norm
-  // kernel (the same bf16 operands the fused prologue would form, so results
-  // are unchanged): one bf16 load per step instead of two fp32 loads per tile
-  // and step, and half the registers for the operands. A single-tile
-  // in-projection or LM head saves less than the extra launch costs. FP8
-  // weights: the single-tile gate/up only.
-  const bool multi_tile = slicing(nseq, P).MT >= 2;
-  const bool bf16_w = sizeof(T) == 2 && m->desc.dtype == EVS_BF16;
-  const bool fp8_w = sizeof(T) == 2 && m->desc.dtype == EVS_BF16_FP8W;
-  auto normed = [&](int& amode, const void*& A, bool gate_up = false) -> evs_status {
+  auto normed = [&](int& amode, const void*& A) -> evs_status {
     amode = A_NORM;
-    A = x;
-    if constexpr (sizeof(T) == 2) {
-      if ((bf16_w && (multi_tile || gate_up)) || (fp8_w && gate_up && !multi_tile)) {
-        bf16* u = wp<bf16>(s, s->w_u);
-        HIP_TRY(launch_norm_rows(x, nrm, d / 16, s->M_max, (float)d, m->desc.norm_eps, M, d, u, st));
-        amode = A_ACT;
-        A = u;
-      }
-    }
+    A = sizeof(T) == 2 ? static_cast<const void*>(xb) : static_cast<const void*>(x);
     return EVS_OK;
   };
   if (tokens)
-    HIP_TRY(launch_embed<T>(tokens, reinterpret_cast<const T*>(m->base + m->embed), x, nrm, s->M_max, M, d,
+    HIP_TRY(launch_embed<T>(tokens, reinterpret_cast<const T*>(m->base + m->embed), x, xb, nrm, d / 16, M, d,
                             m->desc.vocab, P, seq0, t, s->max_ctx, err, st));
   for (size_t i = 0; i < m->plan.size(); ++i) {
     if (i > 0 && export_dst && (int)i - 1 == s->export_block) HIP_TRY(launch_export_rows<T>(x, export_dst, M, d, st));
@@ -454,10 +427,10 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
       a.ldo = p.d.d_ff;
       int am;
       const void* A;
-      EVS_TRY(normed(am, A, true));
+      EVS_TRY(normed(am, A));
       EVS_TRY(gemm_call<T>(m, s, p.w_gu, am, E_GELU, A, d, nseq, P, a, st));
       GemmArgs b{};
-      b.x = x; b.ldx = d; b.nrm_out = nrm;
+      b.x = x; b.ldx = d; b.nrm_out = nrm; b.xb_out = xb;
       EVS_TRY(gemm_call<T>(m, s, p.w_down, A_ACT, E_RESID, wp<void>(s, s->w_h), p.d.d_ff, nseq, P, b, st));
       continue;
     }
@@ -513,7 +486,7 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
       HIP_TRY(timed(s, EVS_KC_ATTN, kvb + 2.0 * nseq * P * d * m->es, st, [&] { return launch_attn<T>(at, nseq, st); }));
     }
     GemmArgs b{};
-    b.x = x; b.ldx = d; b.nrm_out = nrm;
+    b.x = x; b.ldx = d; b.nrm_out = nrm; b.xb_out = xb;
     EVS_TRY(gemm_call<T>(m, s, p.w_out, A_ACT, E_RESID, wp<void>(s, s->w_o), d, nseq, P, b, st));
   }
   if (export_dst && s->export_block == (int)m->plan.size() - 1) HIP_TRY(launch_export_rows<T>(x, export_dst, M, d, st));
@@ -542,16 +515,16 @@ evs_status draft_pass(evs_model* m, evs_state* s, int B, const float* hidden, in
                       void* logits, int32_t* drafts, float* q, hipStream_t st) {
   const int d = m->desc.d_model, K = m->desc.inject_dim, V = m->desc.vocab;
   int* err = sp<int>(s, s->off_err);
-  float* xin = wp<float>(s, s->w_inj_x);
-  float* inrm = wp<float>(s, s->w_inj_nrm);
+  T* xin = wp<T>(s, s->w_inj_x);
   T* z = wp<T>(s, s->w_z);
-  HIP_TRY(launch_inject_prep<T>(hidden, hidden_rows, hidx, B, K, xin, inrm, s->inj_ld, err, st));
+  HIP_TRY(launch_inject_prep<T>(hidden, hidden_rows, hidx, B, K, m->desc.norm_eps, xin, err, st));
   GemmArgs a{};
   a.N = d; a.out = z; a.ldo = d;
-  const NormSrc ns{inrm, K / 16, s->inj_ld, (float)K};
-  EVS_TRY(gemm_call<T>(m, s, m->inj, A_NORM, E_STORE, xin, K, B, 1, a, st, 0, &ns));
+  EVS_TRY(gemm_call<T>(m, s, m->inj, A_ACT, E_STORE, xin, K, B, 1, a, st));
   HIP_TRY(launch_slots<T>(reinterpret_cast<const T*>(m->base + m->embed), reinterpret_cast<const T*>(m->base + m->pos),
-                          z, last, B, gamma, d, V, wp<float>(s, s->w_x), wp<float>(s, s->w_nrm), s->M_max, err, st));
+                          z, last, B, gamma, d, V, wp<float>(s, s->w_x),
+                          sizeof(T) == 2 ? wp<bf16>(s, s->w_xb) : nullptr, wp<float>(s, s->w_nrm), d / 16, err,
+                          st));
   EVS_TRY(forward<T>(m, s, 0, B, gamma, nullptr, logits, st));
   DraftArgs da{};
   da.logits = logits; da.markov = reinterpret_cast<const float*>(m->base + m->markov); da.last = last; da.u = u;

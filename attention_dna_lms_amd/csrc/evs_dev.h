@@ -72,7 +72,7 @@ __device__ __forceinline__ f32x4 mma_k4(const float a[4], const float b[4], f32x
 }
 
 // ------------------------------------------------------------------ GEMM args
-enum AMode { A_ACT = 0, A_NORM = 1 };                      // storage-type rows / fp32 rows + RMSNorm
+enum AMode { A_ACT = 0, A_NORM = 1 };   // storage-type rows / the same rows with each row's RMSNorm scale on the product
 enum Epi { E_STORE = 0, E_RESID = 1, E_GELU = 2, E_MIXER = 3 };
 enum MixKind { MIX_FIR = 1, MIX_IIR = 2, MIX_ATTN = 3 };
 
@@ -101,17 +101,18 @@ struct GemmArgs {
   long long tstride;     //   and between consecutive k-steps of one wave
   int ksteps;            // K / KSTEP
   int n_groups;
-  const void* A;         // A_ACT: T [M, lda]; A_NORM: f32 [M, lda]
+  const void* A;         // T [M, lda] (A_NORM: the residual rows in the storage type)
   int lda;
   int M;                 // rows in this call
   int rows_per_slice;    // rows per blockIdx.y (a multiple of the positions per sequence)
-  const float* nrm_part; int n_part; int nrm_ld; float fd; float eps;      // A_NORM (fd = d)
+  const float* nrm_part; int n_part; int nrm_ld; float fd; float eps;      // A_NORM: [row][nrm_ld] sums of squares, fd = d
   const float* wscale;   // FP8 weights: one scale per packed row ([group][tile][16]); else null
   // epilogue
   int N;                 // valid output columns (E_STORE)
   void* out; int ldo;    // E_STORE / E_GELU / E_MIXER output (storage type)
   float* x; int ldx;     // E_RESID residual stream
-  float* nrm_out;        // E_RESID per-16-column sum of squares [n_tiles][nrm_ld]
+  float* nrm_out;        // E_RESID per-16-column sums of squares [row][nrm_ld]
+  bf16* xb_out;          // E_RESID, bf16 models: the residual rows in bf16 (the normed projections' operand)
   MixArgs mix;
   float* part;           // split-K launches: the k-range partials [slice][nparts][group][MT][NT][64 lanes][4]
   int nparts;            // 8 (one per k-range) or 4 (range pairs r + (r + 4)); 0 reads as 8
@@ -156,8 +157,10 @@ hipError_t launch_gemm(int MT, int NT, int amode, int epi, const GemmArgs& a, in
                        size_t lds_bytes, hipStream_t st);
 template <typename T>
 hipError_t launch_attn(const AttnArgs& a, int n_seq, hipStream_t st);
+// producers of residual rows write fp32 x, its per-16-column sums of squares
+// and, for bf16 models (xb non-null), the rows in bf16 for the normed projections
 template <typename T>
-hipError_t launch_embed(const int* tokens, const T* E, float* x, float* nrm, int nrm_ld, int M, int d,
+hipError_t launch_embed(const int* tokens, const T* E, float* x, bf16* xb, float* nrm, int nrm_ld, int M, int d,
                         int V, int P, int seq0, const int* t, int max_ctx, int* err, hipStream_t st);
 hipError_t launch_commit(int* t, int* iir_buf, int* iir_slot, const int* n_keep, int n_keep_all,
                          int B, int P, int* err, hipStream_t st);
@@ -167,11 +170,9 @@ hipError_t launch_pack(const T* W, uint4* out, int rows_valid, int K, int n_grou
                        int map_kind, int map_stride, hipStream_t st);
 hipError_t launch_copy_row(const void* src, void* dst, size_t bytes, hipStream_t st);
 hipError_t launch_verify(const VerifyArgs& a, int B, hipStream_t st);
-// multi-tile bf16 launches with pre-normed rows: k-range partials, then the
-// reduction and epilogue (results equal launch_gemm's)
+// multi-tile bf16 launches: k-range partials, then the reduction and
+// epilogue (results equal launch_gemm's)
 hipError_t launch_gemm_split(int MT, int NT, int epi, const GemmArgs& a, int slices, size_t lds, hipStream_t st);
-hipError_t launch_norm_rows(const float* x, const float* nrm, int n_part, int nrm_ld, float fd, float eps, int M,
-                            int K, bf16* u, hipStream_t st);
 
 struct DraftArgs {
   const void* logits;    // [B, gamma, V] storage type: the drafter head's logits
@@ -186,11 +187,11 @@ struct DraftArgs {
 };
 template <typename T> hipError_t launch_export_rows(const float* x, float* dst, int M, int d, hipStream_t st);
 template <typename T>
-hipError_t launch_inject_prep(const float* hidden, int rows, const int* index, int B, int K, float* xin, float* nrm,
-                              int nrm_ld, int* err, hipStream_t st);
+hipError_t launch_inject_prep(const float* hidden, int rows, const int* index, int B, int K, float eps, T* u,
+                              int* err, hipStream_t st);
 template <typename T>
 hipError_t launch_slots(const T* E, const T* pos, const T* z, const int* last, int B, int gamma, int d, int V,
-                        float* x, float* nrm, int nrm_ld, int* err, hipStream_t st);
+                        float* x, bf16* xb, float* nrm, int nrm_ld, int* err, hipStream_t st);
 template <typename T> hipError_t launch_draft(const DraftArgs& a, int B, hipStream_t st);
 
 }  // namespace evs

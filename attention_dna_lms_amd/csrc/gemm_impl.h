@@ -12,8 +12,11 @@
 // workgroups as well would need a cross-workgroup reduction whose device-scope
 // round trip costs more than it saves at these sizes.
 //
-// Prologue (A_NORM): RMSNorm of fp32 residual rows, from per-16-column sums of
-// squares the producing epilogue left behind. Epilogues: plain store (LM head),
+// Normed projections (A_NORM): the operand is the residual row as the producer
+// stored it in the storage type, and the row's RMSNorm scale 1/rms, formed in
+// the prologue from the per-16-column sums of squares the producer left
+// behind (fixed order), multiplies the reduced fp32 tile: norm(x) W^T =
+// rinv * (x W^T) with unit gain. Epilogues: plain store (LM head),
 // residual add + sums of squares (out / down projections), gated GELU (MLP up),
 // and the mixer epilogue (in-projection + FIR or IIR operator, or the KV append
 // of attention), which keeps each channel tile's q, k, v in one workgroup.
@@ -51,29 +54,9 @@ template <typename T> struct AFrag<T, A_ACT> {            // storage-type rows
   }
   __device__ __forceinline__ uint4 get(float) const { return v; }
 };
-template <> struct AFrag<bf16, A_NORM> {                  // fp32 rows, RMSNorm -> bf16
-  float4 lo, hi;
-  __device__ __forceinline__ void load(const GemmArgs& a, size_t m, int kofs) {
-    const float* xr = reinterpret_cast<const float*>(a.A) + act_off<8>((int)m, kofs, a.lda);
-    lo = *reinterpret_cast<const float4*>(xr);
-    hi = *reinterpret_cast<const float4*>(xr + 4);
-  }
-  __device__ __forceinline__ uint4 get(float r) const {
-    bf16x8 o;
-    o[0] = (bf16)(lo.x * r); o[1] = (bf16)(lo.y * r); o[2] = (bf16)(lo.z * r); o[3] = (bf16)(lo.w * r);
-    o[4] = (bf16)(hi.x * r); o[5] = (bf16)(hi.y * r); o[6] = (bf16)(hi.z * r); o[7] = (bf16)(hi.w * r);
-    return __builtin_bit_cast(uint4, o);
-  }
-};
-template <> struct AFrag<float, A_NORM> {                 // fp32 rows, RMSNorm -> fp32
-  float4 v;
-  __device__ __forceinline__ void load(const GemmArgs& a, size_t m, int kofs) {
-    v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.A) + act_off<4>((int)m, kofs, a.lda));
-  }
-  __device__ __forceinline__ uint4 get(float r) const {
-    return __builtin_bit_cast(uint4, make_float4(v.x * r, v.y * r, v.z * r, v.w * r));
-  }
-};
+// normed projections read the residual rows in the storage type (the norm's
+// scale goes onto the reduced tile), so their fragments are storage-type rows too
+template <typename T> struct AFrag<T, A_NORM> : AFrag<T, A_ACT> {};
 
 // each 16-lane row rotated by K lanes (DPP row_ror): a lane receives the value
 // of the lane K away in its own row
@@ -179,7 +162,18 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<float4*>(a.x + act_off<St<T>::E>(row0 + m, col0 + 4 * q, a.ldx)) =
             make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-      a.nrm_out[(size_t)(g * NT + nt) * a.nrm_ld + row0 + m] = ss;
+      a.nrm_out[(size_t)(row0 + m) * a.nrm_ld + g * NT + nt] = ss;
+      if constexpr (sizeof(T) == 2) {
+        // the same rows in bf16, two 8-element operand groups
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x8 b;
+#pragma unroll
+          for (int n = 0; n < 8; ++n) b[n] = (bf16)v[8 * h + n];
+          *reinterpret_cast<uint4*>(a.xb_out + act_off<8>(row0 + m, col0 + 8 * h, a.ldx)) =
+              __builtin_bit_cast(uint4, b);
+        }
+      }
     }
   } else if constexpr (EPI == E_GELU) {
     T* out = reinterpret_cast<T*>(a.out);
@@ -448,19 +442,17 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   // a weight step: one MFMA k-step, or two for FP8 weights (16 bytes per lane)
   constexpr int KPW = W8 ? 2 : 1;
   // k-steps per pipeline chunk: one chunk of NT weight fragments and MT
-  // activation fragments (8 registers each for fp32 rows feeding bf16, else 4)
-  // per step stays within ~64 registers, the two chunks in flight within ~128
-  // (pre-normed bf16 rows feeding the in-projection or gate/up of a
-  // multi-tile launch keep the chunk depth of the fused-norm path: the
-  // registers their smaller operands free go to the row tiles)
-  constexpr bool PRENORMED = AMODE == A_ACT && MT >= 2 && (EPI == E_MIXER || EPI == E_GELU);
-  constexpr int AREG = ((AMODE == A_NORM || PRENORMED) && sizeof(T) == 2) ? 2 : 1;
+  // activation fragments (4 registers each) per step stays within ~64
+  // registers, the two chunks in flight within ~128 (normed bf16 rows of a
+  // multi-tile launch keep the shallower chunks measured best for them: the
+  // registers go to the row tiles)
+  constexpr int AREG = (AMODE == A_NORM && MT >= 2 && sizeof(T) == 2) ? 2 : 1;
   // (measured at the 7B shapes: 4 steps for single-tile projections, 2 for
   // the gate/up pairs, the register bound for the in-projection triples)
   constexpr int PER = 16 / (NT + KPW * AREG * MT);
-  // (a single-tile gate/up over bf16 rows keeps 4 steps: one 16-byte
-  // activation load per step leaves the registers for them)
-  constexpr int CAP = NT == 1 ? 4 : NT == 2 ? (AMODE == A_ACT && MT == 1 ? 4 : 2) : 8;
+  // (a single-tile gate/up keeps 4 steps: one 16-byte activation load per
+  // step leaves the registers for them)
+  constexpr int CAP = NT == 1 ? 4 : NT == 2 ? (MT == 1 ? 4 : 2) : 8;
   constexpr int CH = CHO ? CHO : PER < 1 ? 1 : PER < CAP ? PER : CAP;
   extern __shared__ float lds[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -470,8 +462,35 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   const int g = blockIdx.x;
   const int row0 = blockIdx.y * a.rows_per_slice;
   const int rows = min(a.rows_per_slice, a.M - row0);
-  float* rinv = lds;                 // [MT*16]
+  float* rinv = lds;                 // [MT*16] the rows' RMSNorm scales (A_NORM)
   float* red = lds + MT * 16;        // reduction buffers, then the epilogue tile + scratch
+  // rinv[r] = 1 / sqrt(mean(x_r^2) + eps) from the row's n_part per-16-column
+  // sums of squares (contiguous, nrm_ld per row): per pass of 256, lane j of
+  // the row's 32 adds partials 8j .. 8j + 7 in a fixed tree (sum = v when the
+  // first pass was loaded early), then a fixed butterfly over the 32
+  constexpr int NP = AMODE == A_NORM ? (MT * 16 * 32 + C::WAVES * 64 - 1) / (C::WAVES * 64) : 1;
+  auto load8 = [&](float (&v)[8], int r, int i) __attribute__((always_inline)) {
+    const float* pr = a.nrm_part + (size_t)(row0 + min(r, rows - 1)) * a.nrm_ld + i;
+    if (r < rows && i + 8 <= a.n_part && (a.nrm_ld & 3) == 0) {   // two aligned 16-byte loads
+      const float4 lo = *reinterpret_cast<const float4*>(pr), hi = *reinterpret_cast<const float4*>(pr + 4);
+      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w; v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = (r < rows && i + q < a.n_part) ? pr[q] : 0.f;
+    }
+  };
+  auto row_scales = [&](int pss, float sum, int i_begin) __attribute__((always_inline)) {
+    const int idx = pss * C::WAVES * 64 + tid;
+    const int r = idx >> 5, j = idx & 31;
+    for (int i0 = i_begin; i0 < a.n_part; i0 += 256) {   // wide models only, when loaded early
+      float v[8];
+      load8(v, r, i0 + 8 * j);
+      sum += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    }
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 32);
+    if (j == 0 && r < MT * 16) rinv[r] = (r < rows) ? 1.0f / sqrtf(sum / a.fd + a.eps) : 0.f;
+  };
 
   const int kb = 0, ke = a.ksteps;
   const int per_wave = (ke - kb + C::WAVES - 1) / C::WAVES;
@@ -497,6 +516,10 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
 
   f32x4 acc[NT][MT];
   if constexpr (PART) {
+    if constexpr (AMODE == A_NORM) {
+#pragma unroll
+      for (int pss = 0; pss < NP; ++pss) row_scales(pss, 0.f, 0);
+    }
     // the eight k-range partials gemm_part_kernel formed (wave w takes range
     // w's chains, exactly what this kernel's wave w would have computed), or
     // the four pair sums gemm_pair_kernel formed (wave w < 4 takes ranges
@@ -541,7 +564,6 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float rr[MT];   // this lane's RMSNorm scale per row tile (A_NORM)
   auto compute = [&](uint4 (&w)[CH][NT], AFrag<T, AMODE> (&x)[CH][MT][KPW], int k0) {
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
@@ -552,7 +574,7 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
         for (int nt = 0; nt < NT; ++nt) fp8_to_bf16(w[u][nt], wl[nt], wh[nt]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const uint4 xa = x[u][mt][0].get(rr[mt]), xb = x[u][mt][KPW - 1].get(rr[mt]);
+          const uint4 xa = x[u][mt][0].get(1.f), xb = x[u][mt][KPW - 1].get(1.f);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
             acc[nt][mt] = mma_frag(wl[nt], xa, acc[nt][mt], T());
@@ -562,7 +584,7 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
       } else {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const uint4 xv = x[u][mt][0].get(rr[mt]);
+          const uint4 xv = x[u][mt][0].get(1.f);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) acc[nt][mt] = mma_frag(w[u][nt], xv, acc[nt][mt], T());
         }
@@ -575,7 +597,6 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   // then does the norm prologue wait (for its own loads alone), so the
   // weight stream starts at once and two chunks are in flight from the start.
   // (many-row launches skip the early load: its registers would spill)
-  constexpr int NP = AMODE == A_NORM ? (MT * 16 * 32 + C::WAVES * 64 - 1) / (C::WAVES * 64) : 1;
   constexpr bool PRE = AMODE == A_NORM && MT <= 2;
   float nv[PRE ? NP : 1][8];
   const bool nrm_pre = PRE && a.n_part <= 256;
@@ -583,11 +604,7 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int pss = 0; pss < NP; ++pss) {
       const int idx = pss * C::WAVES * 64 + tid, r = idx >> 5, j = idx & 31;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int i = j + 32 * q;
-        nv[pss][q] = (nrm_pre && r < rows && i < a.n_part) ? a.nrm_part[(size_t)i * a.nrm_ld + row0 + r] : 0.f;
-      }
+      load8(nv[pss], nrm_pre ? r : rows, 8 * j);
     }
   }
   issue_x(x0, wk0);
@@ -596,35 +613,16 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   issue_w(w1, wk0 + CH);
 
   if constexpr (AMODE == A_NORM) {
-    // rinv[r] = 1 / sqrt(mean(x_r^2) + eps): 32 lanes per row each add 8
-    // partials (per pass of 256 partials), then a fixed butterfly over the 32.
+    // (the scales are read from LDS by the epilogue tile's formation, after
+    // the reduction's barriers)
 #pragma unroll
     for (int pss = 0; pss < NP; ++pss) {
-      const int idx = pss * C::WAVES * 64 + tid;
-      const int r = idx >> 5, j = idx & 31;
       float sum = 0.f;
       if constexpr (PRE)
         sum = ((nv[pss][0] + nv[pss][1]) + (nv[pss][2] + nv[pss][3])) +
               ((nv[pss][4] + nv[pss][5]) + (nv[pss][6] + nv[pss][7]));
-      for (int i0 = nrm_pre ? a.n_part : 0; i0 < a.n_part; i0 += 256) {   // wide models only
-        float v[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int i = i0 + j + 32 * q;
-          v[q] = (r < rows && i < a.n_part) ? a.nrm_part[(size_t)i * a.nrm_ld + row0 + r] : 0.f;
-        }
-        sum += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-      }
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 32);
-      if (j == 0 && r < MT * 16) rinv[r] = (r < rows) ? 1.0f / sqrtf(sum / a.fd + a.eps) : 0.f;
+      row_scales(pss, sum, nrm_pre ? a.n_part : 0);
     }
-    __syncthreads();
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) rr[mt] = rinv[min(mt * 16 + rl, rows - 1)];
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) rr[mt] = 1.f;
   }
 
   // chunk pipeline: chunks c and c + 1 are in flight while chunk c computes;
@@ -685,7 +683,9 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
       const int ntmt = e >> 8, l = (e >> 2) & 63, i = e & 3;
       const int nt = ntmt / MT, mt = ntmt % MT;
       const float sc = W8 ? a.wscale[(g * NT + nt) * 16 + 4 * (l >> 4) + i] : 1.f;
-      ep[((nt * MT * 16 + mt * 16 + (l & 15)) * 16) + 4 * (l >> 4) + i] = W8 ? v * sc : v;
+      const float vs = W8 ? v * sc : v;
+      ep[((nt * MT * 16 + mt * 16 + (l & 15)) * 16) + 4 * (l >> 4) + i] =
+          AMODE == A_NORM ? vs * rinv[mt * 16 + (l & 15)] : vs;
     }
     __syncthreads();
   } else {
@@ -735,9 +735,11 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
         f32x4 sc = f32x4{1.f, 1.f, 1.f, 1.f};
         if constexpr (W8) sc = *reinterpret_cast<const f32x4*>(a.wscale + (g * NT + nt) * 16 + 4 * (lane >> 4));
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+          const f32x4 vs = W8 ? acc[nt][mt] * sc : acc[nt][mt];
           *reinterpret_cast<f32x4*>(ep + ((nt * MT * 16 + mt * 16 + rl) * 16 + 4 * (lane >> 4))) =
-              W8 ? acc[nt][mt] * sc : acc[nt][mt];
+              AMODE == A_NORM ? vs * rinv[mt * 16 + rl] : vs;
+        }
       }
     }
     __syncthreads();
@@ -746,7 +748,7 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
 }
 
 // ------------------------------------------------------------ split K
-// Multi-tile launches (bf16 rows already normed, read as is) in two kernels.
+// Multi-tile launches (bf16 rows) in two kernels.
 // gemm_part_kernel: one workgroup per (eight column groups, one of the eight
 // k-ranges gemm_kernel gives its waves, row slice); wave w takes group 8c + w
 // and forms, for every row tile, exactly the MFMA chain gemm_kernel's wave r
@@ -1015,10 +1017,11 @@ static hipError_t launch_gemm_split_mt(int NT, int epi, const GemmArgs& a, int s
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (NT == 3 && epi == E_MIXER) gemm_kernel<T, MT, 3, A_ACT, E_MIXER, 8, 0, 1, false, true><<<grid, block, lds, st>>>(a);
-    else if (NT == 2 && epi == E_GELU) gemm_kernel<T, MT, 2, A_ACT, E_GELU, 8, 0, 1, false, true><<<grid, block, lds, st>>>(a);
+    // (the normed projections take their rows' RMSNorm scales in the reduction kernel)
+    if (NT == 3 && epi == E_MIXER) gemm_kernel<T, MT, 3, A_NORM, E_MIXER, 8, 0, 1, false, true><<<grid, block, lds, st>>>(a);
+    else if (NT == 2 && epi == E_GELU) gemm_kernel<T, MT, 2, A_NORM, E_GELU, 8, 0, 1, false, true><<<grid, block, lds, st>>>(a);
     else if (NT == 1 && epi == E_RESID) gemm_kernel<T, MT, 1, A_ACT, E_RESID, 8, 0, 1, false, true><<<grid, block, lds, st>>>(a);
-    else if (NT == 1 && epi == E_STORE) gemm_kernel<T, MT, 1, A_ACT, E_STORE, 8, 0, 1, false, true><<<grid, block, lds, st>>>(a);
+    else if (NT == 1 && epi == E_STORE) gemm_kernel<T, MT, 1, A_NORM, E_STORE, 8, 0, 1, false, true><<<grid, block, lds, st>>>(a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
   }
@@ -1054,18 +1057,9 @@ static hipError_t launch_gemm_mt(int NT, int amode, int epi, const GemmArgs& a, 
     gemm_kernel<T, MT, 2, A_NORM, E_GELU><<<grid, block, lds, st>>>(a);
   else if (NT == 1 && amode == A_NORM && epi == E_STORE)
     gemm_kernel<T, MT, 1, A_NORM, E_STORE><<<grid, block, lds, st>>>(a);
-  else if constexpr (sizeof(T) == 2) {
-    // bf16 launches of the normed projections may take rows the norm kernel
-    // already formed (bf16(x * rinv), the same operands)
-    if (NT == 3 && amode == A_ACT && epi == E_MIXER)
-      gemm_kernel<T, MT, 3, A_ACT, E_MIXER><<<grid, block, lds, st>>>(a);
-    else if (NT == 2 && amode == A_ACT && epi == E_GELU)
-      gemm_kernel<T, MT, 2, A_ACT, E_GELU><<<grid, block, lds, st>>>(a);
-    else if (NT == 1 && amode == A_ACT && epi == E_STORE)
-      gemm_kernel<T, MT, 1, A_ACT, E_STORE><<<grid, block, lds, st>>>(a);
-    else
-      return hipErrorInvalidValue;
-  } else
+  else if (NT == 1 && amode == A_ACT && epi == E_STORE)     // rows normalised by their producer
+    gemm_kernel<T, MT, 1, A_ACT, E_STORE><<<grid, block, lds, st>>>(a);
+  else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -1082,10 +1076,6 @@ static hipError_t launch_gemm_w8_mt(int NT, int amode, int epi, const GemmArgs& 
     // one row tile: one-step chunks within 128 VGPRs, so two workgroups share a CU
     if constexpr (MT == 1) gemm_kernel<bf16, MT, 2, A_NORM, E_GELU, 8, 1, 4, true><<<grid, block, lds, st>>>(a);
     else gemm_kernel<bf16, MT, 2, A_NORM, E_GELU, 8, 0, 1, true><<<grid, block, lds, st>>>(a);
-  } else if (NT == 2 && amode == A_ACT && epi == E_GELU) {
-    // one row tile over pre-normed bf16 rows (the same operands)
-    if constexpr (MT == 1) gemm_kernel<bf16, 1, 2, A_ACT, E_GELU, 8, 1, 4, true><<<grid, block, lds, st>>>(a);
-    else return hipErrorInvalidValue;
   } else
     return hipErrorInvalidValue;
   return hipGetLastError();

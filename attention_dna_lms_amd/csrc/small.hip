@@ -6,14 +6,43 @@
 
 namespace evs {
 
-// ---------------------------------------------------------------- embedding
-// x[m, :] = E[tok[m], :] in fp32, plus the per-16-column sums of squares the
-// first RMSNorm reads. One thread per (row, 16-column tile). Also flags a
-// block that would run past the context capacity.
+// One residual row segment of 16 columns (row m, columns 16 tile ..): the fp32
+// values into the forward's activation layout, their sum of squares (in column
+// order) into the norm partials ([row][tile], nrm_ld partials per row), and for bf16 models the values in bf16, the
+// operand of the normed projections.
 template <typename T>
-__global__ void embed_kernel(const int* __restrict__ tokens, const T* __restrict__ E, float* x, float* nrm,
-                             int nrm_ld, int M, int d, int V, int P, int seq0, const int* t, int max_ctx,
-                             int* err) {
+__device__ __forceinline__ void store_row16(const float (&v)[16], float* x, bf16* xb, float* nrm, int nrm_ld, int m,
+                                            int tile, int K) {
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float* xr = x + act_off<St<T>::E>(m, tile * 16 + 4 * q, K);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      xr[n] = v[4 * q + n];
+      ss = fmaf(v[4 * q + n], v[4 * q + n], ss);
+    }
+  }
+  nrm[(size_t)m * nrm_ld + tile] = ss;   // row-major: a row's partials are contiguous
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 b;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) b[n] = (bf16)v[8 * h + n];
+      *reinterpret_cast<uint4*>(xb + act_off<8>(m, tile * 16 + 8 * h, K)) = __builtin_bit_cast(uint4, b);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- embedding
+// x[m, :] = E[tok[m], :] in fp32 (and bf16 for bf16 models), plus the
+// per-16-column sums of squares the first RMSNorm reads. One thread per (row,
+// 16-column tile). Also flags a block that would run past the context capacity.
+template <typename T>
+__global__ void embed_kernel(const int* __restrict__ tokens, const T* __restrict__ E, float* x, bf16* xb,
+                             float* nrm, int nrm_ld, int M, int d, int V, int P, int seq0, const int* t,
+                             int max_ctx, int* err) {
   const int ntile = d / 16;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= M * ntile) return;
@@ -25,84 +54,24 @@ __global__ void embed_kernel(const int* __restrict__ tokens, const T* __restrict
   }
   if (tile == 0 && m % P == 0 && t[seq0 + m / P] + P > max_ctx) atomicOr(err, 2);
   const T* e = E + (size_t)tok * d + tile * 16;
-  float ss = 0.f;
+  float v[16];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float* xr = x + act_off<St<T>::E>(m, tile * 16 + 4 * q, d);   // the forward's activation layout
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const float v = to_f(e[4 * q + n]);
-      xr[n] = v;
-      ss = fmaf(v, v, ss);
-    }
-  }
-  nrm[(size_t)tile * nrm_ld + m] = ss;
+  for (int n = 0; n < 16; ++n) v[n] = to_f(e[n]);
+  store_row16<T>(v, x, xb, nrm, nrm_ld, m, tile, d);
 }
 
 template <typename T>
-hipError_t launch_embed(const int* tokens, const T* E, float* x, float* nrm, int nrm_ld, int M, int d, int V,
-                        int P, int seq0, const int* t, int max_ctx, int* err, hipStream_t st) {
+hipError_t launch_embed(const int* tokens, const T* E, float* x, bf16* xb, float* nrm, int nrm_ld, int M, int d,
+                        int V, int P, int seq0, const int* t, int max_ctx, int* err, hipStream_t st) {
   const int n = M * (d / 16);
-  embed_kernel<T><<<(n + 255) / 256, 256, 0, st>>>(tokens, E, x, nrm, nrm_ld, M, d, V, P, seq0, t, max_ctx, err);
+  embed_kernel<T><<<(n + 255) / 256, 256, 0, st>>>(tokens, E, x, xb, nrm, nrm_ld, M, d, V, P, seq0, t, max_ctx,
+                                                   err);
   return hipGetLastError();
 }
-template hipError_t launch_embed<bf16>(const int*, const bf16*, float*, float*, int, int, int, int, int, int,
+template hipError_t launch_embed<bf16>(const int*, const bf16*, float*, bf16*, float*, int, int, int, int, int, int,
                                        const int*, int, int*, hipStream_t);
-template hipError_t launch_embed<float>(const int*, const float*, float*, float*, int, int, int, int, int, int,
-                                        const int*, int, int*, hipStream_t);
-
-// ---------------------------------------------------------------- norm rows
-// RMSNorm of fp32 residual rows into bf16 rows in the operand-order layout
-// (bf16 models): u = bf16(x * rinv), with rinv formed from the
-// per-16-column sums of squares exactly as the normed GEMM prologue forms it
-// (32 lanes per row, each adding its partials j + 32q, q < 8, in a fixed tree
-// per 256 partials, then a butterfly over the 32; 1 / sqrt(sum / K + eps)), so
-// u holds, bit for bit, the operands that prologue builds in registers.
-// Workgroup (row, 2048-column chunk); each thread converts one run of 8
-// columns. The run is loaded first, so its latency overlaps the scale's (each
-// workgroup of a row forms the same scale from the same partials).
-__global__ void __launch_bounds__(256) norm_rows_kernel(const float* __restrict__ x, const float* __restrict__ nrm,
-                                                        int n_part, int nrm_ld, float fd, float eps, int K,
-                                                        bf16* __restrict__ u) {
-  __shared__ float rinv_s;
-  const int m = blockIdx.x, tid = threadIdx.x;
-  const int c = (blockIdx.y * 256 + tid) * 8;
-  const bool live = c < K;
-  const size_t o = act_off<8>(m, live ? c : 0, K);
-  const float4 lo = *reinterpret_cast<const float4*>(x + o);
-  const float4 hi = *reinterpret_cast<const float4*>(x + o + 4);
-  if (tid < 32) {
-    const int j = tid;
-    float sum = 0.f;
-    for (int i0 = 0; i0 < n_part; i0 += 256) {
-      float v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int i = i0 + j + 32 * q;
-        v[q] = i < n_part ? nrm[(size_t)i * nrm_ld + m] : 0.f;
-      }
-      sum += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-    }
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 32);
-    if (j == 0) rinv_s = 1.0f / sqrtf(sum / fd + eps);
-  }
-  __syncthreads();
-  const float r = rinv_s;
-  if (live) {
-    bf16x8 b;
-    b[0] = (bf16)(lo.x * r); b[1] = (bf16)(lo.y * r); b[2] = (bf16)(lo.z * r); b[3] = (bf16)(lo.w * r);
-    b[4] = (bf16)(hi.x * r); b[5] = (bf16)(hi.y * r); b[6] = (bf16)(hi.z * r); b[7] = (bf16)(hi.w * r);
-    *reinterpret_cast<uint4*>(u + o) = __builtin_bit_cast(uint4, b);
-  }
-}
-
-hipError_t launch_norm_rows(const float* x, const float* nrm, int n_part, int nrm_ld, float fd, float eps, int M,
-                            int K, bf16* u, hipStream_t st) {
-  if (M <= 0) return hipSuccess;
-  norm_rows_kernel<<<dim3(M, (K + 2047) / 2048), 256, 0, st>>>(x, nrm, n_part, nrm_ld, fd, eps, K, u);
-  return hipGetLastError();
-}
+template hipError_t launch_embed<float>(const int*, const float*, float*, bf16*, float*, int, int, int, int, int,
+                                        int, const int*, int, int*, hipStream_t);
 
 // ---------------------------------------------------------------- commit
 // Slice each sequence's state to its accepted boundary: the committed length
@@ -770,55 +739,63 @@ hipError_t launch_export_rows(const float* x, float* dst, int M, int d, hipStrea
 template hipError_t launch_export_rows<bf16>(const float*, float*, int, int, hipStream_t);
 template hipError_t launch_export_rows<float>(const float*, float*, int, int, hipStream_t);
 
-// The injected rows: sequence b's hidden row hidden[b, index[b], :] into the
-// operand-order layout the normed GEMM reads, with its per-16-column sums of
-// squares (same order as the embedding's). Indices out of range are clamped
-// and flagged.
+// The injected rows, normalised: sequence b's hidden row h = hidden[b,
+// index[b], :] as u = h / sqrt(mean(h^2) + eps) in the storage type (the
+// operand of the injection product), in the operand-order layout. One
+// workgroup per row sees the whole row, so the scale is applied before the
+// rounding and u does not depend on the row's overall scale. The sum of
+// squares runs per 16-column tile (column order), then over the tiles in
+// order. Indices out of range are clamped and flagged.
 template <typename T>
-__global__ void inject_prep_kernel(const float* __restrict__ hidden, int rows, const int* __restrict__ index,
-                                   int B, int K, float* xin, float* nrm, int nrm_ld, int* err) {
-  const int ntile = K / 16;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= B * ntile) return;
-  const int b = idx / ntile, tile = idx % ntile;
+__global__ void __launch_bounds__(256) inject_prep_kernel(const float* __restrict__ hidden, int rows,
+                                                          const int* __restrict__ index, int K, float eps, T* u,
+                                                          int* err) {
+  __shared__ float tile_ss[1024];
+  __shared__ float rinv_s;
+  const int b = blockIdx.x, ntile = K / 16;
   int r = index ? index[b] : 0;
   if (r < 0 || r >= rows) {
-    if (tile == 0) atomicOr(err, 16);
+    if (threadIdx.x == 0) atomicOr(err, 16);
     r = r < 0 ? 0 : rows - 1;
   }
-  const float* src = hidden + ((size_t)b * rows + r) * K + tile * 16;
-  float ss = 0.f;
+  const float* src = hidden + ((size_t)b * rows + r) * K;
+  for (int tile = threadIdx.x; tile < ntile; tile += blockDim.x) {
+    float ss = 0.f;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float* xr = xin + act_off<St<T>::E>(b, tile * 16 + 4 * q, K);
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const float v = src[4 * q + n];
-      xr[n] = v;
-      ss = fmaf(v, v, ss);
-    }
+    for (int n = 0; n < 16; ++n) ss = fmaf(src[tile * 16 + n], src[tile * 16 + n], ss);
+    tile_ss[tile] = ss;
   }
-  nrm[(size_t)tile * nrm_ld + b] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float ss = 0.f;
+    for (int tile = 0; tile < ntile; ++tile) ss += tile_ss[tile];
+    rinv_s = 1.0f / sqrtf(ss / (float)K + eps);
+  }
+  __syncthreads();
+  const float rv = rinv_s;
+  for (int tile = threadIdx.x; tile < ntile; tile += blockDim.x) {
+#pragma unroll
+    for (int n = 0; n < 16; ++n) u[act_off<St<T>::E>(b, tile * 16 + n, K)] = from_f<T>(src[tile * 16 + n] * rv);
+  }
 }
 
 template <typename T>
-hipError_t launch_inject_prep(const float* hidden, int rows, const int* index, int B, int K, float* xin, float* nrm,
-                              int nrm_ld, int* err, hipStream_t st) {
-  const int n = B * (K / 16);
-  inject_prep_kernel<T><<<(n + 255) / 256, 256, 0, st>>>(hidden, rows, index, B, K, xin, nrm, nrm_ld, err);
+hipError_t launch_inject_prep(const float* hidden, int rows, const int* index, int B, int K, float eps, T* u,
+                              int* err, hipStream_t st) {
+  if (K % 16 || K / 16 > 1024) return hipErrorInvalidValue;
+  inject_prep_kernel<T><<<B, 256, 0, st>>>(hidden, rows, index, K, eps, u, err);
   return hipGetLastError();
 }
-template hipError_t launch_inject_prep<bf16>(const float*, int, const int*, int, int, float*, float*, int, int*,
-                                             hipStream_t);
-template hipError_t launch_inject_prep<float>(const float*, int, const int*, int, int, float*, float*, int, int*,
+template hipError_t launch_inject_prep<bf16>(const float*, int, const int*, int, int, float, bf16*, int*, hipStream_t);
+template hipError_t launch_inject_prep<float>(const float*, int, const int*, int, int, float, float*, int*,
                                               hipStream_t);
 
 // The slot rows: x[b * gamma + i] = (embed[last_b] + pos[i]) + z[b] in fp32,
 // in the forward's layout, with their per-16-column sums of squares.
 template <typename T>
 __global__ void slots_kernel(const T* __restrict__ E, const T* __restrict__ pos, const T* __restrict__ z,
-                             const int* __restrict__ last, int B, int gamma, int d, int V, float* x, float* nrm,
-                             int nrm_ld, int* err) {
+                             const int* __restrict__ last, int B, int gamma, int d, int V, float* x, bf16* xb,
+                             float* nrm, int nrm_ld, int* err) {
   const int ntile = d / 16;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= B * gamma * ntile) return;
@@ -831,32 +808,23 @@ __global__ void slots_kernel(const T* __restrict__ E, const T* __restrict__ pos,
   const T* e = E + (size_t)tok * d + tile * 16;
   const T* p = pos + (size_t)i * d + tile * 16;
   const T* zz = z + (size_t)b * d + tile * 16;
-  float ss = 0.f;
+  float v[16];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float* xr = x + act_off<St<T>::E>(m, tile * 16 + 4 * q, d);
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int c = 4 * q + n;
-      const float v = (to_f(e[c]) + to_f(p[c])) + to_f(zz[c]);
-      xr[n] = v;
-      ss = fmaf(v, v, ss);
-    }
-  }
-  nrm[(size_t)tile * nrm_ld + m] = ss;
+  for (int c = 0; c < 16; ++c) v[c] = (to_f(e[c]) + to_f(p[c])) + to_f(zz[c]);
+  store_row16<T>(v, x, xb, nrm, nrm_ld, m, tile, d);
 }
 
 template <typename T>
 hipError_t launch_slots(const T* E, const T* pos, const T* z, const int* last, int B, int gamma, int d, int V,
-                        float* x, float* nrm, int nrm_ld, int* err, hipStream_t st) {
+                        float* x, bf16* xb, float* nrm, int nrm_ld, int* err, hipStream_t st) {
   const int n = B * gamma * (d / 16);
-  slots_kernel<T><<<(n + 255) / 256, 256, 0, st>>>(E, pos, z, last, B, gamma, d, V, x, nrm, nrm_ld, err);
+  slots_kernel<T><<<(n + 255) / 256, 256, 0, st>>>(E, pos, z, last, B, gamma, d, V, x, xb, nrm, nrm_ld, err);
   return hipGetLastError();
 }
 template hipError_t launch_slots<bf16>(const bf16*, const bf16*, const bf16*, const int*, int, int, int, int, float*,
-                                       float*, int, int*, hipStream_t);
+                                       bf16*, float*, int, int*, hipStream_t);
 template hipError_t launch_slots<float>(const float*, const float*, const float*, const int*, int, int, int, int,
-                                        float*, float*, int, int*, hipStream_t);
+                                        float*, bf16*, float*, int, int*, hipStream_t);
 
 // Markov head and draws: one wave per sequence, the slots one after another
 // (each adds the Markov row of the previous draft). Per slot: l' = fp32(l) +

@@ -119,6 +119,37 @@ def family(r, split_gemm=False):
     return name[:40]
 
 
+def projection_roles(sel, n_layers=32):
+    """The role of each GEMM launch of the 7B-shaped stack's rounds, in
+    dispatch order: per layer the mixer in-projection (by mixer kind, reading
+    R2's layer order), its out-projection, gate/up and down; then the LM head."""
+    import evs_synth as es
+    kinds = es.configs.hybrid_layer_kinds(n_layers)
+    names = {"fir_s": "in-proj FIR-7", "fir_m": "in-proj FIR-128", "iir": "in-proj IIR-16", "attn": "in-proj attention"}
+    seq = []
+    for k in kinds:
+        seq += [names[k], "out-proj", "gate/up", "down"]
+    seq.append("LM head")
+    roles, i = [], 0
+    for r in sel:
+        if "gemm_kernel" in r["Kernel_Name"]:
+            roles.append(seq[i % len(seq)])
+            i += 1
+        else:
+            roles.append(None)
+    return roles
+
+
+# algorithmic bytes of one launch of each projection of the 7B-shaped stack at
+# 13 rows: the weights, the input rows (fp32 for the normed projections) and
+# the output rows (fp32 read + write for the residual epilogues)
+def projection_bytes(role, M=13, d=4096, dff=11008, V=512):
+    if role.startswith("in-proj"):
+        return 3 * d * d * 2 + M * d * 4 + M * 3 * d * 2
+    return {"out-proj": d * d * 2 + M * d * 2 + M * d * 8, "gate/up": 2 * dff * d * 2 + M * d * 2 + M * dff * 2,
+            "down": d * dff * 2 + M * dff * 2 + M * d * 8, "LM head": V * d * 2 + M * d * 4 + M * V * 2}[role]
+
+
 def summarize_trace(path, steps, warmup):
     import collections
     import csv
@@ -139,6 +170,19 @@ def summarize_trace(path, steps, warmup):
         for k, v in sorted(g.items(), key=lambda kv: -sum(kv[1])):
             print(f"| {k} | {len(v) / steps:.0f} | {sum(v) / len(v):.2f} | {sum(v) / steps:.1f} |")
         print()
+    # the GEMM launches by projection, with their achieved algorithmic GB/s
+    g = collections.defaultdict(list)
+    for r, role in zip(sel, projection_roles(sel)):
+        if role:
+            g[role].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| projection | launches/round | avg us | us/round | algorithmic MB/launch | GB/s | of 8 TB/s |\n"
+          "|---|---|---|---|---|---|---|")
+    for k, v in sorted(g.items(), key=lambda kv: -sum(kv[1])):
+        us = sum(v) / len(v)
+        mb = projection_bytes(k) / 1e6
+        print(f"| {k} | {len(v) / steps:.0f} | {us:.2f} | {sum(v) / steps:.1f} | {mb:.1f} | {mb * 1e3 / us:.0f} | "
+              f"{mb * 1e3 / us / 8000:.3f} |")
+    print()
 
 
 def summarize_drafter_trace(path, calls=50):

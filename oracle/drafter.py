@@ -19,7 +19,7 @@ The pages name these parts but give none of their formulas; the readings:
     drafter's (frozen) token embedding and pos its position embeddings;
   * trunk: the drafter's blocks (one pre-norm causal attention + gated MLP
     layer) over the gamma slots from an empty state, then the final RMSNorm
-    and the untied head: l_i = st(st(rmsnorm(x_i)) W_o^T). Causal attention makes
+    and the untied head: l_i = st(norm(x_i) W_o^T). Causal attention makes
     slot i independent of the slots after it (the exact causal prefix);
   * Markov head: l'_i = fp32(l_i) + T[d_{i-1}], T a full [V, V] fp32 matrix,
     d_{-1} = x_last, so the drafts are drawn one after another;
@@ -65,7 +65,9 @@ class Drafter:
         self.W = self.lm.W
 
     def prefix(self, hidden_row):
-        """z = st(st(rmsnorm(h)) W_inj^T) for one exported target row h."""
+        """z = st(st(rmsnorm(h)) W_inj^T) for one exported target row h: the row
+        is normalised before it is rounded to the storage type, so z does not
+        depend on the row's overall scale."""
         h = np.asarray(hidden_row, dtype=np.float64)
         return self.lm.st(self.lm.st(rmsnorm(h, self.lm.eps)) @ self.W["inject"].T)
 

@@ -7,9 +7,11 @@ recurrent states that depend on the whole accepted prefix, and append-only
 attention KV caches. The pages give no layer formulas; the readings used here:
 
   * model   = embedding -> pre-norm residual blocks -> RMSNorm -> untied LM head;
-  * norm    = RMSNorm, unit gain, eps from the config; its output is rounded
-              to the storage type as the operand of the product it feeds
-              (the mixer, the MLP and the LM head alike);
+  * norm    = RMSNorm, unit gain, eps from the config, feeding a product:
+              norm(x) W^T = r * (x W^T) with r = 1 / sqrt(mean(x^2) + eps);
+              the product's operand is the residual row rounded to the
+              storage type and r scales the product's sum (the mixer, the MLP
+              and the LM head alike);
   * mixer   = z = u W_in^T split [q | k | v]; h = k * v; y = op(h); o = q * y;
               x += o W_out^T, where op is
       FIR   : y_t[c] = sum_{j<L} taps[c, j] * h_{t-j}[c]   (h before position 0 is 0);
@@ -49,7 +51,7 @@ from typing import Dict
 
 import numpy as np
 
-from .numerics import gelu, rmsnorm, store
+from .numerics import gelu, rms_scale, store
 
 
 def _f64(t):
@@ -168,10 +170,15 @@ class HybridLM:
         other.acc = accumulate
         return other
 
+    def normed_mm(self, X, W):
+        """norm(X) W^T for residual rows X [P, d]: the rows rounded to the
+        storage type as the operand, each row's RMSNorm scale on the sum."""
+        X = np.asarray(X, dtype=np.float64)
+        return rms_scale(X, self.eps) * self.mm(self.st(X), W)
+
     def head(self, X):
-        """Logits of residual rows X [P, d]: final RMSNorm (rounded to the
-        storage type as the head's operand) and the LM head."""
-        return self.st(self.mm(self.st(rmsnorm(X, self.eps)), self.W["lm_head"]))
+        """Logits of residual rows X [P, d]: final RMSNorm and the LM head."""
+        return self.st(self.normed_mm(X, self.W["lm_head"]))
 
     # ------------------------------------------------------------------ state
     def empty_state(self) -> SeqState:
@@ -208,19 +215,21 @@ class HybridLM:
         for i, b in enumerate(self.cfg.blocks):
             x = self._block_step(i, b, s, x)
         s.t += 1
-        logits = self.st(self.W["lm_head"] @ self.st(rmsnorm(x, self.eps)))
+        logits = self.st(rms_scale(x, self.eps)[0] * (self.W["lm_head"] @ self.st(x)))
         return logits, s
 
     def _block_step(self, i, b, s: SeqState, x):
         d = self.d
-        u = self.st(rmsnorm(x, self.eps))
+        # norm(x) W^T: the row in the storage type as the operand, its RMSNorm
+        # scale r on the sum
+        r, u = rms_scale(x, self.eps)[0], self.st(x)
         if b.kind == "mlp":
             wgu = self.W[f"b{i}.w_gu"]
-            g = self.st(wgu[: b.d_ff] @ u)
-            up = self.st(wgu[b.d_ff:] @ u)
+            g = self.st(r * (wgu[: b.d_ff] @ u))
+            up = self.st(r * (wgu[b.d_ff:] @ u))
             m = self.st(gelu(g) * up)
             return x + self.st(self.W[f"b{i}.w_down"] @ m)
-        z = self.st(self.W[f"b{i}.w_in"] @ u)
+        z = self.st(r * (self.W[f"b{i}.w_in"] @ u))
         q, k, v = z[:d], z[d:2 * d], z[2 * d:]
         if b.kind == "fir":
             h = k * v
@@ -281,14 +290,13 @@ class HybridLM:
         """One residual block over P positions (rows of X) from committed
         ``state``; per-position state goes into ``pend``."""
         d, P = self.d, X.shape[0]
-        U = self.st(rmsnorm(X, self.eps))
         if b.kind == "mlp":
             wgu = self.W[f"b{i}.w_gu"]
-            G = self.st(self.mm(U, wgu[: b.d_ff]))
-            Up = self.st(self.mm(U, wgu[b.d_ff:]))
+            G = self.st(self.normed_mm(X, wgu[: b.d_ff]))
+            Up = self.st(self.normed_mm(X, wgu[b.d_ff:]))
             M = self.st(gelu(G) * Up)
             return X + self.st(self.mm(M, self.W[f"b{i}.w_down"]))
-        Z = self.st(self.mm(U, self.W[f"b{i}.w_in"]))
+        Z = self.st(self.normed_mm(X, self.W[f"b{i}.w_in"]))
         pend.z[i] = Z
         Q, K, V = Z[:, :d], Z[:, d:2 * d], Z[:, 2 * d:]
         if b.kind == "fir":

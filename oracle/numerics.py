@@ -6,6 +6,7 @@ Parity pins (tests/test_oracle_numerics.py):
   gelu       — against x * Phi(x) from scipy's normal CDF and the tabulated
                value Phi(1).
   rmsnorm    — unit root-mean-square output and scale invariance.
+  rms_scale  — the factor rmsnorm multiplies by (same pins).
 """
 from __future__ import annotations
 
@@ -42,3 +43,10 @@ def rmsnorm(x, eps: float):
     """RMSNorm with unit gain over the last axis: x / sqrt(mean(x^2) + eps)."""
     x = np.asarray(x, dtype=np.float64)
     return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def rms_scale(x, eps: float):
+    """The RMSNorm scale of each row (last axis): 1 / sqrt(mean(x^2) + eps),
+    keeping the last axis (length 1) so it broadcasts over the row."""
+    x = np.asarray(x, dtype=np.float64)
+    return 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)

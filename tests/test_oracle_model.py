@@ -294,18 +294,22 @@ def test_bf16_storage_points_are_bf16_values():
         assert np.array_equal(torch.from_numpy(k).to(torch.bfloat16).float().numpy(), k)
 
 
-def test_lm_head_reads_the_normed_row_rounded_to_bf16():
-    """Reading R3: the RMSNorm output is rounded to the storage type as the
-    operand of the product it feeds, the LM head included. Hand-worked: x =
-    [9, 1, 1, 1] has rms sqrt(21) = 4.5826, so u = [1.96396, 0.21822 x 3],
-    which bf16 holds as [1.9609375, 0.2177734375 x 3] (steps 2^-7 and 2^-10).
-    A head row of ones sums them to 2.6142578125 -> bf16 2.609375 (step 2^-6);
-    summing the unrounded u (2.61861) would give 2.625 instead."""
+def test_normed_product_reads_the_bf16_row_and_scales_the_sum():
+    """Reading R3: norm(x) W^T = r (st(x) W^T) with r = 1 / sqrt(mean(x^2) +
+    eps): the residual row rounded to bf16 is the operand and r scales the sum,
+    in the LM head as in the blocks. Hand-worked: x = [1, 1 + 2^-8, 1, 2]
+    rounds to [1, 1, 1, 2] (1 + 2^-8 is the tie between 1 and 1 + 2^-7; ties
+    go to the even one) and has r = 1 / sqrt(7.00783 / 4) = 0.75551. Head row
+    [1, -1, 0, 0]: r (1 - 1) = 0. Rounding x r first would give 0.75391 -
+    0.75781 = -2^-8 (0.75551 and 0.75846 lie 193.4 and 194.2 steps of 2^-8 up),
+    and no rounding at all -0.00295. Head row [0, 0, 0, 1]: st(2 r) =
+    st(1.51101) = 1.5078125 (step 2^-7)."""
     from evs_synth.configs import ModelConfig
-    cfg = ModelConfig("lm_head_pin", 4, 2, [], dtype="bf16")
-    w = {"embed": np.array([[9.0, 1, 1, 1], [1, 1, 1, 1]]), "lm_head": np.array([[1.0, 1, 1, 1], [1, 0, 0, 0]])}
+    cfg = ModelConfig("norm_pin", 4, 2, [], dtype="bf16")
+    w = {"embed": np.array([[1.0, 1 + 2.0 ** -8, 1, 2], [1, 1, 1, 1]]),
+         "lm_head": np.array([[1.0, -1, 0, 0], [0, 0, 0, 1]])}
     orc = HybridLM(cfg, w)
-    want = [2.609375, 1.9609375]
+    want = [0.0, 1.5078125]
     assert list(orc.block(orc.empty_state(), [0]).logits[0]) == want
     assert list(orc.step(orc.empty_state(), 0)[0]) == want
     assert list(HybridLM(cfg, w, accumulate="f32").block(orc.empty_state(), [0]).logits[0]) == want
