@@ -401,8 +401,9 @@ evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int 
 // s->export_block are also written out row-major.
 template <typename T>
 evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const int32_t* tokens, void* logits,
-                   hipStream_t st, float* export_dst = nullptr) {
+                   hipStream_t st, float* export_dst = nullptr, int export_m0 = 0, int export_n = -1) {
   const int d = m->desc.d_model, M = nseq * P;
+  if (export_n < 0) export_n = M;
   float* x = wp<float>(s, s->w_x);
   // the residual rows in the storage type: the operand of every normed
   // projection, written by the same producer as x and its norm partials
@@ -419,7 +420,8 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
     HIP_TRY(launch_embed<T>(tokens, reinterpret_cast<const T*>(m->base + m->embed), x, xb, nrm, d / 16, M, d,
                             m->desc.vocab, P, seq0, t, s->max_ctx, err, st));
   for (size_t i = 0; i < m->plan.size(); ++i) {
-    if (i > 0 && export_dst && (int)i - 1 == s->export_block) HIP_TRY(launch_export_rows<T>(x, export_dst, M, d, st));
+    if (i > 0 && export_dst && (int)i - 1 == s->export_block)
+      HIP_TRY(launch_export_rows<T>(x, export_dst, export_m0, export_n, d, st));
     const BlockPlan& p = m->plan[i];
     GemmArgs a{};
     if (p.d.kind == EVS_MLP) {
@@ -489,7 +491,8 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
     b.x = x; b.ldx = d; b.nrm_out = nrm; b.xb_out = xb;
     EVS_TRY(gemm_call<T>(m, s, p.w_out, A_ACT, E_RESID, wp<void>(s, s->w_o), d, nseq, P, b, st));
   }
-  if (export_dst && s->export_block == (int)m->plan.size() - 1) HIP_TRY(launch_export_rows<T>(x, export_dst, M, d, st));
+  if (export_dst && s->export_block == (int)m->plan.size() - 1)
+    HIP_TRY(launch_export_rows<T>(x, export_dst, export_m0, export_n, d, st));
   if (logits) {
     GemmArgs a{};
     a.N = m->desc.vocab; a.out = logits; a.ldo = m->desc.vocab;
@@ -502,9 +505,10 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
 }
 
 evs_status forward_any(evs_model* m, evs_state* s, int seq0, int nseq, int P, const int32_t* tokens, void* logits,
-                       hipStream_t st, float* export_dst = nullptr) {
-  if (storage_dtype(&m->desc) == EVS_BF16) return forward<bf16>(m, s, seq0, nseq, P, tokens, logits, st, export_dst);
-  return forward<float>(m, s, seq0, nseq, P, tokens, logits, st, export_dst);
+                       hipStream_t st, float* export_dst = nullptr, int export_m0 = 0, int export_n = -1) {
+  if (storage_dtype(&m->desc) == EVS_BF16)
+    return forward<bf16>(m, s, seq0, nseq, P, tokens, logits, st, export_dst, export_m0, export_n);
+  return forward<float>(m, s, seq0, nseq, P, tokens, logits, st, export_dst, export_m0, export_n);
 }
 
 // The drafter's pass (evs_draft): injected prefix, slot rows, the drafter's
@@ -532,6 +536,69 @@ evs_status draft_pass(evs_model* m, evs_state* s, int B, const float* hidden, in
   da.drafts = drafts; da.q = q; da.err = err;
   HIP_TRY(launch_draft<T>(da, B, st));
   return EVS_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------- generation
+namespace {
+
+struct GenLayout {
+  size_t cand = 0, drafts = 0, logits = 0, q = 0, n_acc = 0, next = 0, n_keep = 0, last = 0, idx = 0, emitted = 0,
+         dlogits = 0, total = 0;
+};
+
+evs_status gen_check(const evs_model* m, const evs_state* s, const evs_gen_params* p, const evs_draft_source* d) {
+  if (!m || !s || !p || s->m != m) return EVS_E_INVALID;
+  const int src = d ? d->source : EVS_DRAFT_NONE;
+  if (p->n_tokens < 1 || p->gamma < 0 || p->rounds_cap < 1) return EVS_E_INVALID;
+  if (p->gamma + 1 > s->max_block) return EVS_E_RANGE;
+  if ((long long)(p->gamma + 2) * m->desc.vocab > 15360) return EVS_E_UNSUPPORTED;   // the verifier's LDS rows
+  if (!p->greedy) {
+    if (!(p->temperature > 0.f && std::isfinite(p->temperature))) return EVS_E_INVALID;
+    if (!p->u_first_dev || !p->u_target_dev) return EVS_E_INVALID;
+  }
+  switch (src) {
+    case EVS_DRAFT_NONE:
+      if (p->gamma != 0) return EVS_E_INVALID;
+      break;
+    case EVS_DRAFT_TABLE:
+      if (p->gamma < 1 || !d->table_dev || d->table_len < 1) return EVS_E_INVALID;
+      break;
+    case EVS_DRAFT_MODEL: {
+      const evs_model* dm = d->drafter;
+      const evs_state* ds = d->drafter_state;
+      if (p->gamma < 1 || !dm || !ds || ds->m != dm || dm->desc.inject_dim != m->desc.d_model) return EVS_E_INVALID;
+      if (dm->desc.vocab != m->desc.vocab || !ds->wb) return EVS_E_INVALID;
+      if (p->gamma > dm->desc.max_slots || p->gamma > ds->max_block || ds->B < s->B) return EVS_E_RANGE;
+      if (s->export_block < 0 || !s->export_dst) return EVS_E_STATE;   // the drafter reads the exported rows
+      if (!p->greedy && !p->u_draft_dev) return EVS_E_INVALID;
+      break;
+    }
+    default: return EVS_E_INVALID;
+  }
+  return EVS_OK;
+}
+
+GenLayout gen_layout(const evs_model* m, const evs_state* s, const evs_gen_params* p, const evs_draft_source* d) {
+  GenLayout g;
+  const size_t B = s->B, P = p->gamma + 1, V = m->desc.vocab;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + std::max(bytes, (size_t)4)); return o; };
+  g.cand = take(B * P * 4);
+  g.drafts = take(B * std::max(p->gamma, 1) * 4);
+  g.logits = take(B * P * V * m->es);
+  g.q = take(B * p->gamma * V * 4);
+  g.n_acc = take(B * 4);
+  g.next = take(B * 4);
+  g.n_keep = take(B * 4);
+  g.last = take(B * 4);
+  g.idx = take(B * 4);
+  g.emitted = take(B * 4);
+  if (d && d->source == EVS_DRAFT_MODEL)
+    g.dlogits = take(B * p->gamma * (size_t)d->drafter->desc.vocab * d->drafter->es);
+  g.total = off;
+  return g;
 }
 
 }  // namespace
@@ -803,7 +870,10 @@ evs_status evs_prefill(evs_model* m, evs_state* s, const int32_t* tokens, const 
       const int P = std::min(chunk, n - a);
       const bool last = a + P == n;
       void* lg = (last && last_logits) ? wp<void>(s, s->w_logit) : nullptr;
-      EVS_TRY(forward_any(m, s, b, 1, P, tokens + offs[b] + a, lg, st));
+      // with the export on, the last chunk also writes the sequence's last
+      // prompt row to row b of the export buffer
+      float* ex = (last && s->export_block >= 0) ? s->export_dst + (size_t)b * m->desc.d_model : nullptr;
+      EVS_TRY(forward_any(m, s, b, 1, P, tokens + offs[b] + a, lg, st, ex, P - 1, 1));
       HIP_TRY(close_span(s));
       HIP_TRY(launch_commit(sp<int>(s, s->off_t) + b, sp<int>(s, s->off_ib) + b, sp<int>(s, s->off_is) + b,
                             nullptr, P, 1, P, sp<int>(s, s->off_err), st));
@@ -915,6 +985,81 @@ evs_status evs_draft(evs_model* m, evs_state* s, int32_t batch, const float* hid
                           logits, drafts, q, st);
   HIP_TRY(close_span(s));
   return r;
+}
+
+evs_status evs_generate_workspace_bytes(const evs_model* m, const evs_state* s, const evs_gen_params* p,
+                                        const evs_draft_source* d, size_t* bytes) {
+  if (!bytes) return EVS_E_INVALID;
+  EVS_TRY(gen_check(m, s, p, d));
+  *bytes = gen_layout(m, s, p, d).total;
+  return EVS_OK;
+}
+
+evs_status evs_generate(evs_model* m, evs_state* s, const void* last_logits, const evs_gen_params* p,
+                        const evs_draft_source* d, void* work, int32_t* ids, int32_t* stats, int32_t* n_rounds,
+                        void* stream) {
+  EVS_TRY(gen_check(m, s, p, d));
+  if (!last_logits || !work || !ids || !stats || !n_rounds || ((uintptr_t)work % ALIGN)) return EVS_E_INVALID;
+  if (s->pending || !s->wb) return EVS_E_STATE;
+  *n_rounds = 0;
+  const GenLayout L = gen_layout(m, s, p, d);
+  char* w = reinterpret_cast<char*>(work);
+  auto wi = [&](size_t off) { return reinterpret_cast<int32_t*>(w + off); };
+  int32_t *cand = wi(L.cand), *drafts = wi(L.drafts), *n_acc = wi(L.n_acc), *next = wi(L.next),
+          *n_keep = wi(L.n_keep), *last = wi(L.last), *idx = wi(L.idx), *emitted = wi(L.emitted);
+  void* logits = w + L.logits;
+  float* q = reinterpret_cast<float*>(w + L.q);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int B = s->B, g = p->gamma, P = g + 1, V = m->desc.vocab;
+  const int src = d ? d->source : EVS_DRAFT_NONE;
+  const int kind = storage_dtype(&m->desc) == EVS_BF16 ? EVS_TARGET_LOGITS_BF16 : EVS_TARGET_LOGITS_F32;
+  int32_t* err = sp<int>(s, s->off_err);
+  const float T = p->temperature;
+  // the first token, from the last prompt position's logits
+  EVS_TRY(evs_verify_sample(B, 0, V, last_logits, kind, nullptr, nullptr, p->greedy ? nullptr : p->u_first_dev, T,
+                            p->top_k, p->greedy, n_acc, next, nullptr, err, stream));
+  HIP_TRY(launch_gen_start(next, B, p->n_tokens, ids, last, idx, emitted, stats, st));
+  auto round = [&](int r) -> evs_status {
+    if (src == EVS_DRAFT_MODEL) {
+      // the exported rows: one per sequence after the prefill, the block's after a round
+      EVS_TRY(evs_draft(d->drafter, d->drafter_state, B, s->export_dst, r == 0 ? 1 : P, idx, last, g,
+                        p->greedy ? nullptr : p->u_draft_dev + (size_t)r * B * g, T, p->top_k, p->greedy,
+                        w + L.dlogits, drafts, p->greedy ? nullptr : q, stream));
+    }
+    const bool table = src == EVS_DRAFT_TABLE;
+    HIP_TRY(launch_gen_cand(last, emitted, B, g, table ? d->table_dev : nullptr, table ? d->table_len : 0,
+                            (table && d->replace_dev) ? d->replace_dev + (size_t)r * B * g : nullptr, drafts, cand,
+                            (table && !p->greedy) ? q : nullptr, V, st));
+    EVS_TRY(evs_block_verify(m, s, cand, g, logits, stream));
+    EVS_TRY(evs_verify_sample(B, g, V, logits, kind, (p->greedy || g == 0) ? nullptr : q, g > 0 ? drafts : nullptr,
+                              p->greedy ? nullptr : p->u_target_dev + (size_t)r * B * P, T, p->top_k, p->greedy,
+                              n_acc, next, nullptr, err, stream));
+    HIP_TRY(launch_gen_emit(drafts, g, n_acc, next, B, p->n_tokens, ids, emitted, n_keep, last, idx, stats, st));
+    return evs_rollback(s, n_keep, stream);
+  };
+  // Rounds go out in batches without a host read: the sequence furthest from
+  // n_tokens needs at least ceil(remaining / (gamma + 1)) more rounds, so a
+  // batch of that many never overshoots it; sequences that finish earlier
+  // keep nothing in the remaining rounds of the batch.
+  std::vector<int32_t> em(B);
+  int rounds = 0;
+  while (true) {
+    HIP_TRY(hipMemcpyAsync(em.data(), emitted, (size_t)B * 4, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    const int rem = p->n_tokens - *std::min_element(em.begin(), em.end());
+    if (rem <= 0) break;
+    if (rounds >= p->rounds_cap) {
+      *n_rounds = rounds;
+      return EVS_E_RANGE;
+    }
+    const int k = std::min((rem + g) / (g + 1), p->rounds_cap - rounds);
+    for (int i = 0; i < k; ++i) {
+      EVS_TRY(round(rounds));
+      ++rounds;
+    }
+  }
+  *n_rounds = rounds;
+  return EVS_OK;
 }
 
 evs_status evs_state_timing(evs_state* s, int32_t enable, int64_t context_hint) {

@@ -185,7 +185,14 @@ struct DraftArgs {
   float* q;              // [B, gamma, V] or null
   int* err;
 };
-template <typename T> hipError_t launch_export_rows(const float* x, float* dst, int M, int d, hipStream_t st);
+template <typename T> hipError_t launch_export_rows(const float* x, float* dst, int m0, int M, int d, hipStream_t st);
+// generation loop (gen.hip)
+hipError_t launch_gen_start(const int* next, int B, int n_tokens, int* ids, int* last, int* idx, int* emitted,
+                            int* stats, hipStream_t st);
+hipError_t launch_gen_cand(const int* last, const int* emitted, int B, int gamma, const int* table, int table_len,
+                           const int* replace, int* drafts, int* cand, float* q, int V, hipStream_t st);
+hipError_t launch_gen_emit(const int* drafts, int gamma, const int* n_acc, const int* next, int B, int n_tokens,
+                           int* ids, int* emitted, int* n_keep, int* last, int* idx, int* stats, hipStream_t st);
 template <typename T>
 hipError_t launch_inject_prep(const float* hidden, int rows, const int* index, int B, int K, float eps, T* u,
                               int* err, hipStream_t st);

@@ -721,23 +721,25 @@ hipError_t launch_verify(const VerifyArgs& a, int B, hipStream_t st) {
 // Hidden-state export: fp32 residual rows from the forward's operand-order
 // layout to row-major [M, d], four columns per thread (the layout keeps runs of
 // E >= 4 columns of a row contiguous).
+// (rows m0 .. m0 + M - 1 of x to rows 0 .. M - 1 of dst)
 template <int E>
-__global__ void export_rows_kernel(const float* __restrict__ x, float* __restrict__ dst, int M, int d) {
+__global__ void export_rows_kernel(const float* __restrict__ x, float* __restrict__ dst, int m0, int M, int d) {
   const int n4 = d >> 2;
   const long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x;
   if (idx >= (long long)M * n4) return;
   const int m = (int)(idx / n4), c = (int)(idx % n4) * 4;
-  *reinterpret_cast<float4*>(dst + (size_t)m * d + c) = *reinterpret_cast<const float4*>(x + act_off<E>(m, c, d));
+  *reinterpret_cast<float4*>(dst + (size_t)m * d + c) =
+      *reinterpret_cast<const float4*>(x + act_off<E>(m0 + m, c, d));
 }
 
 template <typename T>
-hipError_t launch_export_rows(const float* x, float* dst, int M, int d, hipStream_t st) {
+hipError_t launch_export_rows(const float* x, float* dst, int m0, int M, int d, hipStream_t st) {
   const long long n = (long long)M * (d / 4);
-  export_rows_kernel<St<T>::E><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(x, dst, M, d);
+  export_rows_kernel<St<T>::E><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(x, dst, m0, M, d);
   return hipGetLastError();
 }
-template hipError_t launch_export_rows<bf16>(const float*, float*, int, int, hipStream_t);
-template hipError_t launch_export_rows<float>(const float*, float*, int, int, hipStream_t);
+template hipError_t launch_export_rows<bf16>(const float*, float*, int, int, int, hipStream_t);
+template hipError_t launch_export_rows<float>(const float*, float*, int, int, int, hipStream_t);
 
 // The injected rows, normalised: sequence b's hidden row h = hidden[b,
 // index[b], :] as u = h / sqrt(mean(h^2) + eps) in the storage type (the

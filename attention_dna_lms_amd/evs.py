@@ -12,6 +12,7 @@ import ctypes
 import os
 from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_uint64, c_void_p
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,7 +33,8 @@ EXPORTS = ("evs_status_string", "evs_canonical_count", "evs_canonical_shape", "e
            "evs_model_create", "evs_pack_weights", "evs_model_destroy", "evs_state_bytes", "evs_state_create",
            "evs_state_destroy", "evs_state_tensor", "evs_state_error", "evs_prefill", "evs_block_verify",
            "evs_rollback", "evs_verify_sample", "evs_state_export", "evs_draft", "evs_state_timing",
-           "evs_state_timing_read", "evs_block_verify_noalloc")
+           "evs_state_timing_read", "evs_block_verify_noalloc", "evs_generate_workspace_bytes", "evs_generate")
+EVS_DRAFT_NONE, EVS_DRAFT_MODEL, EVS_DRAFT_TABLE = 0, 1, 2
 EVS_NOALLOC_SCRATCH_BYTES = 32 << 20
 EVS_KC_GEMM, EVS_KC_ATTN = 1, 2
 
@@ -52,6 +54,17 @@ class ModelDesc(ctypes.Structure):
     _fields_ = [("d_model", c_int32), ("vocab", c_int32), ("n_blocks", c_int32), ("dtype", c_int32),
                 ("norm_eps", c_float), ("blocks", POINTER(BlockDesc)), ("inject_dim", c_int32),
                 ("max_slots", c_int32)]
+
+
+class DraftSource(ctypes.Structure):
+    _fields_ = [("source", c_int32), ("drafter", c_void_p), ("drafter_state", c_void_p), ("table_dev", c_void_p),
+                ("table_len", c_int32), ("replace_dev", c_void_p)]
+
+
+class GenParams(ctypes.Structure):
+    _fields_ = [("n_tokens", c_int32), ("gamma", c_int32), ("greedy", c_int32), ("temperature", c_float),
+                ("top_k", c_int32), ("rounds_cap", c_int32), ("u_first_dev", c_void_p), ("u_target_dev", c_void_p),
+                ("u_draft_dev", c_void_p)]
 
 
 class TensorDesc(ctypes.Structure):
@@ -92,6 +105,10 @@ def lib():
         "evs_verify_sample": [c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_float,
                               c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "evs_state_export": [c_void_p, c_int32, c_void_p],
+        "evs_generate_workspace_bytes": [c_void_p, c_void_p, POINTER(GenParams), POINTER(DraftSource),
+                                         POINTER(c_size_t)],
+        "evs_generate": [c_void_p, c_void_p, c_void_p, POINTER(GenParams), POINTER(DraftSource), c_void_p, c_void_p,
+                         c_void_p, POINTER(c_int32), c_void_p],
         "evs_draft": [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p,
                       c_float, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p],
     }
@@ -297,6 +314,102 @@ def evs_draft(drafter: Model, dstate: State, batch, hidden, hidden_rows, hidden_
     _check(lib().evs_draft(drafter.handle, dstate.handle, int(batch), _ptr(hidden), int(hidden_rows),
                            _ptr(hidden_index), _ptr(last), int(gamma), _ptr(u), float(temperature), int(top_k),
                            int(greedy), _ptr(logits), _ptr(drafts), _ptr(q), _stream()), "evs_draft")
+
+
+def _gen_structs(n_tokens, gamma, greedy, temperature, top_k, rounds_cap, u_first, u_target, u_draft, source,
+                 drafter=None, drafter_state=None, table=None, replace=None):
+    p = GenParams(int(n_tokens), int(gamma), int(bool(greedy)), float(temperature), int(top_k), int(rounds_cap),
+                  _ptr(u_first), _ptr(u_target), _ptr(u_draft))
+    d = DraftSource(int(source), drafter.handle if drafter is not None else None,
+                    drafter_state.handle if drafter_state is not None else None, _ptr(table),
+                    0 if table is None else int(table.shape[-1]), _ptr(replace))
+    return p, d
+
+
+def evs_generate_workspace_bytes(model: Model, state: State, params: GenParams, source: DraftSource) -> int:
+    n = c_size_t()
+    _check(lib().evs_generate_workspace_bytes(model.handle, state.handle, ctypes.byref(params), ctypes.byref(source),
+                                              ctypes.byref(n)), "evs_generate_workspace_bytes")
+    return n.value
+
+
+def evs_generate(model: Model, state: State, last_logits, params: GenParams, source: DraftSource, work, ids,
+                 stats) -> int:
+    """Returns the number of rounds."""
+    n = c_int32()
+    _check(lib().evs_generate(model.handle, state.handle, _ptr(last_logits), ctypes.byref(params),
+                              ctypes.byref(source), _ptr(work), _ptr(ids), _ptr(stats), ctypes.byref(n), _stream()),
+           "evs_generate")
+    return n.value
+
+
+class GenResult:
+    """ids [B, n_tokens] (int64 numpy), tok_s (generated tokens per second,
+    all sequences, from the first draw to the last round), mean_tau (mean
+    tokens emitted per round, before the cut at n_tokens), rounds."""
+
+    def __init__(self, ids, tok_s, mean_tau, rounds, stats):
+        self.ids, self.tok_s, self.mean_tau, self.rounds, self.stats = ids, tok_s, mean_tau, rounds, stats
+
+
+def generate(model: Model, state: State, prompts, n_tokens, gamma=12, greedy=False, temperature=1.0, top_k=4,
+             drafter: Model = None, drafter_state: State = None, export_block=None, table=None, replace=None,
+             u_first=None, u_target=None, u_draft=None, rounds_cap=None, seed=0):
+    """Prompts (list of int arrays, one per sequence of `state`) -> GenResult,
+    through evs_prefill and evs_generate (model card, "Library": generate).
+    Drafts from `drafter` (with `drafter_state`, reading the target's
+    residual rows after block `export_block`), or from `table` [B, L]
+    (+ `replace`), or none (gamma must then be 0: generate_native).
+    Uniforms are taken as given, or drawn on the device from `seed`."""
+    dev = state.buf.device
+    B = state.B
+    if len(prompts) != B:
+        raise ValueError("one prompt per sequence of the state")
+    rounds_cap = int(rounds_cap or n_tokens)
+    src = EVS_DRAFT_MODEL if drafter is not None else EVS_DRAFT_TABLE if table is not None else EVS_DRAFT_NONE
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(seed))
+
+    def uni(x, shape):
+        return torch.as_tensor(x, dtype=torch.float32, device=dev).contiguous() if x is not None else \
+            torch.rand(shape, generator=g, device=dev, dtype=torch.float32)
+    uf = uni(u_first, (B,))
+    ut = uni(u_target, (rounds_cap, B, gamma + 1))
+    ud = uni(u_draft, (rounds_cap, B, max(gamma, 1))) if src == EVS_DRAFT_MODEL else None
+    tab = None if table is None else torch.as_tensor(table, dtype=torch.int32, device=dev).contiguous()
+    rep = None if replace is None else torch.as_tensor(replace, dtype=torch.int32, device=dev).contiguous()
+    p, d = _gen_structs(n_tokens, gamma, greedy, temperature, top_k, rounds_cap, uf, ut, ud, src, drafter,
+                        drafter_state, tab, rep)
+    hidden = None
+    if src == EVS_DRAFT_MODEL:
+        hidden = torch.zeros(B * state.max_block * model.cfg.d_model, dtype=torch.float32, device=dev)
+        evs_state_export(state, export_block, hidden)
+    flat = torch.as_tensor(np.concatenate([np.asarray(x, np.int32) for x in prompts]), device=dev)
+    offs = np.concatenate([[0], np.cumsum([len(x) for x in prompts])])
+    last = torch.zeros(B, model.cfg.vocab, dtype=_TORCH_DT[model.desc.dtype if model.desc.dtype != EVS_BF16_FP8W
+                                                           else EVS_BF16], device=dev)
+    evs_prefill(model, state, flat, offs, last)
+    work = _aligned_buffer(evs_generate_workspace_bytes(model, state, p, d), dev)[1]
+    ids = torch.zeros(B, n_tokens, dtype=torch.int32, device=dev)
+    stats = torch.zeros(B, 2, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    try:
+        rounds = evs_generate(model, state, last, p, d, work, ids, stats)
+    finally:
+        if hidden is not None:
+            evs_state_export(state, -1)
+    e1.record()
+    torch.cuda.synchronize()
+    st = stats.cpu().numpy()
+    tok_s = B * n_tokens / (e0.elapsed_time(e1) / 1e3)
+    mean_tau = float(st[:, 1].sum() / max(st[:, 0].sum(), 1))
+    return GenResult(ids.cpu().numpy().astype(np.int64), tok_s, mean_tau, rounds, st)
+
+
+def generate_native(model: Model, state: State, prompts, n_tokens, greedy=False, **kw):
+    """Native decoding (one token per target step) through the same loop."""
+    return generate(model, state, prompts, n_tokens, gamma=0, greedy=greedy, **kw)
 
 
 def status_string(status: int) -> str:

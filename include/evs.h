@@ -269,7 +269,9 @@ evs_status evs_verify_sample(int32_t batch, int32_t gamma, int32_t vocab, const 
  * index into the descriptor's blocks; for a [mixer, MLP] layer stack, layer L
  * ends at block 2L + 1) to dst_dev [B, gamma+1, d] (row-major f32; row i of
  * sequence b is candidate position i). block = -1 (dst_dev NULL) turns it off.
- * dst_dev must hold B * max_block * d floats and outlive its use. */
+ * dst_dev must hold B * max_block * d floats and outlive its use. While the
+ * export is on, evs_prefill writes each sequence's last prompt row (after
+ * block `block`) to dst_dev[b, 0, :] ([B, 1, d]). */
 evs_status evs_state_export(evs_state* s, int32_t block, float* dst_dev);
 
 /* Draft gamma tokens for each of B sequences with a drafter model (inject_dim
@@ -299,6 +301,74 @@ evs_status evs_draft(evs_model* drafter, evs_state* ds, int32_t batch, const flo
                      int32_t hidden_rows, const int32_t* hidden_index_dev, const int32_t* last_dev,
                      int32_t gamma, const float* u_dev, float temperature, int32_t top_k, int32_t greedy,
                      void* logits_dev, int32_t* drafts_dev, float* q_dev, void* stream);
+
+/* ------------------------------------------------------------- generation */
+
+/* Where a speculative round's drafts come from. */
+enum { EVS_DRAFT_NONE = 0, EVS_DRAFT_MODEL = 1, EVS_DRAFT_TABLE = 2 };
+
+typedef struct {
+  int32_t source;               /* EVS_DRAFT_NONE (native decoding: gamma 0), _MODEL or _TABLE */
+  /* EVS_DRAFT_MODEL: a drafter (inject_dim = the target's d_model, same vocab)
+   * and its own state (batch >= B, max_block >= gamma), run through
+   * evs_draft on the target's exported residual rows. The target state's
+   * export must be on (evs_state_export) before the prompt's evs_prefill, so
+   * that the first round reads each sequence's last prompt row. */
+  evs_model* drafter;
+  evs_state* drafter_state;
+  /* EVS_DRAFT_TABLE: proposals table_dev [B, table_len] (i32) by generated
+   * position: after e emitted tokens, draft i (1 .. gamma) is
+   * table[b][min(e + i - 1, table_len - 1)]; replace_dev (may be NULL)
+   * [rounds_cap, B, gamma] (i32): where an entry is >= 0 it replaces that
+   * round's draft. The drafts' q is one-hot (a deterministic drafter). With
+   * the target's own greedy continuation as the table this is the identity
+   * drafter. */
+  const int32_t* table_dev;
+  int32_t table_len;
+  const int32_t* replace_dev;
+} evs_draft_source;
+
+typedef struct {
+  int32_t n_tokens;             /* tokens to emit per sequence, >= 1 */
+  int32_t gamma;                /* drafts per round (0 .. max_block - 1; 0 with EVS_DRAFT_NONE) */
+  int32_t greedy;               /* greedy verification (and greedy drafts) */
+  float temperature;            /* finite, > 0 (sampling) */
+  int32_t top_k;                /* 0 or >= V keeps all */
+  int32_t rounds_cap;           /* rounds the uniform (and replace) arrays cover, >= 1 */
+  const float* u_first_dev;     /* [B]: draw of the first token (sampling) */
+  const float* u_target_dev;    /* [rounds_cap, B, gamma + 1]: each round's verifier uniforms (sampling) */
+  const float* u_draft_dev;     /* [rounds_cap, B, gamma]: each round's drafter uniforms (EVS_DRAFT_MODEL, sampling) */
+} evs_gen_params;
+
+/* Bytes of the caller-owned work buffer evs_generate needs. */
+evs_status evs_generate_workspace_bytes(const evs_model* m, const evs_state* s, const evs_gen_params* p,
+                                        const evs_draft_source* d, size_t* bytes);
+
+/* Generation by speculative rounds (EvSpark model card, "Library": generate,
+ * and generate_native with gamma = 0 and EVS_DRAFT_NONE; preprint, abstract
+ * (i)). Starts from a state whose prompts were just consumed by evs_prefill,
+ * with last_logits_dev [B, V] (storage type) the logits that call returned.
+ * The first token of each sequence is drawn from them (argmax when greedy,
+ * else the inverse CDF of the target distribution at u_first). Each round r
+ * then, on the device: drafts gamma tokens after the last emitted token
+ * x_last; runs evs_block_verify on [x_last, drafts]; verifies them
+ * (evs_verify_sample, uniforms u_target[r]); emits d_1 .. d_{n_accepted} and
+ * the next token, cut at n_tokens (a sequence with r tokens left takes the
+ * first r and keeps r block positions); rolls back to the kept positions.
+ * Outputs: ids_dev [B, n_tokens] (i32), stats_dev [B, 2] (i32: rounds the
+ * sequence took part in, tokens those rounds emitted before the cut, so their
+ * ratio is the mean tokens per round), *n_rounds_host. work_dev: at least
+ * evs_generate_workspace_bytes bytes, 256-byte aligned. Afterwards the state
+ * holds the prompt and every emitted token but the last. Unlike the other
+ * calls this one synchronises `stream`: the host reads the emitted counts
+ * between batches of rounds to decide how many more to enqueue. Errors:
+ * argument checks as listed (EVS_E_STATE: a pending block, a state without a
+ * workspace, or a model drafter without the target's export on);
+ * EVS_E_RANGE if rounds_cap rounds do not reach n_tokens (the outputs then
+ * hold what was emitted). */
+evs_status evs_generate(evs_model* m, evs_state* s, const void* last_logits_dev, const evs_gen_params* p,
+                        const evs_draft_source* d, void* work_dev, int32_t* ids_dev, int32_t* stats_dev,
+                        int32_t* n_rounds_host, void* stream);
 
 /* ------------------------------------------------------------ measurement */
 
