@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["gemm_bf16.hip", "gemm_fp8.hip", "gemm_f32.hip", "gemm_split.hip", "attn.hip", "small.hip", "gen.hip",
-           "evs_api.cpp"]
+           "measure.hip", "evs_api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

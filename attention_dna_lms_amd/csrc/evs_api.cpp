@@ -1062,6 +1062,35 @@ evs_status evs_generate(evs_model* m, evs_state* s, const void* last_logits, con
   return EVS_OK;
 }
 
+evs_status evs_measure_weight_stream(const evs_model* m, int32_t block, int32_t which, void* sink_dev,
+                                     size_t sink_bytes, double* bytes_host, void* stream) {
+  if (!m || !sink_dev || !bytes_host) return EVS_E_INVALID;
+  if (m->desc.dtype != EVS_BF16) return EVS_E_UNSUPPORTED;
+  const Mat* mat = nullptr;
+  if (which == EVS_W_LM) {
+    mat = &m->lm;
+  } else {
+    if (block < 0 || (size_t)block >= m->plan.size()) return EVS_E_INVALID;
+    const BlockPlan& p = m->plan[block];
+    const bool mlp = p.d.kind == EVS_MLP;
+    if (which == EVS_W_IN && !mlp) mat = &p.w_in;
+    else if (which == EVS_W_OUT && !mlp) mat = &p.w_out;
+    else if (which == EVS_W_GU && mlp) mat = &p.w_gu;
+    else if (which == EVS_W_DOWN && mlp) mat = &p.w_down;
+    else return EVS_E_INVALID;
+  }
+  if (sink_bytes < (size_t)mat->n_groups * 512 * 4) return EVS_E_RANGE;
+  // the chunk depth gemm_kernel streams this matrix with at one row tile
+  const int CH = mat->NT == 1 ? 4 : 2;
+  const int ksteps = mat->K / m->kstep;
+  const long long per_wave = (ksteps + GEMM_WAVES - 1) / GEMM_WAVES;
+  *bytes_host = (double)mat->bytes(m->es);
+  return hip_ok(launch_stream(mat->NT, CH, reinterpret_cast<const uint4*>(m->base + mat->off),
+                              (long long)ksteps * mat->NT * 64, per_wave * mat->NT * 64, (long long)mat->NT * 64,
+                              ksteps, mat->n_groups, reinterpret_cast<unsigned*>(sink_dev),
+                              reinterpret_cast<hipStream_t>(stream)));
+}
+
 evs_status evs_state_timing(evs_state* s, int32_t enable, int64_t context_hint) {
   if (!s) return EVS_E_INVALID;
   HIP_TRY(close_span(s));

@@ -186,6 +186,9 @@ struct DraftArgs {
   int* err;
 };
 template <typename T> hipError_t launch_export_rows(const float* x, float* dst, int m0, int M, int d, hipStream_t st);
+// measurement aid (measure.hip): the weight stream of one packed matrix alone
+hipError_t launch_stream(int NT, int CH, const uint4* W, long long gstride, long long wstride, long long tstride,
+                         int ksteps, int n_groups, unsigned* sink, hipStream_t st);
 // generation loop (gen.hip)
 hipError_t launch_gen_start(const int* next, int B, int n_tokens, int* ids, int* last, int* idx, int* emitted,
                             int* stats, hipStream_t st);

@@ -33,7 +33,9 @@ EXPORTS = ("evs_status_string", "evs_canonical_count", "evs_canonical_shape", "e
            "evs_model_create", "evs_pack_weights", "evs_model_destroy", "evs_state_bytes", "evs_state_create",
            "evs_state_destroy", "evs_state_tensor", "evs_state_error", "evs_prefill", "evs_block_verify",
            "evs_rollback", "evs_verify_sample", "evs_state_export", "evs_draft", "evs_state_timing",
-           "evs_state_timing_read", "evs_block_verify_noalloc", "evs_generate_workspace_bytes", "evs_generate")
+           "evs_state_timing_read", "evs_block_verify_noalloc", "evs_generate_workspace_bytes", "evs_generate",
+           "evs_measure_weight_stream")
+EVS_W_IN, EVS_W_OUT, EVS_W_GU, EVS_W_DOWN, EVS_W_LM = 1, 2, 3, 4, 5
 EVS_DRAFT_NONE, EVS_DRAFT_MODEL, EVS_DRAFT_TABLE = 0, 1, 2
 EVS_NOALLOC_SCRATCH_BYTES = 32 << 20
 EVS_KC_GEMM, EVS_KC_ATTN = 1, 2
@@ -105,6 +107,8 @@ def lib():
         "evs_verify_sample": [c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_float,
                               c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "evs_state_export": [c_void_p, c_int32, c_void_p],
+        "evs_measure_weight_stream": [c_void_p, c_int32, c_int32, c_void_p, c_size_t, POINTER(ctypes.c_double),
+                                      c_void_p],
         "evs_generate_workspace_bytes": [c_void_p, c_void_p, POINTER(GenParams), POINTER(DraftSource),
                                          POINTER(c_size_t)],
         "evs_generate": [c_void_p, c_void_p, c_void_p, POINTER(GenParams), POINTER(DraftSource), c_void_p, c_void_p,
@@ -410,6 +414,15 @@ def generate(model: Model, state: State, prompts, n_tokens, gamma=12, greedy=Fal
 def generate_native(model: Model, state: State, prompts, n_tokens, greedy=False, **kw):
     """Native decoding (one token per target step) through the same loop."""
     return generate(model, state, prompts, n_tokens, gamma=0, greedy=greedy, **kw)
+
+
+def evs_measure_weight_stream(model: Model, block: int, which: int, sink) -> float:
+    """Enqueue the weight stream of one projection (measurement aid); returns its bytes."""
+    by = ctypes.c_double()
+    _check(lib().evs_measure_weight_stream(model.handle, int(block), int(which), _ptr(sink),
+                                           sink.numel() * sink.element_size(), ctypes.byref(by), _stream()),
+           "evs_measure_weight_stream")
+    return by.value
 
 
 def status_string(status: int) -> str:

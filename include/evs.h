@@ -384,6 +384,21 @@ enum { EVS_KC_GEMM = 1, EVS_KC_ATTN = 2 };
  * gaps between them). Leave it off for headline timing. */
 evs_status evs_state_timing(evs_state* s, int32_t enable, int64_t context_hint);
 
+/* projections for evs_measure_weight_stream */
+enum { EVS_W_IN = 1, EVS_W_OUT = 2, EVS_W_GU = 3, EVS_W_DOWN = 4, EVS_W_LM = 5 };
+
+/* Measurement aid: enqueue a kernel that reads the packed weights of one
+ * projection exactly as the projection's GEMM does (same workgroups, the
+ * same contiguous per-wave fragment runs, 16-byte non-temporal loads, the
+ * same chunk pipeline at one row tile) and nothing else, so its duration is
+ * the weight-read floor of that projection. `block` selects the block (a
+ * mixer block for EVS_W_IN / EVS_W_OUT, an MLP block for EVS_W_GU /
+ * EVS_W_DOWN; ignored for EVS_W_LM). sink_dev receives one word per thread
+ * (n_groups * 512 * 4 bytes; EVS_E_RANGE if sink_bytes is smaller);
+ * *bytes_host the weight bytes read. EVS_BF16 models only. */
+evs_status evs_measure_weight_stream(const evs_model* m, int32_t block, int32_t which, void* sink_dev,
+                                     size_t sink_bytes, double* bytes_host, void* stream);
+
 /* Synchronise `stream`, then sum the recorded launches of one kernel class:
  * total device time (ms), number of launches and algorithmic bytes. The
  * records read are cleared. */
