@@ -41,11 +41,15 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rounds", type=int, default=3, help="timed oracle rounds for cpu_baseline")
     ap.add_argument("--soak", type=int, metavar="N",
-                    help="generate N tokens natively and speculatively (~75% drafter) from the "
+                    help="generate N tokens natively and speculatively (~75%% drafter) from the "
                          "prefilled context and check they are identical; one JSON line")
     ap.add_argument("--batch-sweep", metavar="B1,B2,...",
-                    help="speculative rounds against plain batched decoding at these batch sizes "
-                         "(imported synthetic state; eager and HIP-graph replay), one JSON line each")
+                    help="speculative generation (identity and ~75%% drafters) against plain batched decoding at "
+                         "these batch sizes, through evs_generate (imported synthetic state), one JSON line each")
+    ap.add_argument("--gen-tokens", type=int, default=64,
+                    help="tokens per sequence in --batch-sweep")
+    ap.add_argument("--graph", action="store_true",
+                    help="one round at B = 1 launched eagerly and as a replayed HIP graph; one JSON line")
     ap.add_argument("--c5", action="store_true",
                     help="the ragged batch (8 sequences, contexts 1k-32k, imported state) at gamma 1..16; "
                          "one JSON line per gamma")
@@ -400,12 +404,86 @@ def import_synthetic_state(evs, es, cfg, state, t, seed, dev, b=0):
 
 
 def batch_sweep(args):
-    """Speculative rounds against plain batched decoding over batch sizes, on
-    the 7B-shaped stack with an imported synthetic state per sequence. Prints
-    one JSON line per batch size: native (gamma = 0) step time and tokens/s,
-    identity-drafter round time and tokens/s (eager launches, then the same
-    round captured once as a HIP graph and replayed, the block gathered on the
-    device from each sequence's own position), and the speculative speedup."""
+    """Speculative generation against plain batched decoding over batch sizes
+    (Evo2 discussion #232, author reply, "Regime overlap": batching amortises
+    the same weight read speculation exploits; the crossover is to be
+    measured). The 7B-shaped stack, each sequence from an imported synthetic
+    state at --context; per batch size, through evs_generate (greedy):
+    native batched decoding (one token per sequence per step), then the
+    identity drafter (the native continuation as the proposals) and a ~75%
+    drafter (a quarter of the slots replaced by a random DNA letter), each
+    emitting --gen-tokens tokens per sequence. One JSON line per batch size:
+    tokens/s of each, tokens per round, and the speedups over native."""
+    import numpy as np
+    import torch
+    import evs_synth as es
+    from attention_dna_lms_amd import evs
+
+    dev = "cuda"
+    gamma, P, ctx, n = args.gamma, args.gamma + 1, args.context, args.gen_tokens
+    cfg = es.stack_7b()
+    log("generating and packing weights")
+    model = evs.Model(cfg, es.make_weights(cfg, seed=args.seed, device=dev), device=dev)
+    acgt = np.asarray(es.ACGT_IDS(cfg.vocab))
+    for B in [int(x) for x in args.batch_sweep.split(",")]:
+        log(f"batch {B}")
+        max_ctx = ctx + n + P + 64
+
+        def fresh():
+            st = evs.State(model, B, max_ctx, P, device=dev)
+            for b in range(B):
+                import_synthetic_state(evs, es, cfg, st, ctx, args.seed + b, dev, b)
+            torch.cuda.synchronize()
+            return st
+        # the first token of each sequence: a DNA letter (logits one-hot)
+        last = torch.zeros(B, cfg.vocab, dtype=torch.bfloat16, device=dev)
+        last[torch.arange(B, device=dev), torch.as_tensor(acgt[np.arange(B) % 4], device=dev)] = 1.0
+
+        def run(gam, table=None, replace=None):
+            st = fresh()
+            src = evs.EVS_DRAFT_TABLE if table is not None else evs.EVS_DRAFT_NONE
+            tab = None if table is None else torch.as_tensor(table, dtype=torch.int32, device=dev).contiguous()
+            rep = None if replace is None else torch.as_tensor(replace, dtype=torch.int32, device=dev).contiguous()
+            p, d = evs._gen_structs(n, gam, True, 1.0, 0, n, None, None, None, src, table=tab, replace=rep)
+            work = evs._aligned_buffer(evs.evs_generate_workspace_bytes(model, st, p, d), dev)[1]
+            ids = torch.zeros(B, n, dtype=torch.int32, device=dev)
+            stats = torch.zeros(B, 2, dtype=torch.int32, device=dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rounds = evs.evs_generate(model, st, last, p, d, work, ids, stats)
+            e1.record()
+            torch.cuda.synchronize()
+            assert st.error() == 0
+            sc = stats.cpu().numpy()
+            t = e0.elapsed_time(e1) / 1e3
+            del st
+            torch.cuda.empty_cache()
+            return ids.cpu().numpy(), B * n / t, float(sc[:, 1].sum() / max(sc[:, 0].sum(), 1)), rounds, t
+
+        nat_ids, nat_tps, _, nat_rounds, nat_t = run(0)
+        table = np.concatenate([nat_ids, np.repeat(nat_ids[:, -1:], P, axis=1)], axis=1)
+        ide_ids, ide_tps, ide_tau, ide_rounds, ide_t = run(gamma, table)
+        rng = np.random.default_rng([args.seed, 75, B])
+        rep = np.where(rng.random((n, B, gamma)) < 0.25, acgt[rng.integers(0, 4, (n, B, gamma))], -1)
+        d75_ids, d75_tps, d75_tau, d75_rounds, d75_t = run(gamma, table, rep)
+        print(json.dumps({"batch": B, "gamma": gamma, "context": ctx, "tokens_per_sequence": n,
+                          "native_tokens_per_s": round(nat_tps, 1), "native_step_ms": round(nat_t / nat_rounds * 1e3, 4),
+                          "identity_tokens_per_s": round(ide_tps, 1), "identity_tokens_per_round": round(ide_tau, 3),
+                          "identity_round_ms": round(ide_t / ide_rounds * 1e3, 4),
+                          "identity_speedup": round(ide_tps / nat_tps, 3),
+                          "drafter75_tokens_per_s": round(d75_tps, 1), "drafter75_tokens_per_round": round(d75_tau, 3),
+                          "drafter75_round_ms": round(d75_t / d75_rounds * 1e3, 4),
+                          "drafter75_speedup": round(d75_tps / nat_tps, 3),
+                          "outputs_equal_native": bool(np.array_equal(ide_ids, nat_ids) and np.array_equal(d75_ids, nat_ids))}),
+              flush=True)
+
+
+def graph_bench(args):
+    """One speculative round (block verify + greedy verify + rollback over
+    fixed device buffers) at B = 1: K rounds launched eagerly, then the same
+    round captured once as a HIP graph and replayed K times, each from the
+    same starting state; per-round times of both and whether every replay
+    matched the eager run."""
     import numpy as np
     import torch
     import evs_synth as es
@@ -416,107 +494,51 @@ def batch_sweep(args):
     cfg = es.stack_7b()
     log("generating and packing weights")
     model = evs.Model(cfg, es.make_weights(cfg, seed=args.seed, device=dev), device=dev)
-    W, K = args.warmup, args.steps
-    rounds = W + K
-    n_nat = 2 * rounds * P + 2          # native tokens per sequence: eager + graph passes
-    for B in [int(x) for x in args.batch_sweep.split(",")]:
-        state = evs.State(model, B, ctx + n_nat + 64, P, device=dev)
-        for b in range(B):
-            import_synthetic_state(evs, es, cfg, state, ctx, args.seed + b, dev, b)
-        snap = state.buf.clone()
-        V = cfg.vocab
-        one = torch.empty(B, 1, V, dtype=torch.bfloat16, device=dev)
-        acc1 = torch.zeros(B, dtype=torch.int32, device=dev)
-        keep1 = torch.zeros(B, dtype=torch.int32, device=dev)
-        nat = torch.zeros(n_nat, B, dtype=torch.int32, device=dev)     # [step, sequence]
-        nat[0] = torch.as_tensor(es.ACGT_IDS(V), dtype=torch.int32, device=dev)[torch.arange(B, device=dev) % 4]
+    K, W = args.steps, args.warmup
+    state = evs.State(model, 1, ctx + (K + W + 2) * P + 64, P, device=dev)
+    import_synthetic_state(evs, es, cfg, state, ctx, args.seed, dev, 0)
+    snap = state.buf.clone()
+    cand = torch.as_tensor(es.prompt_tokens(cfg, P, seed=args.seed + 1), device=dev)
+    drafts = cand[:, 1:].contiguous()
+    lg = torch.zeros(1, P, cfg.vocab, dtype=torch.bfloat16, device=dev)
+    acc, nxt, keep = (torch.zeros(1, dtype=torch.int32, device=dev) for _ in range(3))
 
-        def native_step(i):
-            evs.evs_block_verify(model, state, nat[i].view(B, 1), 0, one)
-            evs.evs_verify_sample(B, 0, V, one, evs.EVS_TARGET_LOGITS_BF16, None, None, None, 1.0, 0, 1,
-                                  acc1, nat[i + 1], keep1)
-            evs.evs_rollback(state, keep1)
-        for i in range(W):
-            native_step(i)
+    def one():
+        evs.evs_block_verify(model, state, cand, gamma, lg)
+        evs.evs_verify_sample(1, gamma, cfg.vocab, lg, evs.EVS_TARGET_LOGITS_BF16, None, drafts, None, 1.0, 0, 1,
+                              acc, nxt, keep)
+        evs.evs_rollback(state, keep)
+
+    def timed(fn):
+        state.buf.copy_(snap)
+        for _ in range(W):
+            fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for i in range(W, n_nat - 1):
-            native_step(i)
+        for _ in range(K):
+            fn()
         e1.record()
         torch.cuda.synchronize()
-        t_nat = e0.elapsed_time(e1) / (n_nat - 1 - W)
-        natT = nat.t().contiguous()                                      # [sequence, step]
+        return e0.elapsed_time(e1) / K
 
-        lg = torch.empty(B, P, V, dtype=torch.bfloat16, device=dev)
-        acc = torch.zeros(B, dtype=torch.int32, device=dev)
-        nxt = torch.zeros(B, dtype=torch.int32, device=dev)
-        keep = torch.zeros(B, dtype=torch.int32, device=dev)
-        pos = torch.zeros(B, dtype=torch.long, device=dev)
-        ar = torch.arange(P, device=dev)
-        rows = torch.arange(B, device=dev)[:, None]
-
-        def spec_round():
-            cand = natT[rows, pos[:, None] + ar]                         # [B, P] from each sequence's position
-            evs.evs_block_verify(model, state, cand, gamma, lg)
-            evs.evs_verify_sample(B, gamma, V, lg, evs.EVS_TARGET_LOGITS_BF16, None, cand[:, 1:].contiguous(), None,
-                                  1.0, 0, 1, acc, nxt, keep)
-            evs.evs_rollback(state, keep)
-            pos.add_(keep)
-
-        def timed(fn, n):
-            torch.cuda.synchronize()
-            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a0.record()
-            for _ in range(n):
-                fn()
-            a1.record()
-            torch.cuda.synchronize()
-            return a0.elapsed_time(a1) / n
-
-        state.buf.copy_(snap)
-        pos.zero_()
-        for _ in range(W):
-            spec_round()
-        t_eager = timed(spec_round, K)
-        acc_eager = acc.clone()
-        t_after, lg_eager = state.tensor(evs.EVS_ST_T).clone(), lg.clone()
-
-        state.buf.copy_(snap)
-        pos.zero_()
-        torch.cuda.synchronize()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            spec_round()                                                 # warm the allocator on the capture stream
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        state.buf.copy_(snap)
-        pos.zero_()
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            spec_round()
-        # capture records without running: replay from the snapshot
-        state.buf.copy_(snap)
-        pos.zero_()
-        torch.cuda.synchronize()
-        for _ in range(W):
-            graph.replay()
-        t_graph = timed(graph.replay, K)
-        same = bool(torch.equal(state.tensor(evs.EVS_ST_T), t_after) and torch.equal(lg, lg_eager)
-                    and torch.equal(acc, acc_eager))
-        assert state.error() == 0
-        print(json.dumps({"batch": B, "gamma": gamma, "context": ctx,
-                          "native_step_ms": round(t_nat, 4), "native_tokens_per_s": round(B * 1e3 / t_nat, 1),
-                          "spec_round_ms": round(t_eager, 4), "spec_tokens_per_s": round(B * P * 1e3 / t_eager, 1),
-                          "spec_round_graph_ms": round(t_graph, 4),
-                          "spec_tokens_per_s_graph": round(B * P * 1e3 / t_graph, 1),
-                          "speedup_identity_drafter": round(P * t_nat / t_eager, 3),
-                          "graph_matches_eager": same,
-                          "all_drafts_accepted": bool((acc_eager == gamma).all())}), flush=True)
-        del state, snap, graph
-        torch.cuda.empty_cache()
+    t_eager = timed(one)
+    t_after, lg_eager = state.tensor(evs.EVS_ST_T).clone(), lg.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one()
+    t_graph = timed(graph.replay)
+    same = bool(torch.equal(state.tensor(evs.EVS_ST_T), t_after) and torch.equal(lg, lg_eager))
+    assert state.error() == 0
+    print(json.dumps({"batch": 1, "gamma": gamma, "context": ctx, "rounds": K, "eager_round_ms": round(t_eager, 4),
+                      "graph_round_ms": round(t_graph, 4), "graph_over_eager": round(t_graph / t_eager, 4),
+                      "graph_matches_eager": same}), flush=True)
 
 
 def drafter_bench(args):
@@ -1010,6 +1032,9 @@ def main():
         return
     if args.batch_sweep:
         batch_sweep(args)
+        return
+    if args.graph:
+        graph_bench(args)
         return
     if args.drafter:
         drafter_bench(args)
