@@ -516,15 +516,12 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
 
   f32x4 acc[NT][MT];
   if constexpr (PART) {
-    if constexpr (AMODE == A_NORM) {
-#pragma unroll
-      for (int pss = 0; pss < NP; ++pss) row_scales(pss, 0.f, 0);
-    }
     // the eight k-range partials gemm_part_kernel formed (wave w takes range
     // w's chains, exactly what this kernel's wave w would have computed), or
     // the four pair sums gemm_pair_kernel formed (wave w < 4 takes ranges
     // w + (w + 4), the tree's first level; waves 4..7 hold -0, the exact
-    // additive identity, so the tree's remaining levels are unchanged)
+    // additive identity, so the tree's remaining levels are unchanged).
+    // Issued before the norm's loads, so both are in flight together.
     const int np = a.nparts == 4 ? 4 : 8;
     const f32x4* pp = reinterpret_cast<const f32x4*>(a.part) +
                       ((((size_t)blockIdx.y * np + min(wave, np - 1)) * a.n_groups + g) * MT) * NT * 64 + lane;
@@ -532,6 +529,10 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = pp[(mt * NT + nt) * 64];
+    if constexpr (AMODE == A_NORM) {
+#pragma unroll
+      for (int pss = 0; pss < NP; ++pss) row_scales(pss, 0.f, 0);
+    }
     if (wave >= np) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)

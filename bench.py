@@ -154,13 +154,18 @@ def projection_roles(sel, n_layers=32):
 
 
 # algorithmic bytes of one launch of each projection of the 7B-shaped stack at
-# 13 rows: the weights, the input rows (fp32 for the normed projections) and
-# the output rows (fp32 read + write for the residual epilogues)
-def projection_bytes(role, M=13, d=4096, dff=11008, V=512):
+# 13 rows: the weights (with FP8 weights one byte per element plus one fp32
+# scale per output row; the LM head stays bf16), the input rows (bf16; the
+# normed projections also read each row's d/16 fp32 sums of squares) and the
+# output rows (fp32 read + write plus bf16 write for the residual epilogues)
+def projection_bytes(role, M=13, d=4096, dff=11008, V=512, fp8=False):
+    def w(n, k):
+        return n * k * (1 if fp8 else 2) + (n * 4 if fp8 else 0)
+    nrm = M * (d // 16) * 4
     if role.startswith("in-proj"):
-        return 3 * d * d * 2 + M * d * 4 + M * 3 * d * 2
-    return {"out-proj": d * d * 2 + M * d * 2 + M * d * 8, "gate/up": 2 * dff * d * 2 + M * d * 2 + M * dff * 2,
-            "down": d * dff * 2 + M * dff * 2 + M * d * 8, "LM head": V * d * 2 + M * d * 4 + M * V * 2}[role]
+        return w(3 * d, d) + M * d * 2 + nrm + M * 3 * d * 2
+    return {"out-proj": w(d, d) + M * d * 2 + M * d * 10, "gate/up": w(2 * dff, d) + M * d * 2 + nrm + M * dff * 2,
+            "down": w(d, dff) + M * dff * 2 + M * d * 10, "LM head": V * d * 2 + M * d * 2 + nrm + M * V * 2}[role]
 
 
 def gemm_trace():
@@ -184,7 +189,7 @@ def rocprof_roofline(bytes_per_launch):
             "frac": round(gbps / HBM_PEAK_GBPS, 4), "source": os.path.relpath(TRACE_FILE, ROOT)}
 
 
-def summarize_trace(path, steps, warmup, json_out=None):
+def summarize_trace(path, steps, warmup, json_out=None, fp8=False):
     import collections
     import csv
     rows = list(csv.DictReader(open(path)))
@@ -221,7 +226,7 @@ def summarize_trace(path, steps, warmup, json_out=None):
           "|---|---|---|---|---|---|---|")
     for k, v in sorted(g.items(), key=lambda kv: -sum(kv[1])):
         us = sum(v) / len(v)
-        mb = projection_bytes(k) / 1e6
+        mb = projection_bytes(k, fp8=fp8) / 1e6
         print(f"| {k} | {len(v) / steps:.0f} | {us:.2f} | {sum(v) / steps:.1f} | {mb:.1f} | {mb * 1e3 / us:.0f} | "
               f"{mb * 1e3 / us / 8000:.3f} |")
     print()
@@ -1019,7 +1024,7 @@ def main():
         c5_bench(args)
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.steps, args.warmup, args.trace_json)
+        summarize_trace(args.summarize_trace, args.steps, args.warmup, args.trace_json, fp8=args.weights == "fp8")
         return
     if args.summarize_c5_counters:
         summarize_c5_counters(*args.summarize_c5_counters, args.steps, args.warmup)
