@@ -77,6 +77,7 @@ struct evs_state {
   size_t w_inj_x = 0, w_z = 0;                  // drafter: the normalised injected rows, the prefix z
   size_t w_xb = 0;                              // bf16 models: the residual rows in bf16 (normed operands)
   size_t w_part = 0, part_bytes = 0;            // bf16 models: split-K partials of multi-tile launches
+  size_t w_pre = 0;                             // batched prefill: candidate blocks, n_keep, picks, offsets (int32)
   int export_block = -1;                        // hidden-state export after this block (evs_block_verify)
   float* export_dst = nullptr;
   bool pending = false;
@@ -263,7 +264,9 @@ void layout_state(evs_state* s) {
   s->w_o = take(M16 * d * es);
   s->w_q = take(M16 * d * es);
   s->w_h = take(M16 * std::max(m->max_dff, 32) * es);
-  s->w_logit = take((size_t)s->max_block * m->desc.vocab * es);
+  // logits staging (evs_prefill's last rows): every sequence's block
+  s->w_logit = take((size_t)B * s->max_block * m->desc.vocab * es);
+  s->w_pre = take(((size_t)B * s->max_block + 3 * (size_t)B + 1) * 4);
   const int H = std::max(m->max_heads, 1), DHm = std::max(m->max_dh, 32);
   s->qtn_max = (s->max_block + 15) / 16;
   s->apart_floats = (size_t)B * s->qtn_max * H * s->S * 16 * (DHm + 2);
@@ -398,10 +401,13 @@ evs_status gemm_call(evs_model* m, evs_state* s, const Mat& mat, int amode, int 
 // (or, with tokens null, input rows the caller already wrote into the
 // residual buffer with their norm partials), every block, and the LM head
 // into `logits` (if not null). With export_dst, the residual rows after block
-// s->export_block are also written out row-major.
+// s->export_block are also written out row-major: rows export_m0 ..
+// export_m0 + export_n - 1 of the call, or with export_pick (device, one entry
+// per sequence) block row export_pick[b] of each sequence into row b.
 template <typename T>
 evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const int32_t* tokens, void* logits,
-                   hipStream_t st, float* export_dst = nullptr, int export_m0 = 0, int export_n = -1) {
+                   hipStream_t st, float* export_dst = nullptr, int export_m0 = 0, int export_n = -1,
+                   const int* export_pick = nullptr) {
   const int d = m->desc.d_model, M = nseq * P;
   if (export_n < 0) export_n = M;
   float* x = wp<float>(s, s->w_x);
@@ -421,7 +427,8 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
                             m->desc.vocab, P, seq0, t, s->max_ctx, err, st));
   for (size_t i = 0; i < m->plan.size(); ++i) {
     if (i > 0 && export_dst && (int)i - 1 == s->export_block)
-      HIP_TRY(launch_export_rows<T>(x, export_dst, export_m0, export_n, d, st));
+      HIP_TRY(export_pick ? launch_export_pick<T>(x, export_dst, export_pick, nseq, P, d, st)
+                          : launch_export_rows<T>(x, export_dst, export_m0, export_n, d, st));
     const BlockPlan& p = m->plan[i];
     GemmArgs a{};
     if (p.d.kind == EVS_MLP) {
@@ -492,7 +499,8 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
     EVS_TRY(gemm_call<T>(m, s, p.w_out, A_ACT, E_RESID, wp<void>(s, s->w_o), d, nseq, P, b, st));
   }
   if (export_dst && s->export_block == (int)m->plan.size() - 1)
-    HIP_TRY(launch_export_rows<T>(x, export_dst, export_m0, export_n, d, st));
+    HIP_TRY(export_pick ? launch_export_pick<T>(x, export_dst, export_pick, nseq, P, d, st)
+                        : launch_export_rows<T>(x, export_dst, export_m0, export_n, d, st));
   if (logits) {
     GemmArgs a{};
     a.N = m->desc.vocab; a.out = logits; a.ldo = m->desc.vocab;
@@ -505,10 +513,11 @@ evs_status forward(evs_model* m, evs_state* s, int seq0, int nseq, int P, const 
 }
 
 evs_status forward_any(evs_model* m, evs_state* s, int seq0, int nseq, int P, const int32_t* tokens, void* logits,
-                       hipStream_t st, float* export_dst = nullptr, int export_m0 = 0, int export_n = -1) {
+                       hipStream_t st, float* export_dst = nullptr, int export_m0 = 0, int export_n = -1,
+                       const int* export_pick = nullptr) {
   if (storage_dtype(&m->desc) == EVS_BF16)
-    return forward<bf16>(m, s, seq0, nseq, P, tokens, logits, st, export_dst, export_m0, export_n);
-  return forward<float>(m, s, seq0, nseq, P, tokens, logits, st, export_dst, export_m0, export_n);
+    return forward<bf16>(m, s, seq0, nseq, P, tokens, logits, st, export_dst, export_m0, export_n, export_pick);
+  return forward<float>(m, s, seq0, nseq, P, tokens, logits, st, export_dst, export_m0, export_n, export_pick);
 }
 
 // The drafter's pass (evs_draft): injected prefix, slot rows, the drafter's
@@ -863,6 +872,32 @@ evs_status evs_prefill(evs_model* m, evs_state* s, const int32_t* tokens, const 
     if (offs[b + 1] - offs[b] > s->max_ctx) return EVS_E_RANGE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int V = m->desc.vocab;
+  if (s->B > 1) {
+    // All sequences advance together, P positions per round (one forward and
+    // one weight read per round for the whole batch), prompts right-aligned
+    // so every last prompt row falls in the final round. Block verify equals
+    // sequential decoding bit for bit whatever the chunking, so the state and
+    // the last logits are those of per-sequence prefill.
+    const int P = std::min(s->max_block, s->max_ctx);
+    int R = 0;
+    for (int b = 0; b < s->B; ++b) R = std::max(R, (offs[b + 1] - offs[b] + P - 1) / P);
+    if (R == 0) return EVS_OK;
+    int32_t* pre = wp<int32_t>(s, s->w_pre);
+    int32_t *cand = pre, *n_keep = pre + (size_t)s->B * s->max_block, *pick = n_keep + s->B, *doffs = pick + s->B;
+    HIP_TRY(hipMemcpyAsync(doffs, offs, (size_t)(s->B + 1) * 4, hipMemcpyHostToDevice, st));
+    for (int j = 0; j < R; ++j) {
+      const bool last = j == R - 1;
+      HIP_TRY(launch_prefill_round(tokens, doffs, s->B, P, R, j, cand, n_keep, pick, st));
+      void* lg = (last && last_logits) ? wp<void>(s, s->w_logit) : nullptr;
+      float* ex = (last && s->export_block >= 0) ? s->export_dst : nullptr;
+      EVS_TRY(forward_any(m, s, 0, s->B, P, cand, lg, st, ex, 0, -1, pick));
+      HIP_TRY(close_span(s));
+      HIP_TRY(launch_commit(sp<int>(s, s->off_t), sp<int>(s, s->off_ib), sp<int>(s, s->off_is), n_keep, 0, s->B, P,
+                            sp<int>(s, s->off_err), st));
+      if (lg) HIP_TRY(launch_pick_rows(lg, last_logits, pick, s->B, P, (size_t)V * m->es, st));
+    }
+    return EVS_OK;
+  }
   const int chunk = s->max_block;
   for (int b = 0; b < s->B; ++b) {
     const int n = offs[b + 1] - offs[b];

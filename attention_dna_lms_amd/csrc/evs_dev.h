@@ -186,6 +186,8 @@ struct DraftArgs {
   int* err;
 };
 template <typename T> hipError_t launch_export_rows(const float* x, float* dst, int m0, int M, int d, hipStream_t st);
+template <typename T>
+hipError_t launch_export_pick(const float* x, float* dst, const int* pick, int B, int P, int d, hipStream_t st);
 // measurement aid (measure.hip): the weight stream of one packed matrix alone
 hipError_t launch_stream(int NT, int CH, const uint4* W, long long gstride, long long wstride, long long tstride,
                          int ksteps, int n_groups, unsigned* sink, hipStream_t st);
@@ -196,6 +198,11 @@ hipError_t launch_gen_cand(const int* last, const int* emitted, int B, int gamma
                            const int* replace, int* drafts, int* cand, float* q, int V, hipStream_t st);
 hipError_t launch_gen_emit(const int* drafts, int gamma, const int* n_acc, const int* next, int B, int n_tokens,
                            int* ids, int* emitted, int* n_keep, int* last, int* idx, int* stats, hipStream_t st);
+// batched prefill: one round's candidate blocks, n_keep and last-row picks; the picked rows
+hipError_t launch_prefill_round(const int* tokens, const int* offs, int B, int P, int R, int j, int* cand,
+                                int* n_keep, int* pick, hipStream_t st);
+hipError_t launch_pick_rows(const void* src, void* dst, const int* pick, int B, int P, size_t row_bytes,
+                            hipStream_t st);
 template <typename T>
 hipError_t launch_inject_prep(const float* hidden, int rows, const int* index, int B, int K, float eps, T* u,
                               int* err, hipStream_t st);

@@ -110,4 +110,48 @@ hipError_t launch_gen_emit(const int* drafts, int gamma, const int* n_acc, const
   return hipGetLastError();
 }
 
+// Batched prefill, round j of R lockstep rounds of P positions over all
+// sequences. The prompts are right-aligned: sequence b with n tokens covers
+// positions [max(e - P, 0), max(e, 0)) in round j, e = n - (R - 1 - j) * P, so
+// its first chunk is the partial one and its last token falls in round R - 1.
+// Its block is those tokens followed by copies of the last one (the commit
+// keeps only n_keep = their count); pick = the block row of its last token in
+// this round, -1 if it has none. One workgroup per sequence.
+__global__ void prefill_round_kernel(const int* tokens, const int* offs, int P, int R, int j, int* cand, int* n_keep,
+                                     int* pick) {
+  const int b = blockIdx.x;
+  const int o = offs[b], n = offs[b + 1] - o;
+  const int e = n - (R - 1 - j) * P;
+  const int s0 = max(e - P, 0), v = max(e, 0) - s0;
+  for (int i = threadIdx.x; i < P; i += blockDim.x) cand[(size_t)b * P + i] = v > 0 ? tokens[o + s0 + min(i, v - 1)] : 0;
+  if (threadIdx.x == 0) {
+    n_keep[b] = v;
+    pick[b] = v - 1;
+  }
+}
+
+hipError_t launch_prefill_round(const int* tokens, const int* offs, int B, int P, int R, int j, int* cand,
+                                int* n_keep, int* pick, hipStream_t st) {
+  prefill_round_kernel<<<B, 64, 0, st>>>(tokens, offs, P, R, j, cand, n_keep, pick);
+  return hipGetLastError();
+}
+
+// dst row b = src row b * P + pick[b] (row_bytes each), for the sequences with
+// pick[b] >= 0 (the last prompt row's logits of a batched prefill)
+__global__ void pick_rows_kernel(const unsigned char* src, unsigned char* dst, const int* pick, int P,
+                                 size_t row_bytes) {
+  const int b = blockIdx.x, r = pick[b];
+  if (r < 0) return;
+  const unsigned char* sr = src + ((size_t)b * P + r) * row_bytes;
+  unsigned char* dr = dst + (size_t)b * row_bytes;
+  for (size_t i = threadIdx.x; i < row_bytes; i += blockDim.x) dr[i] = sr[i];
+}
+
+hipError_t launch_pick_rows(const void* src, void* dst, const int* pick, int B, int P, size_t row_bytes,
+                            hipStream_t st) {
+  pick_rows_kernel<<<B, 256, 0, st>>>(reinterpret_cast<const unsigned char*>(src),
+                                      reinterpret_cast<unsigned char*>(dst), pick, P, row_bytes);
+  return hipGetLastError();
+}
+
 }  // namespace evs

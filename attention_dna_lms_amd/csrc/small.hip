@@ -741,6 +741,26 @@ hipError_t launch_export_rows(const float* x, float* dst, int m0, int M, int d, 
 template hipError_t launch_export_rows<bf16>(const float*, float*, int, int, int, hipStream_t);
 template hipError_t launch_export_rows<float>(const float*, float*, int, int, int, hipStream_t);
 
+// The residual row of block row pick[b] of each sequence (P rows per
+// sequence) into row b of dst; sequences with pick[b] < 0 are skipped.
+template <int E>
+__global__ void export_pick_kernel(const float* __restrict__ x, float* __restrict__ dst, const int* __restrict__ pick,
+                                   int P, int d) {
+  const int b = blockIdx.y, r = pick[b];
+  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (r < 0 || c >= d) return;
+  *reinterpret_cast<float4*>(dst + (size_t)b * d + c) = *reinterpret_cast<const float4*>(x + act_off<E>(b * P + r, c, d));
+}
+
+template <typename T>
+hipError_t launch_export_pick(const float* x, float* dst, const int* pick, int B, int P, int d, hipStream_t st) {
+  dim3 grid((d / 4 + 255) / 256, B);
+  export_pick_kernel<St<T>::E><<<grid, 256, 0, st>>>(x, dst, pick, P, d);
+  return hipGetLastError();
+}
+template hipError_t launch_export_pick<bf16>(const float*, float*, const int*, int, int, int, hipStream_t);
+template hipError_t launch_export_pick<float>(const float*, float*, const int*, int, int, int, hipStream_t);
+
 // The injected rows, normalised: sequence b's hidden row h = hidden[b,
 // index[b], :] as u = h / sqrt(mean(h^2) + eps) in the storage type (the
 // operand of the injection product), in the operand-order layout. One

@@ -187,13 +187,22 @@ evs_status evs_state_error(evs_state* s, int32_t* host_word, int32_t clear, void
 
 /* --------------------------------------------------------------- hot path */
 
-/* Consume prompt tokens into committed sequences. tokens_dev holds the
- * concatenated prompts (i32); seq_offsets_host[B+1] delimits sequence b's
- * tokens. Each sequence's tokens are appended after its committed length, in
- * chunks of at most max_block positions. last_logits_dev [B, V] (storage
- * type; may be NULL) receives the logits after each sequence's last token
- * (rows of sequences with no tokens are left untouched). Requires no pending
- * block. */
+/* Consume prompt tokens into committed sequences (model card, "Library":
+ * generation starts from a prompt, which is consumed before the first round). tokens_dev holds the concatenated
+ * prompts (i32); seq_offsets_host[B+1] delimits sequence b's tokens (copied
+ * before the call returns). Each sequence's tokens are appended after its
+ * committed length. With one sequence, the prompt goes in chunks of at most
+ * max_block positions. With several, all sequences advance together in
+ * rounds of P = min(max_block, max_ctx) positions, one forward per round for
+ * the whole batch. The prompts are right-aligned so that every last prompt
+ * token falls in the final round. A sequence's block in a round is its
+ * tokens of that round followed by copies of the last one, of which the
+ * commit keeps only the tokens. The committed state and the logits equal
+ * per-sequence prefill bit for bit. last_logits_dev [B, V] (storage type; may
+ * be NULL) receives the logits after each sequence's last token. With the
+ * hidden-state export on, row b of the export buffer receives that token's
+ * residual row. Rows of sequences with no tokens are left untouched.
+ * Requires no pending block. */
 evs_status evs_prefill(evs_model* m, evs_state* s, const int32_t* tokens_dev,
                        const int32_t* seq_offsets_host, void* last_logits_dev, void* stream);
 
@@ -393,9 +402,13 @@ enum { EVS_W_IN = 1, EVS_W_OUT = 2, EVS_W_GU = 3, EVS_W_DOWN = 4, EVS_W_LM = 5 }
  * same chunk pipeline at one row tile) and nothing else, so its duration is
  * the weight-read floor of that projection. `block` selects the block (a
  * mixer block for EVS_W_IN / EVS_W_OUT, an MLP block for EVS_W_GU /
- * EVS_W_DOWN; ignored for EVS_W_LM). sink_dev receives one word per thread
- * (n_groups * 512 * 4 bytes; EVS_E_RANGE if sink_bytes is smaller);
- * *bytes_host the weight bytes read. EVS_BF16 models only. */
+ * EVS_W_DOWN; ignored for EVS_W_LM; EVS_E_INVALID if the block has no such
+ * projection). sink_dev receives one word per thread, the XOR of every 32-bit
+ * word that thread loaded (n_groups * 512 * 4 bytes, workgroup-major;
+ * EVS_E_RANGE if sink_bytes is smaller), which keeps the loads from being
+ * removed and lets a caller check that exactly the matrix's bytes were read;
+ * *bytes_host the weight bytes read. EVS_BF16 models only
+ * (EVS_E_UNSUPPORTED otherwise). */
 evs_status evs_measure_weight_stream(const evs_model* m, int32_t block, int32_t which, void* sink_dev,
                                      size_t sink_bytes, double* bytes_host, void* stream);
 

@@ -114,7 +114,8 @@ def test_attention_mid_capacity_ranges_match_oracle():
 # ------------------------------------------------------------------- C5
 def committed_equal(cfg, sa, ba, sb, bb):
     """Committed state of sequence ba of sa equals that of sequence bb of sb:
-    length, FIR windows (their rows at positions >= 0), the committed IIR modes, all K/V rows."""
+    length, FIR windows (their rows at positions >= 0), the committed IIR modes
+    (slot -1 on both sides: the zero state), all K/V rows."""
     t = int(sa.tensor(evs.EVS_ST_T)[ba])
     if t != int(sb.tensor(evs.EVS_ST_T)[bb]):
         return False
@@ -128,6 +129,11 @@ def committed_equal(cfg, sa, ba, sb, bb):
         elif blk.kind == "iir":
             ia, sla = int(sa.tensor(evs.EVS_ST_IIR_BUF)[ba]), int(sa.tensor(evs.EVS_ST_IIR_SLOT)[ba])
             ib, slb = int(sb.tensor(evs.EVS_ST_IIR_BUF)[bb]), int(sb.tensor(evs.EVS_ST_IIR_SLOT)[bb])
+            if sla < 0 or slb < 0:
+                # slot -1 is the zero state: nothing stored to compare
+                if sla != slb:
+                    return False
+                continue
             if not torch.equal(sa.tensor(evs.EVS_ST_IIR, i)[ba, ia, sla], sb.tensor(evs.EVS_ST_IIR, i)[bb, ib, slb]):
                 return False
         elif blk.kind == "attn":
