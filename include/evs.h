@@ -368,7 +368,10 @@ evs_status evs_generate_workspace_bytes(const evs_model* m, const evs_state* s, 
  * sequence took part in, tokens those rounds emitted before the cut, so their
  * ratio is the mean tokens per round), *n_rounds_host. work_dev: at least
  * evs_generate_workspace_bytes bytes, 256-byte aligned. Afterwards the state
- * holds the prompt and every emitted token but the last. Unlike the other
+ * holds the prompt and every emitted token but the last. Each round needs
+ * gamma + 1 free positions past the committed length, so max_ctx must cover
+ * the prompt plus n_tokens + gamma; a block that would pass it sets
+ * EVS_ERR_CONTEXT in the sticky error word (and is clamped in bounds). Unlike the other
  * calls this one synchronises `stream`: the host reads the emitted counts
  * between batches of rounds to decide how many more to enqueue. Errors:
  * argument checks as listed (EVS_E_STATE: a pending block, a state without a
