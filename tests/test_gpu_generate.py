@@ -158,3 +158,28 @@ def test_greedy_corrupted_drafter_equals_oracle_native_greedy():
     res = evs.generate(model, state, prompts, n, gamma=gamma, greedy=True, table=table, replace=rep)
     assert np.array_equal(res.ids, want)
     assert res.rounds >= 3 and 1.0 < res.mean_tau < gamma + 1
+
+
+def test_one_token_is_the_prefill_draw_and_no_round():
+    """n_tokens = 1: the only token is the draw from the prefill's last logits
+    (argmax when greedy, the inverse CDF at u_first when sampling); no round
+    runs and the state holds the prompt alone."""
+    cfg = es.tiny_c1()
+    w = es.make_weights(cfg, seed=251)
+    prompts = [es.prompt_tokens(cfg, L, seed=252 + b)[0] for b, L in enumerate((19, 7))]
+    model = evs.Model(cfg, w, device=DEV)
+    orc = HybridLM(cfg, w)
+    from oracle.verifier import argmax_lowest, icdf, target_probs
+    u_first = es.uniforms((2,), seed=255)
+    for greedy in (True, False):
+        state = evs.State(model, 2, 128, 8, device=DEV)
+        res = evs.generate(model, state, prompts, 1, gamma=4, greedy=greedy, temperature=1.0, top_k=0,
+                           table=np.zeros((2, 8), np.int32), u_first=u_first, u_target=es.uniforms((1, 2, 5), seed=256))
+        assert res.rounds == 0 and res.ids.shape == (2, 1)
+        for b, p in enumerate(prompts):
+            lg, _ = orc.prefill(p, chunk=8)
+            want = argmax_lowest(lg) if greedy else icdf(target_probs(lg, 1.0, 0), np.float32(u_first[b]),
+                                                         argmax_lowest(lg))
+            assert res.ids[b, 0] == want, (greedy, b)
+        assert list(lengths(state)) == [len(p) for p in prompts]
+        assert state.error() == 0
