@@ -884,7 +884,10 @@ evs_status evs_prefill(evs_model* m, evs_state* s, const int32_t* tokens, const 
     if (R == 0) return EVS_OK;
     int32_t* pre = wp<int32_t>(s, s->w_pre);
     int32_t *cand = pre, *n_keep = pre + (size_t)s->B * s->max_block, *pick = n_keep + s->B, *doffs = pick + s->B;
+    // the offsets are the caller's host memory: the copy has completed when
+    // the call returns (a pageable source may be read after an async copy returns)
     HIP_TRY(hipMemcpyAsync(doffs, offs, (size_t)(s->B + 1) * 4, hipMemcpyHostToDevice, st));
+    HIP_TRY(hipStreamSynchronize(st));
     for (int j = 0; j < R; ++j) {
       const bool last = j == R - 1;
       HIP_TRY(launch_prefill_round(tokens, doffs, s->B, P, R, j, cand, n_keep, pick, st));

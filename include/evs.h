@@ -20,7 +20,9 @@
  *              pointer; the library never allocates device memory. Host
  *              handles (evs_model, evs_state) are small host objects.
  *   Streams  — `stream` is a hipStream_t (NULL = default stream). Calls only
- *              enqueue work; none synchronises except evs_state_error.
+ *              enqueue work; none synchronises except evs_state_error,
+ *              evs_state_timing_read, evs_generate (between batches of rounds)
+ *              and evs_prefill with several sequences (once, for the offsets).
  *   Errors   — argument and state-machine checks run on the host before
  *              anything is enqueued: on failure nothing is enqueued and a
  *              negative evs_status is returned. A failed kernel launch returns
@@ -189,8 +191,9 @@ evs_status evs_state_error(evs_state* s, int32_t* host_word, int32_t clear, void
 
 /* Consume prompt tokens into committed sequences (model card, "Library":
  * generation starts from a prompt, which is consumed before the first round). tokens_dev holds the concatenated
- * prompts (i32); seq_offsets_host[B+1] delimits sequence b's tokens (copied
- * before the call returns). Each sequence's tokens are appended after its
+ * prompts (i32); seq_offsets_host[B+1] delimits sequence b's tokens. With
+ * several sequences the offsets are copied to the workspace and the call
+ * synchronises `stream` once, so the host array may be reused on return. Each sequence's tokens are appended after its
  * committed length. With one sequence, the prompt goes in chunks of at most
  * max_block positions. With several, all sequences advance together in
  * rounds of P = min(max_block, max_ctx) positions, one forward per round for
