@@ -88,6 +88,9 @@ def parse():
                          "(evs_measure_weight_stream), per projection and for a whole round; JSON lines")
     ap.add_argument("--summarize-stream-trace", metavar="KERNEL_TRACE_CSV",
                     help="per-projection table of a kernel trace of `bench.py --stream-floor`")
+    ap.add_argument("--summarize-kernel-counters", nargs="+", metavar="COUNTER_CSV",
+                    help="mean per-dispatch value of every counter in rocprofv3 --pmc counter files, for the "
+                         "GEMM and weight-stream launches grouped by grid size (a markdown table), and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy kernel five times (the "
                          "known-size reference for scaling the HBM byte counters) and exit")
@@ -98,8 +101,9 @@ GEMM_SOURCES = ("attention_dna_lms_amd/csrc/gemm_impl.h", "attention_dna_lms_amd
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_kernel_c3_traffic.json")
 TRACE_FILE = os.path.join(ROOT, "profiles", "gemm_kernel_c3_trace.json")
 KERNEL_FAMILIES = ("attn_merge_kernel", "gemm_part_kernel", "gemm_pair_kernel", "gemm_kernel", "attn32_kernel", "attn_kernel",
-                   "verify_kernel", "commit_kernel", "embed_kernel", "norm_rows_kernel", "draft_reg_kernel",
-                   "draft_kernel", "inject_prep_kernel", "slots_kernel", "export_rows_kernel")
+                   "verify_kernel", "commit_kernel", "embed_kernel", "draft_reg_kernel", "draft_kernel",
+                   "inject_prep_kernel", "slots_kernel", "export_rows_kernel", "export_pick_kernel", "stream_kernel",
+                   "gen_start_kernel", "gen_cand_kernel", "gen_emit_kernel", "prefill_round_kernel", "pick_rows_kernel")
 C5_GAMMAS = (1, 4, 8, 12, 16)
 
 
@@ -861,6 +865,34 @@ def stream_floor(args):
                       "frac_of_8tbps": round(by / ms / 1e6 / HBM_PEAK_GBPS, 4)}), flush=True)
 
 
+def summarize_kernel_counters(paths):
+    """Per-dispatch means of the counters in rocprofv3 --pmc counter files
+    (one pass each) for gemm_kernel and stream_kernel launches, by grid size:
+    the GEMM and the weight-read floor kernel side by side."""
+    import collections
+    import csv
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            fam = "gemm_kernel" if "gemm_kernel" in name else "stream_kernel" if "stream_kernel" in name else None
+            if fam is None:
+                continue
+            grid = r["Grid_Size"] if "Grid_Size" in r else r["Grid_Size_X"]
+            vals[(fam, int(grid) // 512)][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    keys = sorted(vals, key=lambda k: (k[1], k[0]))
+    counters = sorted({c for k in keys for c in vals[k]})
+    print("| counter | " + " | ".join(f"{f} ({g} workgroups)" for f, g in keys) + " |")
+    print("|---|" + "---|" * len(keys))
+    for c in counters:
+        cells = []
+        for k in keys:
+            v = vals[k].get(c)
+            cells.append(f"{sum(v) / len(v):.4g}" if v else "")
+        print(f"| {c} | " + " | ".join(cells) + " |")
+    print("| dispatches | " + " | ".join(str(len(next(iter(vals[k].values())))) for k in keys) + " |")
+
+
 def summarize_stream_trace(path, steps, warmup):
     """Per-projection durations of a kernel trace of `bench.py --stream-floor`:
     3 + STREAM_REPS launches per projection in STREAM_PROJECTIONS order, then
@@ -1004,6 +1036,9 @@ def main():
         return
     if args.stream_floor:
         stream_floor(args)
+        return
+    if args.summarize_kernel_counters:
+        summarize_kernel_counters(args.summarize_kernel_counters)
         return
     if args.summarize_stream_trace:
         summarize_stream_trace(args.summarize_stream_trace, args.steps, args.warmup)
