@@ -1,10 +1,13 @@
-"""Python binding of libevs (include/evs.h): ctypes marshalling only.
+"""Python binding of libevs (include/evs.h): ctypes marshalling.
 
 Every function named evs_* here forwards to the C function of the same name;
 tensors are passed as device pointers and the current torch stream as the HIP
 stream. ``Model`` and ``State`` own the device buffers (torch tensors) that
-the C API asks the caller for. There is no fallback: if libevs.so is missing
-or cannot be loaded, importing the library raises.
+the C API asks the caller for. ``generate`` / ``generate_native`` (model
+card, "Library") only allocate the buffers, draw the uniforms the caller did
+not pass from a seeded device generator, and call evs_prefill and
+evs_generate; every step of the method runs in the library. There is no
+fallback: if libevs.so is missing or cannot be loaded, the first call raises.
 """
 from __future__ import annotations
 
