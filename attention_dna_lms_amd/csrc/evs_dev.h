@@ -43,6 +43,23 @@ __host__ __device__ __forceinline__ size_t act_off(int m, int c, int K) {
   return ((size_t)(m >> 4) * (K / KS) + c / KS) * (16 * KS) + (size_t)((c % KS) / E) * (16 * E) + (m & 15) * E + (c % E);
 }
 
+// Packed weights: 1 KB fragments (64 lanes x 16 bytes) in the order
+// [wave step i][group g][wave w][tile nt], wave w of a workgroup owning the
+// weight steps w * pw + i, i < pw. Slot idx (in 16-byte units) -> its group,
+// weight step, tile and lane.
+constexpr int PACK_WAVES = 8;
+__host__ __device__ __forceinline__ void packed_slot(long long idx, int n_groups, int NT, int pw, int& g, int& k,
+                                                     int& nt, int& lane) {
+  lane = (int)(idx % 64);
+  long long r = idx / 64;
+  nt = (int)(r % NT);
+  r /= NT;
+  const int w = (int)(r % PACK_WAVES);
+  r /= PACK_WAVES;
+  g = (int)(r % n_groups);
+  k = w * pw + (int)(r / n_groups);
+}
+
 // D += A * B for one 16x16 tile. Fragments: lane l holds row (l % 16) of A and
 // column (l % 16) of B over the same reduction slots; D: lane l holds rows
 // 4*(l/16) + i (i = 0..3) of column l % 16.

@@ -1,9 +1,10 @@
 // Skinny GEMM for the block-verification forward: Y[M, N] = A[M, K] * W[N, K]^T
 // with M = batch * (gamma + 1) small (13 rows at gamma = 12). At such M every
 // projection is bound by reading W from HBM once, so the kernel is a weight
-// streamer: W is pre-packed into 1 KB MFMA fragments in exactly the order a
-// wave consumes them (each wave reads one contiguous run of memory), the
-// activations ride along from L2, and MFMA does the dot products.
+// streamer: W is pre-packed into 1 KB MFMA fragments ordered by step across
+// the whole grid (step i of every wave of every workgroup side by side), so
+// the chip reads one contiguous window of W front to back; the activations
+// ride along from L2, and MFMA does the dot products.
 //
 // Work split: workgroup = group of NT 16-column tiles over the whole K; its 8
 // waves split the k-range and are reduced through LDS in a fixed tree, so
@@ -781,7 +782,8 @@ __global__ void __launch_bounds__(512) gemm_part_kernel(GemmArgs a) {
   const int ks = a.ksteps, pw = (ks + 7) / 8;
   const int kb = min(r * pw, ks), ke = min(kb + pw, ks);
   const int nchk = (ke - kb + PK - 1) / PK;
-  const u32x4* wp = reinterpret_cast<const u32x4*>(a.W) + lane + (gv ? (size_t)g * a.gstride : 0);
+  // range r's steps are gemm_kernel's wave r's: local step k - kb of wave slot r
+  const u32x4* wp = reinterpret_cast<const u32x4*>(a.W) + lane + (gv ? (size_t)g * a.gstride + (size_t)r * a.wstride : 0);
   const T* A = reinterpret_cast<const T*>(a.A);
 
   // staging: unit idx = (u * MT + mt) * 64 + l holds lane l's 16 bytes of row
@@ -798,7 +800,7 @@ __global__ void __launch_bounds__(512) gemm_part_kernel(GemmArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int k = min(kb + c * PK + u, ke - 1);
-        w[u][nt] = ld_stream(wp + (size_t)max(k, 0) * a.tstride + nt * 64);
+        w[u][nt] = ld_stream(wp + (size_t)max(k - kb, 0) * a.tstride + nt * 64);
       }
   };
 
@@ -895,7 +897,10 @@ __global__ void __launch_bounds__(512) gemm_pair_kernel(GemmArgs a) {
   const int kb1 = min((p + 4) * pw, ks), ke1 = min(kb1 + pw, ks);
   const int kb = h ? kb1 : kb0, ke = h ? ke1 : ke0;  // this wave's range
   const int nchk = (ke0 - kb0 + PK - 1) / PK;
-  const u32x4* wp = reinterpret_cast<const u32x4*>(a.W) + lane + (gv ? (size_t)g * a.gstride : 0);
+  // (an empty range p + 4 re-reads its wave slot's first fragment: the packed
+  // buffer holds every slot at full length)
+  const u32x4* wp = reinterpret_cast<const u32x4*>(a.W) + lane +
+                    (gv ? (size_t)g * a.gstride + (size_t)(h ? p + 4 : p) * a.wstride : 0);
   const T* A = reinterpret_cast<const T*>(a.A);
 
   // staging unit idx (< 2 * XF): range idx / XF, then (u * MT + mt) * 64 + l
@@ -919,7 +924,7 @@ __global__ void __launch_bounds__(512) gemm_pair_kernel(GemmArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int k = min(kb + c * PK + u, ke - 1);
-        w[u][nt] = ld_stream(wp + (size_t)max(k, 0) * a.tstride + nt * 64);
+        w[u][nt] = ld_stream(wp + (size_t)max(k - kb, 0) * a.tstride + nt * 64);
       }
   };
 

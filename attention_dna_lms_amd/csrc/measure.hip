@@ -1,5 +1,5 @@
 // Measurement aid: stream one packed weight matrix exactly as gemm_kernel
-// streams it (same workgroups, same contiguous per-wave fragment runs, same
+// streams it (same workgroups, same fragment order and strides, same
 // 16-byte non-temporal loads, two chunks of CH steps in flight) and do
 // nothing else: no activations, no MFMA, no reduction, no epilogue. Its time
 // is the floor of the projection's weight read on this part, against which

@@ -126,30 +126,29 @@ hipError_t launch_copy_row(const void* src, void* dst, size_t bytes, hipStream_t
 }
 
 // ---------------------------------------------------------------- packing
-// Canonical row-major W [rows, K] -> MFMA fragment stream
-// [n_groups][K/KSTEP][NT][64 lanes] of 16 bytes; lane l of (group g, step k,
-// tile nt) holds W[row][k*KSTEP + (l/16)*E .. + E-1] with row = the (l % 16)-th
-// row of that tile: consecutive tiles (map_kind 0) or tile g of section nt of
-// size map_stride (map_kind 1: q|k|v or gate|up kept side by side). Rows past
-// rows_valid are zero.
+// Canonical row-major W [rows, K] -> MFMA fragments of 64 lanes x 16 bytes,
+// stored [wave step i][group g][wave w][tile nt]: the GEMM's wave w of
+// workgroup g owns steps k = w * pw + i (i < pw = ceil(steps / 8)), so at any
+// moment the whole chip reads one contiguous window. Lane l of (g, k, nt)
+// holds W[row][k*KSTEP + (l/16)*E .. + E-1] with row = the (l % 16)-th row of
+// that tile: consecutive tiles (map_kind 0) or tile g of section nt of size
+// map_stride (map_kind 1: q|k|v or gate|up kept side by side). Rows past
+// rows_valid, and steps past the last (the padding of the last ranges), are
+// zero.
 template <typename T>
 __global__ void pack_kernel(const T* __restrict__ W, uint4* __restrict__ out, int rows_valid, int K, int n_groups,
                             int NT, int map_kind, int map_stride) {
   constexpr int E = St<T>::E, KSTEP = St<T>::KSTEP;
-  const int ksteps = K / KSTEP;
-  const long long total = (long long)n_groups * ksteps * NT * 64;
+  const int ksteps = K / KSTEP, pw = (ksteps + PACK_WAVES - 1) / PACK_WAVES;
+  const long long total = (long long)pw * n_groups * PACK_WAVES * NT * 64;
   for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < total;
        idx += (long long)gridDim.x * blockDim.x) {
-    const int lane = (int)(idx % 64);
-    long long r1 = idx / 64;
-    const int nt = (int)(r1 % NT);
-    r1 /= NT;
-    const int k = (int)(r1 % ksteps);
-    const int g = (int)(r1 / ksteps);
+    int g, k, nt, lane;
+    packed_slot(idx, n_groups, NT, pw, g, k, nt, lane);
     const int r = lane % 16;
     const long long row = map_kind == 0 ? (long long)(g * NT + nt) * 16 + r : (long long)nt * map_stride + g * 16 + r;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (row < rows_valid)
+    if (row < rows_valid && k < ksteps)
       v = *reinterpret_cast<const uint4*>(W + row * (long long)K + (long long)k * KSTEP + (lane / 16) * E);
     out[idx] = v;
   }
@@ -216,26 +215,23 @@ __device__ __forceinline__ unsigned e4m3_code(float v) {
   return sign | (unsigned)(((p + 7) << 3) | ((int)q - 8));
 }
 
-// [n_groups][K/64][NT][64 lanes] of 16 bytes: lane l of (group g, step s,
-// tile nt) holds the codes of W[row][64 s + 8 (l / 16) + j] (bytes j = 0..7)
-// and W[row][64 s + 32 + 8 (l / 16) + j] (bytes 8 + j), row = packed row
-// (g, nt, l % 16). Rows past rows_valid are zero.
+// Weight steps of 64 k (two MFMA k-steps), in pack_kernel's slot order: lane
+// l of (group g, step s, tile nt) holds the codes of W[row][64 s + 8 (l / 16)
+// + j] (bytes j = 0..7) and W[row][64 s + 32 + 8 (l / 16) + j] (bytes 8 + j),
+// row = packed row (g, nt, l % 16). Rows past rows_valid, and padding steps,
+// are zero.
 __global__ void pack_fp8_kernel(const bf16* __restrict__ W, const float* __restrict__ scales, uint4* __restrict__ out,
                                 int rows_valid, int K, int n_groups, int NT, int map_kind, int map_stride) {
-  const int steps = K / 64;
-  const long long total = (long long)n_groups * steps * NT * 64;
+  const int steps = K / 64, pw = (steps + PACK_WAVES - 1) / PACK_WAVES;
+  const long long total = (long long)pw * n_groups * PACK_WAVES * NT * 64;
   for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < total;
        idx += (long long)gridDim.x * blockDim.x) {
-    const int lane = (int)(idx % 64);
-    long long r1 = idx / 64;
-    const int nt = (int)(r1 % NT);
-    r1 /= NT;
-    const int st = (int)(r1 % steps);
-    const int g = (int)(r1 / steps);
+    int g, st, nt, lane;
+    packed_slot(idx, n_groups, NT, pw, g, st, nt, lane);
     const int r = lane % 16, kb = lane / 16;
     const long long row = packed_row(g, nt, r, NT, map_kind, map_stride);
     unsigned w[4] = {0u, 0u, 0u, 0u};
-    if (row < rows_valid) {
+    if (row < rows_valid && st < steps) {
       const float inv = 1.f / scales[(g * NT + nt) * 16 + r];   // a power of two: exact
       const bf16* src = W + row * (long long)K + (long long)st * 64 + kb * 8;
 #pragma unroll

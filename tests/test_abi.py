@@ -47,7 +47,8 @@ def test_weights_bytes_and_canonical_shapes():
     d = _desc(cfg)
     n = ctypes.c_size_t()
     assert L.evs_weights_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
-    # packed matrices are exactly the canonical bytes (no padding: every size is a tile multiple)
+    # packed matrices are exactly the canonical bytes (no padding: every size is a tile multiple
+    # and every K a multiple of 8 k-steps, one range per wave)
     assert n.value >= cfg.weight_bytes()
     assert n.value - cfg.weight_bytes() < 64 * 1024 * 1024
     cnt = ctypes.c_int32()
