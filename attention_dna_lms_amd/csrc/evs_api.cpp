@@ -1137,7 +1137,7 @@ evs_status evs_measure_weight_stream(const evs_model* m, int32_t block, int32_t 
   }
   if (sink_bytes < (size_t)mat->n_groups * 512 * 4) return EVS_E_RANGE;
   // the chunk depth gemm_kernel streams this matrix with at one row tile
-  const int CH = mat->NT == 1 ? 4 : 2;
+  const int CH = mat->NT == 3 ? 1 : 2;
   const MatStrides ms = mat_strides(*mat);
   *bytes_host = (double)mat->bytes(m->es);
   return hip_ok(launch_stream(mat->NT, CH, reinterpret_cast<const uint4*>(m->base + mat->off), ms.g, ms.w, ms.t,

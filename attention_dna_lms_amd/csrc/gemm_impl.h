@@ -448,12 +448,14 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   // multi-tile launch keep the shallower chunks measured best for them: the
   // registers go to the row tiles)
   constexpr int AREG = (AMODE == A_NORM && MT >= 2 && sizeof(T) == 2) ? 2 : 1;
-  // (measured at the 7B shapes: 4 steps for single-tile projections, 2 for
-  // the gate/up pairs, the register bound for the in-projection triples)
   constexpr int PER = 16 / (NT + KPW * AREG * MT);
-  // (gate/up at one tile: 2-step chunks measured best, 2.763 against 2.797
-  // ms per round with 4-step chunks and 2.801 with 1-step chunks)
-  constexpr int CAP = NT == 1 ? 4 : NT == 2 ? 2 : 8;
+  // Measured at the 7B shapes with the step-major weight layout (round time,
+  // 8k context, gamma 12): single-tile bf16 out- and down-projections 2-step
+  // chunks (2.623 ms per round against 2.631 / 2.629 with 1 / 3 steps and
+  // 2.665 with 4), gate/up 2 (1: +11 us, 3: +61 us); the single-tile
+  // in-projection takes 1-step chunks at its launch. Multi-tile and FP8
+  // launches keep the depths measured for them before.
+  constexpr int CAP = NT == 1 ? ((MT == 1 && !W8) ? 2 : 4) : NT == 2 ? 2 : 8;
   constexpr int CH = CHO ? CHO : PER < 1 ? 1 : PER < CAP ? PER : CAP;
   extern __shared__ float lds[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1053,9 +1055,9 @@ static hipError_t launch_gemm_mt(int NT, int amode, int epi, const GemmArgs& a, 
                                  size_t lds, hipStream_t st) {
   dim3 grid(a.n_groups, slices), block(512);
   if (NT == 3 && amode == A_NORM && epi == E_MIXER) {
-    // single tile: 2-step chunks (a wave's 16 steps at the 7B shapes in whole
-    // chunk pairs; measured 17.9 us against 20.7 us for 3-step chunks)
-    if constexpr (MT == 1) gemm_kernel<T, 1, 3, A_NORM, E_MIXER, 8, 2><<<grid, block, lds, st>>>(a);
+    // single tile: 1-step chunks, two steps in flight (2.623 against 2.631
+    // ms per round with 2-step chunks, 2.645 with 3 or 4)
+    if constexpr (MT == 1) gemm_kernel<T, 1, 3, A_NORM, E_MIXER, 8, 1><<<grid, block, lds, st>>>(a);
     else gemm_kernel<T, MT, 3, A_NORM, E_MIXER><<<grid, block, lds, st>>>(a);
   } else if (NT == 1 && amode == A_ACT && epi == E_RESID)
     gemm_kernel<T, MT, 1, A_ACT, E_RESID><<<grid, block, lds, st>>>(a);

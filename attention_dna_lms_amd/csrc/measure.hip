@@ -66,9 +66,9 @@ __global__ void __launch_bounds__(512) stream_kernel(const uint4* __restrict__ W
 hipError_t launch_stream(int NT, int CH, const uint4* W, long long gstride, long long wstride, long long tstride,
                          int ksteps, int n_groups, unsigned* sink, hipStream_t st) {
   dim3 grid(n_groups), block(512);
-  if (NT == 1 && CH == 4) stream_kernel<1, 4><<<grid, block, 0, st>>>(W, gstride, wstride, tstride, ksteps, sink);
+  if (NT == 1 && CH == 2) stream_kernel<1, 2><<<grid, block, 0, st>>>(W, gstride, wstride, tstride, ksteps, sink);
   else if (NT == 2 && CH == 2) stream_kernel<2, 2><<<grid, block, 0, st>>>(W, gstride, wstride, tstride, ksteps, sink);
-  else if (NT == 3 && CH == 2) stream_kernel<3, 2><<<grid, block, 0, st>>>(W, gstride, wstride, tstride, ksteps, sink);
+  else if (NT == 3 && CH == 1) stream_kernel<3, 1><<<grid, block, 0, st>>>(W, gstride, wstride, tstride, ksteps, sink);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
