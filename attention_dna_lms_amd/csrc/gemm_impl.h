@@ -1061,9 +1061,14 @@ static hipError_t launch_gemm_mt(int NT, int amode, int epi, const GemmArgs& a, 
     else gemm_kernel<T, MT, 3, A_NORM, E_MIXER><<<grid, block, lds, st>>>(a);
   } else if (NT == 1 && amode == A_ACT && epi == E_RESID)
     gemm_kernel<T, MT, 1, A_ACT, E_RESID><<<grid, block, lds, st>>>(a);
-  else if (NT == 2 && amode == A_NORM && epi == E_GELU)
-    gemm_kernel<T, MT, 2, A_NORM, E_GELU><<<grid, block, lds, st>>>(a);
-  else if (NT == 1 && amode == A_NORM && epi == E_STORE)
+  else if (NT == 2 && amode == A_NORM && epi == E_GELU) {
+    // bf16 rows of 2-4 tiles: 1-step chunks; 5-6 tiles: 2-step chunks
+    // (ragged batch of 8 sequences at gamma 2 / 4 / 8 / 10: 4.270 / 4.851 /
+    // 6.220 / 6.858 ms per round against 4.372 / 5.034 / 6.238 / 6.915 ms
+    // with the register-bound depth; gamma 6, 4 tiles, the same either way)
+    constexpr int GU_CH = (MT >= 2 && sizeof(T) == 2) ? (MT <= 4 ? 1 : 2) : 0;
+    gemm_kernel<T, MT, 2, A_NORM, E_GELU, 8, GU_CH><<<grid, block, lds, st>>>(a);
+  } else if (NT == 1 && amode == A_NORM && epi == E_STORE)
     gemm_kernel<T, MT, 1, A_NORM, E_STORE><<<grid, block, lds, st>>>(a);
   else if (NT == 1 && amode == A_ACT && epi == E_STORE)     // rows normalised by their producer
     gemm_kernel<T, MT, 1, A_ACT, E_STORE><<<grid, block, lds, st>>>(a);
