@@ -30,17 +30,19 @@ template <typename T> __device__ __forceinline__ float rnd(float x) { return to_
 
 // Layout of the activations inside the forward (the residual stream x, the
 // mixer outputs, the MLP hidden rows, the attention queries): rows in tiles of
-// 16, each tile split into k-steps of 4E columns, each step stored in MFMA
-// operand order [column group of E][row][E]. The operand fragment of row tile
-// t and k-step s is then one contiguous run of 64 lanes x E elements, lane l
-// at offset l * E (rows of a tile past the valid count are never written and
-// only feed discarded output columns). E is the storage type's per-lane
-// element count (8 for bf16 models, 4 for fp32), also for the fp32 residual
-// stream. K is the matrix's column count (a multiple of 4E).
+// 16, each tile split into k-steps of 4E columns, each step one contiguous
+// block [row][4E]. The operand fragment of row tile t and k-step s is that
+// block (lane l reads row l % 16, columns (l / 16) * E .. + E - 1), and the
+// rows of a partial tile fill its front: a launch whose last tile holds 13
+// rows (gamma = 12) points the lanes of rows 13..15 at row 12 and touches 7
+// of the block's 8 128-byte lines (rows of a tile past the valid count are
+// never written and only feed discarded output columns). E is the storage
+// type's per-lane element count (8 for bf16 models, 4 for fp32), also for
+// the fp32 residual stream. K is the matrix's column count (a multiple of 4E).
 template <int E>
 __host__ __device__ __forceinline__ size_t act_off(int m, int c, int K) {
   constexpr int KS = 4 * E;
-  return ((size_t)(m >> 4) * (K / KS) + c / KS) * (16 * KS) + (size_t)((c % KS) / E) * (16 * E) + (m & 15) * E + (c % E);
+  return ((size_t)(m >> 4) * (K / KS) + c / KS) * (16 * KS) + (size_t)(m & 15) * KS + (c % KS);
 }
 
 // Packed weights: 1 KB fragments (64 lanes x 16 bytes) in the order
