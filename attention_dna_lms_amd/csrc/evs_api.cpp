@@ -45,17 +45,8 @@ struct Mat {            // one packed matrix
   size_t packed_bytes(int kstep) const { return (size_t)n_groups * NT * GEMM_WAVES * per_wave(kstep) * 1024; }
 };
 
-// Packed layout, in 1 KB fragments: [wave step i][group g][wave w][tile nt],
-// with step i of wave w the weight step w * per_wave + i. At any moment the
-// waves of every workgroup are at about the same step, so the whole chip
-// reads one contiguous window of the matrix, front to back (measured faster
-// on MI355X than per-wave contiguous runs: 2-8% by projection). Strides in
-// 16-byte units, as the kernels take them.
-struct MatStrides { long long g, w, t; };
-MatStrides mat_strides(const Mat& mm) {
-  const long long f = (long long)mm.NT * 64;   // one step of one wave: NT fragments
-  return MatStrides{GEMM_WAVES * f, f, (long long)mm.n_groups * GEMM_WAVES * f};
-}
+// The kernels' strides of a packed matrix (the layout packed_slot describes)
+MatStrides mat_strides(const Mat& mm) { return packed_strides(mm.n_groups, mm.NT); }
 
 // storage type of activations, states and the non-FP8 tensors
 int storage_dtype(const evs_model_desc* d) { return d->dtype == EVS_F32 ? EVS_F32 : EVS_BF16; }

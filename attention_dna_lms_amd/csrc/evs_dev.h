@@ -47,9 +47,18 @@ __host__ __device__ __forceinline__ size_t act_off(int m, int c, int K) {
 
 // Packed weights: 1 KB fragments (64 lanes x 16 bytes) in the order
 // [wave step i][group g][wave w][tile nt], wave w of a workgroup owning the
-// weight steps w * pw + i, i < pw. Slot idx (in 16-byte units) -> its group,
-// weight step, tile and lane.
+// weight steps w * pw + i, i < pw. At any moment the waves of every
+// workgroup are at about the same step, so the whole chip reads one
+// contiguous window of the matrix, front to back (on MI355X 2-8% faster by
+// projection than one contiguous run per wave). packed_slot: slot idx (in
+// 16-byte units) -> its group, weight step, tile and lane; packed_strides:
+// the strides (16-byte units) between groups, waves and steps.
 constexpr int PACK_WAVES = 8;
+struct MatStrides { long long g, w, t; };
+__host__ __device__ __forceinline__ MatStrides packed_strides(int n_groups, int NT) {
+  const long long f = (long long)NT * 64;   // one step of one wave: NT fragments
+  return MatStrides{PACK_WAVES * f, f, (long long)n_groups * PACK_WAVES * f};
+}
 __host__ __device__ __forceinline__ void packed_slot(long long idx, int n_groups, int NT, int pw, int& g, int& k,
                                                      int& nt, int& lane) {
   lane = (int)(idx % 64);

@@ -97,7 +97,8 @@ def parse():
     return ap.parse_args()
 
 
-GEMM_SOURCES = ("attention_dna_lms_amd/csrc/gemm_impl.h", "attention_dna_lms_amd/csrc/gemm_bf16.hip")
+GEMM_SOURCES = ("attention_dna_lms_amd/csrc/gemm_impl.h", "attention_dna_lms_amd/csrc/gemm_bf16.hip",
+                "attention_dna_lms_amd/csrc/evs_dev.h")   # the kernel, its instantiation, the layouts
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_kernel_c3_traffic.json")
 TRACE_FILE = os.path.join(ROOT, "profiles", "gemm_kernel_c3_trace.json")
 KERNEL_FAMILIES = ("attn_merge_kernel", "gemm_part_kernel", "gemm_pair_kernel", "gemm_kernel", "attn32_kernel", "attn_kernel",
