@@ -81,8 +81,16 @@ struct EpiPre {
   float win[FIR_PRE];        // MIX_FIR: window of the slice's first sequence
   float tap[FIR_PRE];        // MIX_FIR: taps of this channel tile
   float s0, lam, res;        // MIX_IIR: committed mode, pole, residue of (c, n)
+  int tb;                    // MIX_FIR, MIX_ATTN: the first sequence's committed length
+  int ibuf, islot;           // MIX_IIR: the first sequence's state buffer and slot
 };
 
+// Two phases, so that no wave waits on memory before its weight stream
+// starts: epi_prefetch loads what needs no other load (the residual tile,
+// taps, poles and residues, the per-sequence integers) and is issued first;
+// epi_prefetch_dep loads what is addressed by those integers (the FIR window,
+// the committed IIR mode) and is issued after the first two chunks of weights
+// and activations, so its wait for the integers overlaps their flight.
 template <typename T, int MT, int NT, int EPI>
 __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, EpiPre& pf, int g, int row0, int rows) {
   const int tid = threadIdx.x;
@@ -98,32 +106,56 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, EpiPre& pf, int 
   } else if constexpr (EPI == E_MIXER) {
     const MixArgs& x = a.mix;
     const int ch0 = g * 16;
-    if (x.kind == MIX_FIR && x.L <= FIR_PRE * 32) {
-      const int b = x.seq0 + row0 / x.P;
-      const int tb = x.t[b];
-      const float* ring = x.ring + (size_t)b * x.ring_bs;
+    const int b = x.seq0 + row0 / x.P;
+    if (x.kind == MIX_ATTN) {
+      pf.tb = x.t[b];
+    } else if (x.kind == MIX_FIR && x.L <= FIR_PRE * 32) {
+      pf.tb = x.t[b];
 #pragma unroll
       for (int q = 0; q < FIR_PRE; ++q) {
-        const int idx = tid + q * 512, jj = idx >> 4, c = idx & 15;
-        const int pos = tb - (x.L - 1) + jj;   // ring rows are always in range; pos < 0 reads as 0
-        const float v = ring[(size_t)(pos & (x.R - 1)) * x.d + ch0 + c];
-        pf.win[q] = (jj < x.L - 1 && pos >= 0) ? v : 0.f;
+        const int idx = tid + q * 512;
         const int tc = idx / x.L, tj = idx % x.L;
         pf.tap[q] = idx < 16 * x.L ? x.taps[(size_t)(ch0 + tc) * x.L + tj] : 0.f;
       }
     } else if (x.kind == MIX_IIR) {
       // every thread: its channel's pole and residue of mode n; the first 256
-      // (the first sequence's threads): that sequence's committed mode
+      // (the first sequence's threads): that sequence's state buffer and slot
       const int c = (tid >> 4) & 15, n = tid & 15, ch = ch0 + c;
       const bool vn = n < x.N;
       pf.lam = vn ? x.lam[(size_t)ch * x.N + n] : 0.f;
       pf.res = vn ? x.res[(size_t)ch * x.N + n] : 0.f;
+      if (tid < 256) {
+        pf.ibuf = x.iir_buf[b];
+        pf.islot = x.iir_slot[b];
+      }
+    }
+  }
+}
+
+template <typename T, int MT, int NT, int EPI>
+__device__ __forceinline__ void epi_prefetch_dep(const GemmArgs& a, EpiPre& pf, int g, int row0) {
+  if constexpr (EPI == E_MIXER) {
+    const int tid = threadIdx.x;
+    const MixArgs& x = a.mix;
+    const int ch0 = g * 16;
+    const int b = x.seq0 + row0 / x.P;
+    if (x.kind == MIX_FIR && x.L <= FIR_PRE * 32) {
+      const float* ring = x.ring + (size_t)b * x.ring_bs;
+#pragma unroll
+      for (int q = 0; q < FIR_PRE; ++q) {
+        const int idx = tid + q * 512, jj = idx >> 4, c = idx & 15;
+        const int pos = pf.tb - (x.L - 1) + jj;   // ring rows are always in range; pos < 0 reads as 0
+        const float v = ring[(size_t)(pos & (x.R - 1)) * x.d + ch0 + c];
+        pf.win[q] = (jj < x.L - 1 && pos >= 0) ? v : 0.f;
+      }
+    } else if (x.kind == MIX_IIR) {
+      const int c = (tid >> 4) & 15, n = tid & 15, ch = ch0 + c;
+      const bool vn = n < x.N;
       pf.s0 = 0.f;
       if (tid < 256) {
-        const int b = x.seq0 + row0 / x.P;
-        const int buf = x.iir_buf[b], slot = x.iir_slot[b];
+        const int slot = pf.islot;
         const float* base = x.iirst + (size_t)b * x.iir_bs;
-        const size_t so = (size_t)buf * x.iir_buf_s + ((size_t)(slot < 0 ? 0 : slot) * x.d + ch) * x.N + (vn ? n : 0);
+        const size_t so = (size_t)pf.ibuf * x.iir_buf_s + ((size_t)(slot < 0 ? 0 : slot) * x.d + ch) * x.N + (vn ? n : 0);
         const float sv = base[so];
         pf.s0 = (vn && slot >= 0) ? sv : 0.f;
       }
@@ -202,12 +234,14 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
       T* kc = reinterpret_cast<T*>(x.kc);
       T* vt = reinterpret_cast<T*>(x.vt);
       int* tl = reinterpret_cast<int*>(scratch);   // [nseq] committed lengths
-      for (int j = tid; j < nseq; j += nth) tl[j] = x.t[sbase + j];
-      __syncthreads();
+      if (nseq > 1) {   // (one sequence: its length came with the prologue)
+        for (int j = tid; j < nseq; j += nth) tl[j] = x.t[sbase + j];
+        __syncthreads();
+      }
       for (int idx = tid; idx < rows * 16; idx += nth) {
         const int m = idx / 16, c = idx & 15;
         const int b = sbase + m / P, p = m % P;
-        const int pos = tl[m / P] + p;
+        const int pos = (nseq > 1 ? tl[m / P] : pf.tb) + p;
         const int ch = ch0 + c, h = ch / x.Dh, dh = ch % x.Dh;
         out[act_off<St<T>::E>(row0 + m, ch, a.ldo)] = from_f<T>(eq[idx]);
         if (pos < x.cap) {
@@ -244,8 +278,13 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
         // (indices clamped to the batch), so all are in flight together; a
         // single-sequence launch keeps the window loaded with the prologue
         int tbv[FIR_FB];
+        if (pre && nseq == 1) {   // (the length came with the prologue)
 #pragma unroll
-        for (int u = 0; u < FIR_FB; ++u) tbv[u] = x.t[sbase + j0 + min(u, nb - 1)];
+          for (int u = 0; u < FIR_FB; ++u) tbv[u] = pf.tb;
+        } else {
+#pragma unroll
+          for (int u = 0; u < FIR_FB; ++u) tbv[u] = x.t[sbase + j0 + min(u, nb - 1)];
+        }
         if (pre) {
           float wv[FIR_FB][FIR_PRE];
           if (nseq == 1) {
@@ -349,11 +388,19 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
         // repeats the last and is skipped below)
         int dbv[RB], slv[RB];
         float sv[RB];
+        if (nseq == 1) {   // (buffer and slot came with the prologue, to the first 256 threads: the ones that work)
 #pragma unroll
-        for (int u = 0; u < RB; ++u) {
-          const int j = min(2 * (r0 + min(u, nb - 1)) + half, nseq - 1);
-          dbv[u] = x.iir_buf[sbase + j];
-          slv[u] = x.iir_slot[sbase + j];
+          for (int u = 0; u < RB; ++u) {
+            dbv[u] = pf.ibuf;
+            slv[u] = pf.islot;
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < RB; ++u) {
+            const int j = min(2 * (r0 + min(u, nb - 1)) + half, nseq - 1);
+            dbv[u] = x.iir_buf[sbase + j];
+            slv[u] = x.iir_slot[sbase + j];
+          }
         }
         if (nseq == 1) {
 #pragma unroll
@@ -390,25 +437,42 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
             float* dst = x.iirst + (size_t)(sbase + j) * x.iir_bs + (size_t)(dbv[u] ^ 1) * x.iir_buf_s;
             for (int p0 = 0; p0 < P; p0 += IIR_CH) {
               const int np = min(IIR_CH, P - p0);
-              float hv[IIR_CH];
+              // a chunk's inputs h = k v and gates q first (LDS), then the
+              // recurrence alone (one fma per position), then the state
+              // stores, the mode sums and the outputs: no wait and no branch
+              // inside the serial part
+              float hv[IIR_CH], qv[IIR_CH], sq[IIR_CH];
 #pragma unroll
               for (int q = 0; q < IIR_CH; ++q) {
                 const int m = j * P + p0 + min(q, np - 1);
                 hv[q] = rnd<T>(ek[m * 16 + c]) * rnd<T>(ev[m * 16 + c]);
+                qv[q] = rnd<T>(eq[m * 16 + c]);
               }
 #pragma unroll
               for (int q = 0; q < IIR_CH; ++q) {
-                if (q < np) {
-                  const int m = j * P + p0 + q;
-                  s = fmaf(lam, s, hv[q]);
-                  if (vn) dst[((size_t)(p0 + q) * x.d + ch) * x.N + n] = s;
-                  float rs = vn ? res * s : 0.f;
-                  rs += dpp_row_ror<8>(rs);
-                  rs += dpp_row_ror<4>(rs);
-                  rs += dpp_row_ror<2>(rs);
-                  rs += dpp_row_ror<1>(rs);
-                  if (n == 0) out[act_off<St<T>::E>(row0 + m, ch, a.ldo)] = from_f<T>(rnd<T>(eq[m * 16 + c]) * rs);
-                }
+                s = q < np ? fmaf(lam, s, hv[q]) : s;
+                sq[q] = s;
+              }
+              // (slots past the chunk's last position repeat its state and
+              // gate: their stores rewrite that position's values, so no
+              // branch is needed around them)
+              if (vn) {
+#pragma unroll
+                for (int q = 0; q < IIR_CH; ++q) dst[((size_t)(p0 + min(q, np - 1)) * x.d + ch) * x.N + n] = sq[q];
+              }
+#pragma unroll
+              for (int q = 0; q < IIR_CH; ++q) {
+                float rs = vn ? res * sq[q] : 0.f;
+                rs += dpp_row_ror<8>(rs);
+                rs += dpp_row_ror<4>(rs);
+                rs += dpp_row_ror<2>(rs);
+                rs += dpp_row_ror<1>(rs);
+                sq[q] = rs;
+              }
+              if (n == 0) {
+#pragma unroll
+                for (int q = 0; q < IIR_CH; ++q)
+                  out[act_off<St<T>::E>(row0 + j * P + p0 + min(q, np - 1), ch, a.ldo)] = from_f<T>(qv[q] * sq[q]);
               }
             }
           }
@@ -532,6 +596,7 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = pp[(mt * NT + nt) * 64];
+    epi_prefetch_dep<T, MT, NT, EPI>(a, pf, g, row0);
     if constexpr (AMODE == A_NORM) {
 #pragma unroll
       for (int pss = 0; pss < NP; ++pss) row_scales(pss, 0.f, 0);
@@ -615,6 +680,7 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   issue_w(w0, wk0);
   issue_x(x1, wk0 + CH);
   issue_w(w1, wk0 + CH);
+  epi_prefetch_dep<T, MT, NT, EPI>(a, pf, g, row0);
 
   if constexpr (AMODE == A_NORM) {
     // (the scales are read from LDS by the epilogue tile's formation, after
