@@ -430,7 +430,7 @@ __device__ int wave_target_row(float* pr, int V, float temperature, int top_k, b
       for (int y = lane; y < V; y += 64) {
         const float z = pr[y];
         const okey_t k = isnan(z) ? 0 : ord_key(z, y);
-        c = (k < pk) & (k > c) ? k : c;
+        c = ((k < pk) & (k > c)) ? k : c;
       }
       pk = wave_keymax(c);
     }
@@ -1049,7 +1049,7 @@ __global__ void __launch_bounds__(64) draft_reg_kernel(DraftArgs a) {
       for (int r = 0; r < passes; ++r) {
         okey_t c = 0;
 #pragma unroll
-        for (int k = 0; k < NPL; ++k) c = (zk[k] < pk) & (zk[k] > c) ? zk[k] : c;
+        for (int k = 0; k < NPL; ++k) c = ((zk[k] < pk) & (zk[k] > c)) ? zk[k] : c;
         // the same in every lane (scalar registers), so the work on the kept
         // entries below branches uniformly
         pk = wave_keymax(c);
