@@ -85,12 +85,16 @@ struct EpiPre {
   int ibuf, islot;           // MIX_IIR: the first sequence's state buffer and slot
 };
 
-// Two phases, so that no wave waits on memory before its weight stream
+// Two phases, both issued after the first two chunks of weights and
+// activations, so that no wave waits on memory before its weight stream
 // starts: epi_prefetch loads what needs no other load (the residual tile,
-// taps, poles and residues, the per-sequence integers) and is issued first;
-// epi_prefetch_dep loads what is addressed by those integers (the FIR window,
-// the committed IIR mode) and is issued after the first two chunks of weights
-// and activations, so its wait for the integers overlaps their flight.
+// taps, poles and residues, the per-sequence integers); epi_prefetch_dep
+// loads what is addressed by those integers (the FIR window, the committed
+// IIR mode), and its wait for the integers overlaps the chunks' flight.
+// (Issued before the weights, the residual tile's row stride sits in an
+// argument line of its own, and the wait for that line held the out- and
+// down-projections' streams back by one more memory round trip: a round of
+// the 7B-shaped stack took 2.605 ms that way against 2.586 ms.)
 template <typename T, int MT, int NT, int EPI>
 __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, EpiPre& pf, int g, int row0, int rows) {
   const int tid = threadIdx.x;
@@ -572,10 +576,9 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
                     (nch > 0 ? (size_t)g * a.gstride + (size_t)wave * a.wstride : 0);
   const int rl = lane & 15, aoff = (lane >> 4) * E;
 
-  // epilogue inputs first (only the workgroup that runs the epilogue needs
-  // them, but which one that is is known only at the end)
+  // epilogue inputs (only the workgroup that runs the epilogue needs them,
+  // but which one that is is known only at the end)
   EpiPre pf;
-  epi_prefetch<T, MT, NT, EPI>(a, pf, g, row0, rows);
   // each lane feeds activation rows mt*16 + rl (clamped to the last valid row)
   size_t arow[MT];
 #pragma unroll
@@ -589,6 +592,7 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
     // w + (w + 4), the tree's first level; waves 4..7 hold -0, the exact
     // additive identity, so the tree's remaining levels are unchanged).
     // Issued before the norm's loads, so both are in flight together.
+    epi_prefetch<T, MT, NT, EPI>(a, pf, g, row0, rows);
     const int np = a.nparts == 4 ? 4 : 8;
     const f32x4* pp = reinterpret_cast<const f32x4*>(a.part) +
                       ((((size_t)blockIdx.y * np + min(wave, np - 1)) * a.n_groups + g) * MT) * NT * 64 + lane;
@@ -662,9 +666,10 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   };
 
   // Start-up order: the norm's per-16-column sums of squares are loaded
-  // first, then the first two chunks of activations and weights, and only
-  // then does the norm prologue wait (for its own loads alone), so the
-  // weight stream starts at once and two chunks are in flight from the start.
+  // first, then the first two chunks of activations and weights, then the
+  // epilogue's inputs, and only then does the norm prologue wait (for its
+  // own loads alone), so the weight stream starts at once and two chunks are
+  // in flight from the start.
   // (many-row launches skip the early load: its registers would spill)
   constexpr bool PRE = AMODE == A_NORM && MT <= 2;
   float nv[PRE ? NP : 1][8];
@@ -680,6 +685,7 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   issue_w(w0, wk0);
   issue_x(x1, wk0 + CH);
   issue_w(w1, wk0 + CH);
+  epi_prefetch<T, MT, NT, EPI>(a, pf, g, row0, rows);
   epi_prefetch_dep<T, MT, NT, EPI>(a, pf, g, row0);
 
   if constexpr (AMODE == A_NORM) {
