@@ -572,8 +572,10 @@ __global__ void __launch_bounds__(WV * 64, MINB) gemm_kernel(GemmArgs a) {
   // with no k-steps streams nothing useful: its (never consumed) loads read
   // the matrix's first fragment, so every load below is unconditional and
   // each wait covers exactly the loads it needs.
-  const u32x4* wp = reinterpret_cast<const u32x4*>(a.W) + lane +
-                    (nch > 0 ? (size_t)g * a.gstride + (size_t)wave * a.wstride : 0);
+  // (the offset is formed unconditionally and selected, so its strides are
+  // read with the other argument fields instead of behind a branch)
+  const size_t woff = (size_t)g * a.gstride + (size_t)wave * a.wstride;
+  const u32x4* wp = reinterpret_cast<const u32x4*>(a.W) + lane + (nch > 0 ? woff : 0);
   const int rl = lane & 15, aoff = (lane >> 4) * E;
 
   // epilogue inputs (only the workgroup that runs the epilogue needs them,
