@@ -1032,6 +1032,10 @@ def cpu_baseline(cfg, weights_gpu, ctx, gamma, seed, rounds=3):
 
 def main():
     args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the block-verify path runs on one GPU)", file=sys.stderr)
+        sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
         return
@@ -1074,10 +1078,6 @@ def main():
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, args.steps, args.warmup)
         return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the block-verify path runs on one GPU)", file=sys.stderr)
-        sys.exit(2)
     import numpy as np
     import torch
     import evs_synth as es

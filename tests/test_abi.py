@@ -111,3 +111,16 @@ def test_verify_sample_rejects_bad_arguments_before_launch():
     assert L.evs_verify_sample(1, 4, 512, p, 1, p, p, p, 0.0, 0, 0, p, p, z, z, z) == -1
     assert L.evs_verify_sample(1, 40, 512, p, 1, p, p, p, 1.0, 0, 0, p, p, z, z, z) == -5
     assert L.evs_verify_sample(1, 64, 4, p, 1, p, p, p, 1.0, 0, 0, p, p, z, z, z) == -1
+
+
+@pytest.mark.parametrize("mode", [[], ["--c5"], ["--soak", "64"], ["--stream-floor"]])
+def test_bench_refuses_more_than_one_gpu(mode):
+    """bench.py measures one GPU: any mode with --gpus N > 1 exits with status 2
+    and says so, before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"] + mode,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
