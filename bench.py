@@ -31,14 +31,15 @@ METRIC = "block-verify tokens/s (γ=12, d=4096 hybrid stack) + achieved HBM GB/s
 
 
 def parse():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--gamma", type=int, default=12)
-    ap.add_argument("--context", type=int, default=8192)
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap = argparse.ArgumentParser(description="Block-verify rounds of the 7B-shaped hybrid stack on one MI355X; "
+                                             "prints one JSON line (see the modes below for the other workloads)")
+    ap.add_argument("--gpus", type=int, default=1, help="GPUs to measure on: 1 only (other values exit with status 2)")
+    ap.add_argument("--steps", type=int, default=50, help="timed rounds")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed rounds before the timed ones")
+    ap.add_argument("--gamma", type=int, default=12, help="drafts per round (blocks of gamma + 1 positions)")
+    ap.add_argument("--context", type=int, default=8192, help="committed context length before the rounds")
+    ap.add_argument("--seed", type=int, default=0, help="seed of the synthetic weights, prompt and drafts")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the oracle on the host cores")
     ap.add_argument("--cpu-rounds", type=int, default=3, help="timed oracle rounds for cpu_baseline")
     ap.add_argument("--soak", type=int, metavar="N",
                     help="generate N tokens natively and speculatively (~75%% drafter) from the "
