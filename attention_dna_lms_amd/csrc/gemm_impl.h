@@ -432,6 +432,76 @@ __device__ void gemm_epilogue(const GemmArgs& a, const EpiPre& pf, const float* 
             sv[u] = __uint_as_float(__float_as_uint(v[u]) & keep);
           }
         }
+        if (nseq > 1) {
+          // Several sequences: this thread's RB sequences run together, their
+          // chains interleaved position by position so that their latencies
+          // overlap (each sequence's arithmetic and stores exactly as in the
+          // one-sequence loop below). A round past the batch (or past an odd
+          // count) computes on the clamped sequence and stores nothing.
+          constexpr int ICH = 4;
+          const float lam = pf.lam, res = pf.res;
+          int jv[RB];
+          bool ok[RB];
+          float* dst[RB];
+          float sr[RB];
+#pragma unroll
+          for (int u = 0; u < RB; ++u) {
+            const int j = 2 * (r0 + u) + half;
+            ok[u] = u < nb && j < nseq;   // uniform per wave
+            jv[u] = min(2 * (r0 + min(u, nb - 1)) + half, nseq - 1);
+            dst[u] = x.iirst + (size_t)(sbase + jv[u]) * x.iir_bs + (size_t)(dbv[u] ^ 1) * x.iir_buf_s;
+            sr[u] = sv[u];
+          }
+          for (int p0 = 0; p0 < P; p0 += ICH) {
+            const int np = min(ICH, P - p0);
+            float hv[RB][ICH], qv[RB][ICH], sq[RB][ICH];
+#pragma unroll
+            for (int u = 0; u < RB; ++u)
+#pragma unroll
+              for (int q = 0; q < ICH; ++q) {
+                const int m = jv[u] * P + p0 + min(q, np - 1);
+                hv[u][q] = rnd<T>(ek[m * 16 + c]) * rnd<T>(ev[m * 16 + c]);
+                qv[u][q] = rnd<T>(eq[m * 16 + c]);
+              }
+#pragma unroll
+            for (int q = 0; q < ICH; ++q)
+#pragma unroll
+              for (int u = 0; u < RB; ++u) {
+                sr[u] = q < np ? fmaf(lam, sr[u], hv[u][q]) : sr[u];
+                sq[u][q] = sr[u];
+              }
+            if (vn) {
+#pragma unroll
+              for (int u = 0; u < RB; ++u)
+                if (ok[u]) {
+#pragma unroll
+                  for (int q = 0; q < ICH; ++q)
+                    dst[u][((size_t)(p0 + min(q, np - 1)) * x.d + ch) * x.N + n] = sq[u][q];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < RB; ++u)
+#pragma unroll
+              for (int q = 0; q < ICH; ++q) {
+                float rs = vn ? res * sq[u][q] : 0.f;
+                rs += dpp_row_ror<8>(rs);
+                rs += dpp_row_ror<4>(rs);
+                rs += dpp_row_ror<2>(rs);
+                rs += dpp_row_ror<1>(rs);
+                sq[u][q] = rs;
+              }
+            if (n == 0) {
+#pragma unroll
+              for (int u = 0; u < RB; ++u)
+                if (ok[u]) {
+#pragma unroll
+                  for (int q = 0; q < ICH; ++q)
+                    out[act_off<St<T>::E>(row0 + jv[u] * P + p0 + min(q, np - 1), ch, a.ldo)] =
+                        from_f<T>(qv[u][q] * sq[u][q]);
+                }
+            }
+          }
+        } else
 #pragma unroll
         for (int u = 0; u < RB; ++u) {
           const int j = 2 * (r0 + u) + half;
