@@ -1,5 +1,8 @@
 """The hybrid (FIR / IIR / attention + MLP) stack, in two independent forms.
 
+Part of the oracle: test infrastructure only (the tests, the smoke check and
+the benchmark's CPU-baseline leg may import it; the HIP path never does).
+
 What is computed (EvSpark preprint, abstract (i); Evo2 discussion #232, "The
 systems problem" and "What we implemented"): a StripedHyena2-style stack whose
 inference state mixes three classes — fixed-length FIR sliding windows, IIR

@@ -1,5 +1,8 @@
 """Scalar numerics of the oracle (fp64).
 
+Part of the oracle: test infrastructure only (the tests, the smoke check and
+the benchmark's CPU-baseline leg may import it; the HIP path never does).
+
 Parity pins (tests/test_oracle_numerics.py):
   round_bf16 — against torch's float->bfloat16 conversion and hand-checked
                tie cases.

@@ -1,5 +1,8 @@
 """One speculative round, native decoding, and snapshot-and-replay.
 
+Part of the oracle: test infrastructure only (the tests, the smoke check and
+the benchmark's CPU-baseline leg may import it; the HIP path never does).
+
 A round (EvSpark preprint, abstract (i); Evo2 discussion #232, "What we
 implemented"): the candidate block is [x_last, d_1 .. d_gamma], where x_last is
 the last emitted token, not yet consumed. One block-verification forward gives

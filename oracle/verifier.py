@@ -1,5 +1,8 @@
 """Verification of a drafted block: exact rejection sampling and greedy.
 
+Part of the oracle: test infrastructure only (the tests, the smoke check and
+the benchmark's CPU-baseline leg may import it; the HIP path never does).
+
 Sampling mode follows the exact rejection-sampling verifier the pages name
 (EvSpark preprint, abstract (iii): the scheme preserves the target
 distribution in exact arithmetic; Evo2 discussion #232, "A few other
